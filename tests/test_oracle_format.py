@@ -1,0 +1,318 @@
+"""Pins for the oracle's block format: page-given sizes, hand-worked
+blocks, IEEE binary16 against numpy, codebooks against the E2M1 definition,
+the nearest-code rule, the bit layout and encoder invariants."""
+
+import math
+
+import numpy as np
+import pytest
+
+import inputgen
+import oracle as O
+from conftest import expand_list, load_golden
+
+FMTS = (2, 3, 4)
+
+
+def test_block_sizes_from_pages():
+    recs = load_golden("format_sizes.txt")
+    wpb = [r for r in recs if "weights_per_block" in r][0]
+    assert int(wpb["weights_per_block"]) == 32
+    rows = [r for r in recs if "fmt" in r]
+    assert len(rows) == 3
+    for r in rows:
+        parts = r["fmt"].split()
+        fmt, bpw, nbytes = int(parts[0]), float(parts[2]), int(parts[4])
+        assert nbytes == 32 * bpw / 8
+        assert O.block_bytes(fmt) == nbytes
+
+
+@pytest.mark.parametrize("rec", [r for r in load_golden("hand_blocks.txt") if "fmt" in r],
+                         ids=lambda r: r["name"])
+def test_hand_worked_blocks(rec):
+    fmt = int(rec["fmt"])
+    w = np.array(expand_list(rec["w"]), np.float32)
+    blk = O.quantize_block(fmt, w)
+    want = bytes(int(b, 16) for b in rec["bytes"].split())
+    assert bytes(blk) == want
+    vals = O.dequantize_block(fmt, blk)
+    assert list(vals[:8]) == expand_list(rec["values"])
+    xq = np.ones((1, 32), np.int8)
+    xs = np.ones((1, 1), np.float32)
+    y, d = O.gemv(fmt, blk[None, None, :], xq, xs, want_dots=True)
+    assert d[0, 0, 0] == int(rec["dot1"])
+
+
+def test_hand_worked_activation_and_product():
+    recs = {r["name"]: r for r in load_golden("hand_blocks.txt")}
+    act = recs["ACT-D"]
+    x = np.array(expand_list(act["x"]), np.float32)
+    q, s = O.quantize_act(x)
+    assert list(q) == expand_list(act["xq"], int)
+    assert float(s[0]) == float(act["xs"])
+    fp4 = recs["FP4-A"]
+    blk = O.quantize_block(4, np.array(expand_list(fp4["w"]), np.float32))
+    y, d = O.gemv(4, blk[None, None, :], q[None], s[None], want_dots=True)
+    assert d[0, 0, 0] == int(act["dot_with"].split()[1])
+    assert y[0, 0] == float(act["y_with"].split()[1])
+
+
+def test_f16_decode_every_pattern_matches_numpy():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([O.f16_to_f64(int(h)) for h in pats])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+    # signed zeros keep their sign
+    assert math.copysign(1.0, O.f16_to_f64(0x8000)) == -1.0
+
+
+def _f16_cases():
+    rng = np.random.default_rng(5)
+    xs = [0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, 70000.0, 5.96e-8, 2.98e-8, 2.99e-8,
+          6.1035e-5, 6.1e-5, 1e-10, -3.3333333, 1.0 / 3.0]
+    # exact halfway points between binary16 neighbours (ties to even)
+    for h in list(range(1, 40)) + list(range(1020, 1030)) + list(range(0x3bf0, 0x3c10)) + [0x7bfe]:
+        a = np.uint16(h).view(np.float16).astype(np.float64)
+        b = np.uint16(h + 1).view(np.float16).astype(np.float64)
+        mid = (a + b) / 2
+        xs += [mid, -mid, np.nextafter(np.float32(mid), np.float32(0)),
+               np.nextafter(np.float32(mid), np.float32(1e9))]
+    xs += list(rng.standard_normal(3000) * 10.0 ** rng.uniform(-9, 5, 3000))
+    return np.array(xs, np.float32)
+
+
+def test_f32_to_f16_matches_numpy_rne():
+    xs = _f16_cases()
+    with np.errstate(over="ignore"):
+        ref = xs.astype(np.float16).view(np.uint16)
+    got = np.array([O.f32_to_f16(float(x)) for x in xs], np.uint16)
+    assert np.array_equal(ref, got)
+
+
+def _e2m1_value(m):
+    """OCP E2M1 (1 sign bit dropped): 2 exponent bits, 1 mantissa bit,
+    exponent bias 1; e = 0 is subnormal (mantissa * 0.5)."""
+    e, man = (m >> 1) & 3, m & 1
+    if e == 0:
+        return 0.5 * man
+    return (1.0 + 0.5 * man) * 2.0 ** (e - 1)
+
+
+def test_codebooks_closed_forms():
+    assert [O.codebook(2, c) for c in range(4)] == [-3, -1, 1, 3]
+    assert [O.codebook(3, c) for c in range(8)] == [-7, -5, -3, -1, 1, 3, 5, 7]
+    for c in range(16):
+        mag = 2.0 * _e2m1_value(c & 7)
+        want = -mag if c & 8 else mag
+        assert O.codebook(4, c) == want
+    # FP4 with one e8m0 scale is MX: max |E2M1| is 6, times 2 = 12
+    assert max(abs(O.codebook(4, c)) for c in range(16)) == 12
+
+
+def _values(fmt):
+    return {c: O.codebook(fmt, c) for c in range(4 if fmt == 2 else 8 if fmt == 3 else 16)
+            if not (fmt == 4 and c == 8)}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_nearest_code_is_an_argmin(fmt):
+    vals = _values(fmt)
+    rng = np.random.default_rng(fmt)
+    for t in rng.uniform(-16, 16, 4000):
+        c = O.nearest_code(fmt, float(t))
+        d = abs(t - vals[c])
+        assert all(d <= abs(t - v) for v in vals.values())
+
+
+@pytest.mark.parametrize("fmt,t,want", [
+    (2, 2.0, 3), (2, -2.0, -3), (2, 0.0, 1), (2, -0.0, 1), (2, 1e-30, 1), (2, -1e-30, -1),
+    (2, 99.0, 3), (2, -99.0, -3),
+    (3, 2.0, 3), (3, 4.0, 5), (3, 6.0, 7), (3, -2.0, -3), (3, -4.0, -5), (3, -6.0, -7),
+    (3, 0.0, 1), (3, -0.0, 1), (3, 8.0, 7),
+    # FP4: E2M1 round half to even, in int8 units (2x E2M1)
+    (4, 0.5, 0), (4, 1.5, 2), (4, 2.5, 2), (4, 3.5, 4), (4, 5.0, 4), (4, 7.0, 8), (4, 10.0, 8),
+    (4, -0.5, 0), (4, -1.5, -2), (4, -2.5, -2), (4, -3.5, -4), (4, -5.0, -4), (4, -7.0, -8),
+    (4, -10.0, -8), (4, 11.0, 12), (4, 15.9, 12), (4, -15.9, -12), (4, 0.0, 0), (4, -0.0, 0),
+])
+def test_nearest_code_ties_and_saturation(fmt, t, want):
+    c = O.nearest_code(fmt, t)
+    assert O.codebook(fmt, c) == want
+    if fmt == 4 and want == 0:
+        assert c == 0  # -0 is never emitted
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_pack_unpack_bijection(fmt):
+    rng = np.random.default_rng(10 + fmt)
+    ncode = 4 if fmt == 2 else 8 if fmt == 3 else 16
+    seen = set()
+    for _ in range(500):
+        codes = rng.integers(0, ncode, 32)
+        blk = O.pack_codes(fmt, codes)
+        assert len(blk) == O.code_bytes(fmt)
+        full = np.concatenate([blk, np.zeros(O.block_bytes(fmt) - len(blk), np.uint8)])
+        assert np.array_equal(O.unpack_codes(fmt, full), codes)
+        seen.add(bytes(blk))
+    assert len(seen) == 500
+
+
+def test_bit_positions_single_code():
+    """Each code lands in the documented bits and nowhere else."""
+    for t in range(32):
+        c = np.zeros(32, np.int64)
+        c[t] = 3
+        word = np.frombuffer(O.pack_codes(2, c).tobytes(), "<u4")
+        m, r = divmod(t, 16)
+        i, j = divmod(r, 4)
+        want = np.zeros(2, np.uint32)
+        want[m] = 3 << (8 * j + 2 * i)
+        assert np.array_equal(word, want)
+        c[t] = 4  # FP3 high bit only
+        word = np.frombuffer(O.pack_codes(3, c).tobytes(), "<u4")
+        want = np.zeros(3, np.uint32)
+        ih, jh = divmod(t, 4)
+        want[2] = 1 << (8 * jh + ih)
+        assert np.array_equal(word, want)
+        c[t] = 15
+        word = np.frombuffer(O.pack_codes(4, c).tobytes(), "<u4")
+        m, r = divmod(t, 8)
+        i, j = divmod(r, 4)
+        want = np.zeros(4, np.uint32)
+        want[m] = 15 << (8 * j + 4 * i)
+        assert np.array_equal(word, want)
+
+
+def _random_blocks(seed, n=300):
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        w = (rng.standard_normal(32) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        if k % 7 == 0:
+            w[rng.integers(0, 32, 3)] *= 10  # outliers
+        if k % 11 == 0:
+            w[rng.integers(0, 32, 8)] = 0
+        out.append(w)
+    return out
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_idempotent(fmt):
+    for w in _random_blocks(20 + fmt):
+        b1 = O.quantize_block(fmt, w)
+        w2 = O.dequantize_block(fmt, b1).astype(np.float32)
+        assert np.array_equal(O.dequantize_block(fmt, b1), w2.astype(np.float64))  # exact in fp32
+        b2 = O.quantize_block(fmt, w2)
+        assert np.array_equal(O.dequantize_block(fmt, b2), O.dequantize_block(fmt, b1))
+        assert bytes(b1) == bytes(b2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_scale_equivariance(fmt):
+    for w in _random_blocks(30 + fmt, 100):
+        b = O.quantize_block(fmt, w)
+        for k in (-3, 1, 4):
+            if fmt in (2, 3):
+                s = O.block_scale(fmt, b) * 2.0 ** k
+                if not (6.2e-5 < s < 6.0e4):  # binary16 normal range only
+                    continue
+            bk = O.quantize_block(fmt, (w * np.float32(2.0 ** k)).astype(np.float32))
+            assert np.array_equal(O.unpack_codes(fmt, bk), O.unpack_codes(fmt, b))
+            assert O.block_scale(fmt, bk) == O.block_scale(fmt, b) * 2.0 ** k
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_sign_symmetry(fmt):
+    for w in _random_blocks(40 + fmt, 150):
+        d = O.dequantize_block(fmt, O.quantize_block(fmt, w))
+        dn = O.dequantize_block(fmt, O.quantize_block(fmt, -w))
+        nz = w != 0
+        assert np.array_equal(dn[nz], -d[nz])
+        if fmt == 4:
+            assert np.array_equal(dn, -d + 0.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_error_bound(fmt):
+    for w in _random_blocks(50 + fmt):
+        blk = O.quantize_block(fmt, w)
+        S = O.block_scale(fmt, blk)
+        d = O.dequantize_block(fmt, blk)
+        err = np.abs(w.astype(np.float64) - d)
+        amax = float(np.max(np.abs(w)))
+        if fmt in (2, 3):
+            cmax = 3 if fmt == 2 else 7
+            # interior: half the spacing 2S; top clip: amax/S may exceed cmax
+            # by fp16 rounding of the scale (relative 2^-11)
+            bound = S * (1 + 1e-6) + amax * 2.0 ** -10
+            assert np.all(err <= bound)
+            assert S == pytest.approx(amax / cmax, rel=2 ** -10)
+        else:
+            t = np.abs(w.astype(np.float64)) / S
+            assert np.all(t < 16)  # floor rule keeps amax in [8, 16) * S
+            spacing = np.where(t <= 4, 1.0, np.where(t <= 8, 2.0, 4.0))
+            inside = t <= 12
+            assert np.all(err[inside] <= spacing[inside] / 2 * S * (1 + 1e-12))
+            assert np.all(err[~inside] <= (t[~inside] - 12) * S * (1 + 1e-12))
+
+
+@pytest.mark.parametrize("fmt", (2, 3))
+def test_fp16_scale_matches_numpy(fmt):
+    cmax = np.float32(3 if fmt == 2 else 7)
+    for w in _random_blocks(60 + fmt):
+        amax = np.max(np.abs(w))
+        want = (amax / cmax).astype(np.float16).view(np.uint16)
+        blk = O.quantize_block(fmt, w)
+        got = int(blk[-2]) | (int(blk[-1]) << 8)
+        assert got == int(want)
+
+
+@pytest.mark.parametrize("amax,E", [(6.0, 127), (1.0, 125), (0.999, 124), (8.0, 128), (7.99, 127),
+                                    (2.0 ** -130, 0), (2.0 ** -125, 0), (2.0 ** -124, 1),
+                                    (3.0e38, 252), (0.0, 0)])
+def test_fp4_exponent_hand_values(amax, E):
+    w = np.zeros(32, np.float32)
+    w[5] = np.float32(amax)
+    blk = O.quantize_block(4, w)
+    assert blk[16] == E
+
+
+def test_zero_and_tiny_blocks():
+    z = np.zeros(32, np.float32)
+    b2 = O.quantize_block(2, z)
+    assert list(O.unpack_codes(2, b2)) == [2] * 32 and O.block_scale(2, b2) == 0.0
+    b3 = O.quantize_block(3, z)
+    assert list(O.unpack_codes(3, b3)) == [4] * 32 and O.block_scale(3, b3) == 0.0
+    b4 = O.quantize_block(4, z)
+    assert list(O.unpack_codes(4, b4)) == [0] * 32 and b4[16] == 0
+    # fp16 scale underflows to 0 -> every weight decodes to 0
+    tiny = np.full(32, 1e-9, np.float32)
+    assert np.all(O.dequantize_block(2, O.quantize_block(2, tiny)) == 0.0)
+    # subnormal fp16 scale is kept
+    small = inputgen.raw_normal(1, 32, 1e-5)
+    b = O.quantize_block(2, small)
+    s = O.block_scale(2, b)
+    assert 0 < s < 6.1e-5
+
+
+def test_nonfinite_rejected():
+    for bad in (np.inf, -np.inf, np.nan):
+        w = np.zeros(32, np.float32)
+        w[3] = bad
+        for fmt in FMTS:
+            with pytest.raises(O.OracleError):
+                O.quantize_block(fmt, w)
+    big = np.full(32, 3.0e5, np.float32)  # 3e5/3 overflows binary16
+    with pytest.raises(O.OracleError):
+        O.quantize_block(2, big)
+    O.quantize_block(4, big)  # e8m0 has the range
+
+
+def test_matrix_is_rowwise_blocks():
+    W = inputgen.dense_weight(5, 96, seed=3, outliers=True)
+    for fmt in FMTS:
+        M = O.quantize_matrix(fmt, W)
+        assert M.shape == (5, 3, O.block_bytes(fmt))
+        for r in range(5):
+            for b in range(3):
+                assert bytes(M[r, b]) == bytes(O.quantize_block(fmt, W[r, 32 * b:32 * b + 32]))
