@@ -1,0 +1,49 @@
+"""Build librfx.so (host encoder + HIP kernels for gfx950) in-tree.
+
+    python -m bit_block_quantized_amd.build        # or build() from Python
+
+Always compiles (it is the "does it build" check); the library lands next
+to this file as librfx.so.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "librfx.so")
+
+SOURCES = ["rfx_host.cpp", "rfx_gemv.hip", "rfx_moe.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # Packed fp32 VALU ops (v_pk_*_f32) stay off: scalar fp32 only.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE-exact fp32 division and sqrt (the quantizers depend on it).
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", OUT + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(OUT + ".tmp", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

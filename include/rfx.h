@@ -1,0 +1,227 @@
+/*
+ * rfx — ROCmFPX-style block-quantized decode kernels for AMD Instinct MI355X
+ * (gfx950, CDNA4). C ABI.
+ *
+ * Pages cited (title, site):
+ *   [HM]  "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
+ *         (hellomarvisaitoday.com), paragraphs numbered from the top.
+ *   [AIN] "Token Freedom via APU: AMD Ryzen AI MAX+ 395 Runs DeepSeek V4
+ *         Flash at 32 tok/s on a 284B Model" (ainomam.com), by section.
+ *   [KK]  the kaikai365.com post on DeepSeek V4 Flash on Strix Halo, by
+ *         section heading.
+ *
+ * Conventions for every entry point:
+ *   - Return value: RFX_OK (0) or a negative RFX_E_* status. Nothing throws
+ *     across the ABI. rfx_last_error() gives a thread-local message for the
+ *     last failure.
+ *   - Arguments are validated synchronously, before any HIP call, so bad
+ *     shapes, null pointers and bad alignment fail the same way on a host
+ *     without a GPU.
+ *   - Device entry points enqueue on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream) and return at once; there is no
+ *     implicit synchronisation. A launch failure returns RFX_E_HIP.
+ *   - The caller allocates every buffer. The library allocates nothing and
+ *     keeps no device state. Where a workspace is taken it must be
+ *     zero-filled before its first use; every completed call leaves its
+ *     counters at zero again, so one zero fill serves any number of calls.
+ *     A workspace must not be shared by calls that can run concurrently.
+ *   - Device pointers must be 16-byte aligned unless stated otherwise.
+ *   - Floating-point inputs are assumed finite on the device side; the host
+ *     encoder checks and rejects non-finite weights.
+ */
+#ifndef RFX_H
+#define RFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    RFX_OK = 0,
+    RFX_E_INVAL = -1,      /* bad shape, format, count or null pointer */
+    RFX_E_ALIGN = -2,      /* pointer not aligned as required */
+    RFX_E_RANGE = -3,      /* non-finite weight, or fp16 scale overflow */
+    RFX_E_UNSUPPORTED = -4,/* valid request this build does not implement */
+    RFX_E_WORKSPACE = -5,  /* workspace missing or too small */
+    RFX_E_HIP = -6         /* a HIP runtime call or launch failed */
+};
+
+/* Block formats. A block is 32 consecutive weights of one row along the
+ * reduction dimension, stored as packed codes plus one scale ([HM] para 2:
+ * "packed low-bit codes plus one or two small scales"; this library uses one).
+ *   RFX_FP2: 2-bit codes, codebook {-3,-1,+1,+3}, fp16 scale: 10 B / block
+ *   RFX_FP3: 3-bit codes, codebook {-7,-5,...,+7}, fp16 scale: 14 B / block
+ *   RFX_FP4: 4-bit OCP E2M1 codes (value = 2 x E2M1, |v| <= 12), one e8m0
+ *            exponent byte E, scale 2^(E-128): 17 B / block (MXFP4)
+ * 10 / 14 / 17 bytes are the pages' 2.50 / 3.50 / 4.25 bits per weight
+ * ([HM] para 2; [KK] mixed-precision section). */
+enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4 };
+
+const char *rfx_status_str(int status);
+const char *rfx_last_error(void);
+const char *rfx_version(void);
+
+int rfx_block_bytes(int fmt); /* 10 / 14 / 17, or RFX_E_INVAL */
+int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 */
+int rfx_scale_bytes(int fmt); /* 2 / 2 / 1 */
+
+/* ------------------------------------------------------------------ */
+/* Host-side encoder (synchronous, host memory).                       */
+/* ------------------------------------------------------------------ */
+
+/* Quantize 32 fp32 weights into one canonical block: code bytes, then the
+ * scale (fp16 little-endian, or the e8m0 byte).
+ * Scale: FP2/FP3 s = fp16_rne(amax / 3 or 7) computed in fp32; FP4 E =
+ * clamp(floor(log2 amax) - 2 + 127, 0, 254) (OCP MX rule), amax = 0 -> 0.
+ * Code: nearest codebook value to w/s (fp32 division; FP4: w * 2^(128-E));
+ * ties go to the larger magnitude for FP2/FP3 (0 -> +1) and to the even
+ * E2M1 mantissa for FP4. A zero (or underflowed) FP2/FP3 scale codes every
+ * weight as +1 with s = 0.
+ * Bit layout of the code bytes, as little-endian 32-bit words:
+ *   FP2: weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
+ *   FP3: low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
+ *        at word 2 bit 8j+i
+ *   FP4: weight 8m+4i+j (m<4, i<2, j<4) at word m bits [8j+4i, 8j+4i+4)
+ * Returns RFX_E_RANGE for a non-finite weight or an fp16 scale overflow. */
+int rfx_quantize_block(int fmt, const float *w32, uint8_t *blk);
+int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
+
+/* ------------------------------------------------------------------ */
+/* Device weight layout.                                               */
+/* ------------------------------------------------------------------ */
+/* A matrix of `rows` x `cols` (cols % 32 == 0) is stored as tiles of 64 rows
+ * by 256 columns (8 blocks). Tile (g, s) covers rows 64g..64g+63 and blocks
+ * 8s..8s+7 and sits at byte offset (g * S + s) * tile_bytes, S = ceil(cols/
+ * 256). Inside a tile, 16-byte chunks are interleaved by row so that one
+ * 64-lane load of chunk c reads 1 KiB of contiguous memory:
+ *   byte offset of (chunk c, row r in 0..63) = c * 1024 + r * 16.
+ *   FP2 (tile 5120 B): chunks 0-3 = codes of blocks 2c, 2c+1 (8 B each);
+ *       chunk 4 = the eight fp16 scales.
+ *   FP3 (tile 7168 B): chunks 0-3 = low-bit words of blocks 2c, 2c+1;
+ *       chunks 4-5 = high-bit words of blocks 4(c-4)..4(c-4)+3 (4 B each);
+ *       chunk 6 = the eight fp16 scales.
+ *   FP4 (tile 8704 B): chunks 0-7 = codes of block c; then 64 rows x 8 B of
+ *       e8m0 scales at byte 8192 + r * 8.
+ * Rows beyond `rows` and blocks beyond cols/32 are zero (scale 0). Block
+ * bits are exactly those of the canonical block. A stack of `count`
+ * matrices (MoE experts) places matrix e at e * rfx_qmat_bytes(...). */
+typedef struct rfx_qmat {
+    int32_t fmt;      /* RFX_FP2 / RFX_FP3 / RFX_FP4 */
+    int32_t rows;     /* N (output features), >= 1 */
+    int32_t cols;     /* K (reduction length), multiple of 32 */
+    int32_t count;    /* matrices in the stack, >= 1 */
+    const void *data; /* device, count * rfx_qmat_bytes(fmt, rows, cols), 256-B aligned */
+} rfx_qmat;
+
+int64_t rfx_qmat_bytes(int fmt, int64_t rows, int64_t cols); /* one matrix, padded */
+
+/* fp32 row-major [rows][cols] (host) -> tiled layout (host buffer of
+ * rfx_qmat_bytes). Uses up to `threads` host threads (<= 0: hardware
+ * concurrency). Same encoder as rfx_quantize_block. */
+int rfx_quantize_matrix(int fmt, const float *W, int64_t rows, int64_t cols, void *tiled,
+                        int threads);
+/* Tiled layout (host) -> canonical blocks [rows][cols/32][block_bytes]. */
+int rfx_export_blocks(int fmt, const void *tiled, int64_t rows, int64_t cols, uint8_t *blocks);
+/* Canonical blocks (host) -> tiled layout (host), for pre-quantized data. */
+int rfx_import_blocks(int fmt, const uint8_t *blocks, int64_t rows, int64_t cols, void *tiled);
+
+/* ------------------------------------------------------------------ */
+/* Activations.                                                        */
+/* ------------------------------------------------------------------ */
+/* Quantize q columns of K fp32 values (K % 32 == 0), device to device.
+ * Per 32-block: s = amax / 127 (fp32, IEEE division), code = clamp(round
+ * half to even(x / s), -127, 127), all-zero block -> s = 0, codes 0; xsum =
+ * the block's integer sum of codes (used by the FP2/FP3 decoders, whose
+ * codebooks are affine in the code). Integer activations feed the integer
+ * dot products ([HM] para 3).
+ * x fp32 [q][K]; xq int8 [q][K]; xs fp32 [q][K/32]; xsum int32 [q][K/32].
+ * q >= 1. xq needs 16-B alignment, xs and xsum 4-B. */
+int rfx_quantize_act(const float *x, int q, int K, int8_t *xq, float *xs, int32_t *xsum,
+                     void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Fused dequantize-and-multiply (GEMV).                                */
+/* ------------------------------------------------------------------ */
+/* y[j][n] = sum_b S[n][b] * xs[j][b] * D[j][n][b], D the exact integer dot
+ * of block b of row n with column j's int8 block. Packed blocks are read
+ * once from HBM and expanded in registers; each decoded weight is applied
+ * to all q columns ([HM] para 3; [AIN] optimization-trio section: decode
+ * once for the four verification columns). fp32 accumulation.
+ * W: count must be 1 (use W->data of one expert for stacks). q in 1..4.
+ * xq [q][K], xs/xsum [q][K/32] as produced by rfx_quantize_act; y fp32
+ * [q][N] (4-B aligned).
+ * ws: zero-filled workspace of rfx_gemv_workspace_bytes(W, q) bytes, or
+ * NULL to run without splitting K across workgroups (slower for small N). */
+size_t rfx_gemv_workspace_bytes(const rfx_qmat *W, int q);
+int rfx_gemv(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum, int q,
+             float *y, void *ws, size_t ws_bytes, void *stream);
+int rfx_gemv_q1(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum,
+                float *y, void *ws, size_t ws_bytes, void *stream);
+int rfx_gemv_q4(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum,
+                float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Test hook: the same decode path, storing every per-block integer dot
+ * D[j][n][b] (int32 [q][N][K/32]) instead of the scaled sum. */
+int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,
+                         int32_t *dots, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* MoE decode layer.                                                   */
+/* ------------------------------------------------------------------ */
+/* Routed experts: gate and up (rows = inter, cols = hidden) and down
+ * (rows = hidden, cols = inter), `n_experts` stacked each ([HM] para 2 and
+ * [KK] ROCmFPX section: gate/up in FP2, down in FP3; any format is
+ * accepted). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
+ * or sh_gate.data == NULL for none. Router: fp32 [n_experts][hidden]
+ * weights and an optional fp32 [n_experts] bias. */
+typedef struct rfx_moe_layer {
+    int32_t hidden;    /* H, multiple of 32 */
+    int32_t inter;     /* I, multiple of 32 */
+    int32_t n_experts; /* E, 1..256 */
+    int32_t reserved;
+    rfx_qmat gate, up, down;
+    rfx_qmat sh_gate, sh_up, sh_down;
+    const float *router_w; /* device fp32 [E][H] */
+    const float *router_b; /* device fp32 [E], or NULL */
+} rfx_moe_layer;
+
+size_t rfx_moe_workspace_bytes(const rfx_moe_layer *L, int q, int k);
+
+/* Router for q tokens ([HM] para 3 and [KK] DSpark section: dedicated
+ * TOP_K and ARGSORT kernels). logits l = x.Wr^T + b (fp32); experts ranked
+ * by logit, equal logits to the lower id; top-k picked; weights = softmax
+ * over all experts of the picked logits, not renormalised. Pairs p = t*k+j
+ * are grouped by expert with a stable sort: pairs_sorted [q*k], expert_off
+ * [E+1] (exclusive prefix sum of per-expert counts). The tokens are also
+ * quantized for the experts (as rfx_quantize_act).
+ * x fp32 [q][H]; topk_idx int32 [q][k]; topk_w fp32 [q][k]; 1 <= k <= 8.
+ * q in 1..4 here (decode and speculative verification); larger q is the
+ * prefill path. */
+int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx,
+                       float *topk_w, int32_t *pairs_sorted, int32_t *expert_off, int8_t *xq,
+                       float *xs, int32_t *xsum, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFN and combine. For every pair (t, j) with expert e: g = G_e.x~_t,
+ * u = U_e.x~_t, h = silu(g) * u, h~ = activation-quantized h, o = D_e.h~;
+ * shared expert likewise with weight 1; y_t = o_shared + sum_j w_tj o_tj in
+ * slot order (deterministic, no float atomics). y fp32 [q][H]. */
+int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
+                const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
+                const int32_t *pairs_sorted, const int32_t *expert_off, float *y, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* Test hook: after rfx_moe_ffn with the same workspace, copy out the
+ * intermediate activations of the last call: h fp32 [(q*k)+q][I] (pairs in
+ * pair order, then the shared expert per token), h~ int8 and its scales.
+ * Any output pointer may be NULL. */
+int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, float *h,
+                         int8_t *hq, float *hs, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RFX_H */

@@ -1,0 +1,133 @@
+"""GPU parity of the activation quantizer and the fused block GEMV against
+the CPU oracle: quantized activations and per-block integer dots bit-exact,
+fp32 outputs within 1e-4 (floored relative), at small ragged shapes, at the
+1024 x 1024 FP4 workload and at the 7168 x 7168 FP2/FP3/FP4 workloads in
+the launch configuration the benchmark times (split-K with a workspace)."""
+
+import numpy as np
+import pytest
+
+import bit_block_quantized_amd as R
+import inputgen
+import oracle as O
+from gpu_common import TOL, need_gpu, quantize_on_gpu, rel_err, say, upload_matrix, workspace
+
+pytestmark = pytest.mark.gpu
+FMTS = (2, 3, 4)
+
+
+def _sync(torch):
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ activations
+
+@pytest.mark.parametrize("q,K", [(1, 32), (4, 544), (4, 7168), (3, 4096)])
+def test_act_quant_bit_exact(q, K):
+    torch = need_gpu()
+    say(f"act_quant q={q} K={K}")
+    x = inputgen.activations(q, K, seed=3) * np.float32(2.0)
+    x[0, :32] = 0.0  # a zero block
+    if K >= 64:  # exact rounding ties: amax 127 -> s = 1
+        x[-1, 32] = 127.0
+        x[-1, 33:63] = np.arange(-15, 15, dtype=np.float32) + np.float32(0.5)
+    xq, xs, xsum = quantize_on_gpu(torch, x)
+    _sync(torch)
+    oq, os_ = O.quantize_act(x)
+    assert np.array_equal(xq.cpu().numpy(), oq)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(xsum.cpu().numpy(), O.act_sums(oq))
+
+
+# ------------------------------------------------------------------ gemv
+
+def _run(torch, fmt, W, x, q, split, blocks=None):
+    """Returns (y_gpu, dots_gpu, y_oracle, dots_oracle)."""
+    N, K = W.shape
+    dW = upload_matrix(torch, fmt, W)
+    xq, xs, xsum = quantize_on_gpu(torch, x)
+    y = torch.full((q, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = workspace(torch, R.gemv_workspace_bytes(dW, q)) if split else None
+    R.gemv(dW, xq, xs, xsum, q, y, ws)
+    dots = torch.full((q, N, K // 32), -(2 ** 31), dtype=torch.int32, device="cuda")
+    R.debug_block_dots(dW, xq, xsum, q, dots)
+    _sync(torch)
+    if blocks is None:
+        blocks = O.quantize_matrix(fmt, W)
+    oq, os_ = O.quantize_act(x)
+    yo, do = O.gemv(fmt, blocks, oq, os_, want_dots=True)
+    return y.cpu().numpy(), dots.cpu().numpy(), yo, do
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("q", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [(200, 544), (64, 256), (1, 32), (65, 288), (130, 2080)])
+def test_gemv_small_shapes(fmt, q, shape):
+    torch = need_gpu()
+    N, K = shape
+    say(f"gemv small fmt={fmt} q={q} N={N} K={K}")
+    W = inputgen.dense_weight(N, K, seed=N + K + fmt, outliers=True)
+    x = inputgen.activations(q, K, seed=5)
+    for split in (False, True):
+        y, d, yo, do = _run(torch, fmt, W, x, q, split)
+        assert np.array_equal(d, do)
+        assert rel_err(y, yo) <= TOL, (split, rel_err(y, yo))
+
+
+def test_gemv_fp4_1024_q1():
+    """Dense FP4 1024 x 1024, W seed 0, one column seed 1."""
+    torch = need_gpu()
+    say("gemv fp4 1024x1024 q=1")
+    W = inputgen.dense_weight(1024, 1024, seed=0)
+    x = inputgen.activations(1, 1024, seed=1)
+    y, d, yo, do = _run(torch, 4, W, x, 1, split=True)
+    assert np.array_equal(d, do)
+    assert rel_err(y, yo) <= TOL
+
+
+_BIG = {}
+
+
+def _big(fmt):
+    if fmt not in _BIG:
+        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20}[fmt], outliers=True)
+        _BIG[fmt] = (W, O.quantize_matrix(fmt, W))
+    return _BIG[fmt]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("q", [1, 4])
+def test_gemv_7168_full(fmt, q):
+    """7168 x 7168 with 1% outliers, q columns seeds 1..q, split-K launch."""
+    torch = need_gpu()
+    say(f"gemv 7168 fmt={fmt} q={q}")
+    W, blocks = _big(fmt)
+    x = inputgen.activations(q, 7168, seed=1)
+    y, d, yo, do = _run(torch, fmt, W, x, q, split=True, blocks=blocks)
+    assert np.array_equal(d, do)
+    err = rel_err(y, yo)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_deterministic_and_columns_independent(fmt):
+    torch = need_gpu()
+    say(f"gemv determinism fmt={fmt}")
+    N, K = 7168, 4096
+    W = inputgen.dense_weight(N, K, seed=11)
+    dW = upload_matrix(torch, fmt, W)
+    x = inputgen.activations(4, K, seed=12)
+    xq, xs, xsum = quantize_on_gpu(torch, x)
+    ws = workspace(torch, R.gemv_workspace_bytes(dW, 4))
+    outs = []
+    for _ in range(3):  # the same workspace reused: counters reset each call
+        y = torch.empty((4, N), dtype=torch.float32, device="cuda")
+        R.gemv(dW, xq, xs, xsum, 4, y, ws)
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    for j in range(4):
+        ws1 = workspace(torch, R.gemv_workspace_bytes(dW, 1))
+        y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        R.gemv(dW, xq[j:j + 1], xs[j:j + 1], xsum[j:j + 1], 1, y1, ws1)
+        assert rel_err(y1.cpu().numpy()[0], outs[0][j]) <= 1e-6

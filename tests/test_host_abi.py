@@ -1,0 +1,185 @@
+"""CPU tests of librfx's host side: the library loads and exports every
+symbol the header declares; the host encoder and the tiled packer agree
+bit for bit with the oracle; argument validation fails before any HIP call.
+No GPU is touched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_block_quantized_amd as R
+import inputgen
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FMTS = (2, 3, 4)
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "rfx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rfx_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = R.lib()
+    names = _header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(R.EXPORTED)
+    assert R.lib().rfx_version().decode().startswith("rfx")
+
+
+def test_sizes():
+    for fmt, (bb, cb, sb, tile) in {2: (10, 8, 2, 5120), 3: (14, 12, 2, 7168),
+                                     4: (17, 16, 1, 8704)}.items():
+        assert R.block_bytes(fmt) == bb == O.block_bytes(fmt)
+        assert R.code_bytes(fmt) == cb and R.scale_bytes(fmt) == sb
+        assert R.qmat_bytes(fmt, 64, 256) == tile == 64 * 8 * bb
+        assert R.qmat_bytes(fmt, 65, 288) == 4 * tile
+    assert R.block_bytes(5) == -1
+
+
+def _adversarial_blocks():
+    rng = np.random.default_rng(77)
+    blocks = []
+    for k in range(400):
+        w = (rng.standard_normal(32) * 10.0 ** rng.uniform(-6, 3)).astype(np.float32)
+        blocks.append(w)
+    # exact ties for every format: amax fixes s = 1 (FP2: 3, FP3: 7), FP4 S = 1/2
+    for amax, grid in ((3.0, [2.0, -2.0, 0.0, -0.0, 1.0, 2.5]),
+                       (7.0, [2.0, 4.0, 6.0, -2.0, -4.0, -6.0, 0.0, -0.0]),
+                       (6.0, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -1.25, -2.5, -3.5])):
+        w = np.zeros(32, np.float32)
+        w[0] = amax
+        w[1:1 + len(grid)] = grid
+        blocks.append(w)
+    blocks.append(np.zeros(32, np.float32))
+    blocks.append(np.full(32, 1e-9, np.float32))     # fp16 scale underflow
+    blocks.append(np.full(32, 3e-6, np.float32))     # subnormal fp16 scale
+    blocks.append(np.full(32, -2.0 ** -140, np.float32))  # subnormal weights
+    w = np.zeros(32, np.float32)
+    w[7] = 2.0 ** -130
+    blocks.append(w)
+    return blocks
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_host_encoder_matches_oracle(fmt):
+    for w in _adversarial_blocks():
+        a = R.quantize_block(fmt, w)
+        b = O.quantize_block(fmt, w)
+        assert bytes(a) == bytes(b), (fmt, w)
+        assert np.array_equal(R.dequantize_block(fmt, a).astype(np.float64),
+                              O.dequantize_block(fmt, b))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 32), (64, 256), (65, 288), (200, 544), (130, 1024)])
+def test_tiled_packer_roundtrip(fmt, shape):
+    rows, cols = shape
+    W = inputgen.dense_weight(rows, cols, seed=rows + cols, outliers=True)
+    t = R.quantize_matrix(fmt, W, threads=3)
+    assert t.nbytes == R.qmat_bytes(fmt, rows, cols)
+    blocks = R.export_blocks(fmt, t, rows, cols)
+    assert np.array_equal(blocks, O.quantize_matrix(fmt, W))
+    assert np.array_equal(R.import_blocks(fmt, blocks), t)
+
+
+def test_tiled_layout_positions():
+    """A block's bytes land where the header says: tile (g, s), chunk c,
+    row r at c*1024 + r*16."""
+    rows, cols = 130, 600
+    for fmt in FMTS:
+        nb = cols // 32
+        bb = R.block_bytes(fmt)
+        blocks = np.zeros((rows, nb, bb), np.uint8)
+        r, b = 70, 9  # g = 1, lane 6, s = 1, bi = 1
+        blocks[r, b] = np.arange(1, bb + 1, dtype=np.uint8)
+        t = R.import_blocks(fmt, blocks)
+        S = -(-cols // 256)
+        tile = (1 * S + 1) * R.qmat_bytes(fmt, 64, 256)
+        lane, bi = 6, 1
+        if fmt == 4:
+            assert list(t[tile + bi * 1024 + lane * 16: tile + bi * 1024 + lane * 16 + 16]) == list(range(1, 17))
+            assert t[tile + 8192 + lane * 8 + bi] == 17
+        else:
+            c0 = tile + (bi // 2) * 1024 + lane * 16 + (bi % 2) * 8
+            assert list(t[c0:c0 + 8]) == list(range(1, 9))
+            if fmt == 3:
+                c1 = tile + (4 + bi // 4) * 1024 + lane * 16 + (bi % 4) * 4
+                assert list(t[c1:c1 + 4]) == [9, 10, 11, 12]
+                sc = tile + 6 * 1024 + lane * 16 + bi * 2
+                assert list(t[sc:sc + 2]) == [13, 14]
+            else:
+                sc = tile + 4 * 1024 + lane * 16 + bi * 2
+                assert list(t[sc:sc + 2]) == [9, 10]
+        assert int(t.astype(np.int64).sum()) == int(np.arange(1, bb + 1).sum())
+
+
+def test_encoder_errors():
+    w = np.zeros(32, np.float32)
+    w[0] = np.nan
+    with pytest.raises(R.RfxError) as e:
+        R.quantize_block(2, w)
+    assert e.value.status == -3
+    with pytest.raises(R.RfxError):
+        R.quantize_block(2, np.full(32, 3e5, np.float32))
+    with pytest.raises(R.RfxError) as e:
+        R.quantize_matrix(9, np.zeros((4, 32), np.float32))
+    assert e.value.status == -1
+    with pytest.raises(R.RfxError):
+        R.quantize_matrix(2, np.zeros((4, 40), np.float32))
+    W = np.zeros((70, 64), np.float32)
+    W[69, 3] = np.inf
+    with pytest.raises(R.RfxError) as e:
+        R.quantize_matrix(3, W, threads=4)
+    assert e.value.status == -3
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_device_entry_validation_without_gpu():
+    """Every check runs before the first HIP call."""
+    L = R.lib()
+    good = 0x7f0000000000  # aligned fake address; never dereferenced
+    W = R.QMat(2, 128, 512, 1, good)
+    null = None
+    st = L.rfx_gemv(None, _fake(good), _fake(good), _fake(good), 1, _fake(good), null, 0, null)
+    assert st == -1
+    st = L.rfx_gemv(ctypes.byref(W), _fake(good), _fake(good), _fake(good), 5, _fake(good), null, 0, null)
+    assert st == -1
+    st = L.rfx_gemv(ctypes.byref(W), None, _fake(good), _fake(good), 1, _fake(good), null, 0, null)
+    assert st == -1
+    st = L.rfx_gemv(ctypes.byref(W), _fake(good + 1), _fake(good), _fake(good), 1, _fake(good), null, 0, null)
+    assert st == -2
+    bad = R.QMat(2, 128, 500, 1, good)
+    assert L.rfx_gemv(ctypes.byref(bad), _fake(good), _fake(good), _fake(good), 1, _fake(good), null, 0, null) == -1
+    mis = R.QMat(2, 128, 512, 1, good + 16)
+    assert L.rfx_gemv(ctypes.byref(mis), _fake(good), _fake(good), _fake(good), 1, _fake(good), null, 0, null) == -2
+    stack = R.QMat(2, 128, 512, 3, good)
+    assert L.rfx_gemv(ctypes.byref(stack), _fake(good), _fake(good), _fake(good), 1, _fake(good), null, 0, null) == -1
+    # split-K workspace too small -> RFX_E_WORKSPACE, still before HIP
+    big = R.QMat(4, 7168, 7168, 1, good)
+    need = L.rfx_gemv_workspace_bytes(ctypes.byref(big), 4)
+    assert need > 0
+    st = L.rfx_gemv(ctypes.byref(big), _fake(good), _fake(good), _fake(good), 4, _fake(good),
+                    _fake(good), need - 4, null)
+    assert st == -5
+    assert L.rfx_quantize_act(_fake(good), 1, 40, _fake(good), _fake(good), _fake(good), null) == -1
+    assert L.rfx_quantize_act(None, 1, 64, _fake(good), _fake(good), _fake(good), null) == -1
+    assert L.rfx_debug_block_dots(ctypes.byref(W), _fake(good), _fake(good), 0, _fake(good), null) == -1
+    assert b"q" in L.rfx_last_error()
+
+
+def test_status_strings():
+    L = R.lib()
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert L.rfx_status_str(st)
+    assert L.rfx_status_str(-99) == b"unknown status"
