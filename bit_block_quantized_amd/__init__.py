@@ -245,3 +245,32 @@ def gemv_q4(W: DeviceQMat, xq, xs, xsum, y, ws=None, stream=None):
 def debug_block_dots(W: DeviceQMat, xq, xsum, q, dots, stream=None):
     _check(lib().rfx_debug_block_dots(W.ref(), _dptr(xq), _dptr(xsum), q, _dptr(dots),
                                       _stream(stream)))
+
+
+# ------------------------------------------------------------------ MoE
+
+def moe_workspace_bytes(layer, q: int, k: int) -> int:
+    return int(lib().rfx_moe_workspace_bytes(layer.ref(), q, k))
+
+
+def moe_route_topk(layer, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, ws,
+                   stream=None):
+    _check(lib().rfx_moe_route_topk(layer.ref(), _dptr(x), q, k, _dptr(topk_idx), _dptr(topk_w),
+                                    _dptr(pairs_sorted), _dptr(expert_off), _dptr(xq), _dptr(xs),
+                                    _dptr(xsum), _dptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+
+
+def moe_ffn(layer, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_off, y, ws,
+            stream=None):
+    _check(lib().rfx_moe_ffn(layer.ref(), q, k, _dptr(xq), _dptr(xs), _dptr(xsum), _dptr(topk_idx),
+                             _dptr(topk_w), _dptr(pairs_sorted), _dptr(expert_off), _dptr(y),
+                             _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_debug_hidden(layer, q, k, ws, h=None, hq=None, hs=None, stream=None):
+    _check(lib().rfx_moe_debug_hidden(layer.ref(), q, k, _dptr(ws), _dptr(h), _dptr(hq), _dptr(hs),
+                                      _stream(stream)))
+
+
+from .layer import DeviceMoeLayer, MoeBuffers  # noqa: E402,F401

@@ -1,0 +1,230 @@
+// Device-side decode core shared by the GEMV and MoE kernels (gfx950).
+//
+// Pages cited (title, site):
+//   [HM] "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
+//        (hellomarvisaitoday.com), paragraphs numbered from the top.
+//
+// [HM] para 3: packed blocks are read directly, codebooks are expanded with
+// byte-permute instructions in registers and feed integer dot products.
+// Here: one lane owns one output row of a 64-row x 8-block tile; the
+// activation block is uniform across the wave and lives in SGPRs, used as
+// the SGPR operand of v_dot4_i32_i8.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rfx.h"
+
+namespace rfx {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const int32_t __attribute__((address_space(4))) *sptr_i32;
+typedef const float __attribute__((address_space(4))) *sptr_f32;
+
+// Uniform pointer -> constant address space, so the compiler reads it with
+// scalar loads (s_load_dwordxN) into SGPRs.
+__device__ __forceinline__ sptr_i32 as_scalar_i32(const void *p) { return (sptr_i32)(uintptr_t)p; }
+__device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p) { return (sptr_f32)(uintptr_t)p; }
+
+template <int FMT>
+struct TileFmt {
+    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : 8704;
+    static constexpr int code_chunks = FMT == RFX_FP2 ? 4 : FMT == RFX_FP3 ? 6 : 8;
+};
+
+// ------------------------------------------------------------------
+// Selector / value bytes of one block, computed once for every column.
+// ------------------------------------------------------------------
+struct Sel8 {
+    int v[8];
+};
+
+// FP2: word m holds weights 16m..16m+15, group i (x dword 4m+i) in bits
+// 2i..2i+1 of each byte. The selector byte is the code c; the codebook is
+// v = 2c - 3, so sum(v x) = 2 sum(c x) - 3 sum(x).
+__device__ __forceinline__ Sel8 sel_fp2(uint32_t w0, uint32_t w1)
+{
+    Sel8 s;
+    s.v[0] = (int)(w0 & 0x03030303u);
+    s.v[1] = (int)((w0 >> 2) & 0x03030303u);
+    s.v[2] = (int)((w0 >> 4) & 0x03030303u);
+    s.v[3] = (int)((w0 >> 6) & 0x03030303u);
+    s.v[4] = (int)(w1 & 0x03030303u);
+    s.v[5] = (int)((w1 >> 2) & 0x03030303u);
+    s.v[6] = (int)((w1 >> 4) & 0x03030303u);
+    s.v[7] = (int)((w1 >> 6) & 0x03030303u);
+    return s;
+}
+
+// FP3: low two bits as FP2, high bit of weight 4i+j at bit 8j+i of h;
+// selector byte = lo | hi << 2 = the 3-bit code (v = 2c - 7).
+__device__ __forceinline__ Sel8 sel_fp3(uint32_t w0, uint32_t w1, uint32_t h)
+{
+    Sel8 s = sel_fp2(w0, w1);
+    s.v[0] |= (int)((h << 2) & 0x04040404u);
+    s.v[1] |= (int)((h << 1) & 0x04040404u);
+    s.v[2] |= (int)(h & 0x04040404u);
+    s.v[3] |= (int)((h >> 1) & 0x04040404u);
+    s.v[4] |= (int)((h >> 2) & 0x04040404u);
+    s.v[5] |= (int)((h >> 3) & 0x04040404u);
+    s.v[6] |= (int)((h >> 4) & 0x04040404u);
+    s.v[7] |= (int)((h >> 5) & 0x04040404u);
+    return s;
+}
+
+// FP4: nibble codes sign<<3 | m (m = E2M1 magnitude pattern). Two v_perm
+// lookups give the positive and negative value of each byte lane; a third
+// v_perm picks per byte on the sign bit. Values are 2 x E2M1 as int8.
+constexpr uint32_t kPosLo = 0x03020100u; // 0 1 2 3
+constexpr uint32_t kPosHi = 0x0C080604u; // 4 6 8 12
+constexpr uint32_t kNegLo = 0xFDFEFF00u; // 0 -1 -2 -3
+constexpr uint32_t kNegHi = 0xF4F8FAFCu; // -4 -6 -8 -12
+
+__device__ __forceinline__ int fp4_expand(uint32_t nib_shifted_word, uint32_t sign_shifted_word)
+{
+    const uint32_t idx = nib_shifted_word & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
+    const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
+    const uint32_t msel = (sign_shifted_word & 0x04040404u) | 0x03020100u;
+    return (int)__builtin_amdgcn_perm(neg, pos, msel);
+}
+
+__device__ __forceinline__ Sel8 sel_fp4(u32x4 c)
+{
+    Sel8 s;
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        s.v[2 * m] = fp4_expand(w[m], w[m] >> 1);
+        s.v[2 * m + 1] = fp4_expand(w[m] >> 4, w[m] >> 5);
+    }
+    return s;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16);
+}
+
+// ------------------------------------------------------------------
+// One 64-row x 8-block tile in registers (one lane = one row).
+// ------------------------------------------------------------------
+template <int FMT>
+struct TileRegs {
+    u32x4 c[TileFmt<FMT>::code_chunks];
+    u32x4 sc16; // FP2/FP3: eight fp16 scales
+    u32x2 sc8;  // FP4: eight e8m0 bytes
+};
+
+template <int FMT>
+__device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ tile, int lane)
+{
+    TileRegs<FMT> t;
+    const u32x4 *tp = reinterpret_cast<const u32x4 *>(tile) + lane;
+#pragma unroll
+    for (int k = 0; k < TileFmt<FMT>::code_chunks; k++)
+        t.c[k] = __builtin_nontemporal_load(tp + 64 * k);
+    if (FMT == RFX_FP4)
+        t.sc8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(tile + 8 * 1024) + lane);
+    else
+        t.sc16 = __builtin_nontemporal_load(tp + 64 * TileFmt<FMT>::code_chunks);
+    return t;
+}
+
+// Selector bytes and dequantization scale of block bi (0..7) of a tile.
+template <int FMT>
+__device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel8 &sel, float &sw)
+{
+    if (FMT == RFX_FP4) {
+        sel = sel_fp4(t.c[bi]);
+        const uint32_t e = ((bi < 4 ? t.sc8.x : t.sc8.y) >> (8 * (bi & 3))) & 0xffu;
+        sw = ldexpf(1.0f, (int)e - 128); // 2 x E2M1 codebook: scale 2^(E-128)
+    } else {
+        const uint32_t w0 = (bi & 1) ? t.c[bi >> 1].z : t.c[bi >> 1].x;
+        const uint32_t w1 = (bi & 1) ? t.c[bi >> 1].w : t.c[bi >> 1].y;
+        if (FMT == RFX_FP3) {
+            const u32x4 h4 = t.c[4 + (bi >> 2)];
+            const uint32_t h = (bi & 3) == 0 ? h4.x : (bi & 3) == 1 ? h4.y : (bi & 3) == 2 ? h4.z : h4.w;
+            sel = sel_fp3(w0, w1, h);
+        } else {
+            sel = sel_fp2(w0, w1);
+        }
+        const uint32_t sw2 = (bi >> 1) == 0 ? t.sc16.x : (bi >> 1) == 1 ? t.sc16.y : (bi >> 1) == 2 ? t.sc16.z : t.sc16.w;
+        sw = half_bits_to_float((bi & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+    }
+}
+
+// ------------------------------------------------------------------
+// Activation columns: int8 codes, fp32 block scales, int32 block sums.
+// Column j starts at element xoff[j] (a multiple of 32) of xq and at block
+// moff[j] of xs / xsum. Offsets are uniform (SGPRs).
+// ------------------------------------------------------------------
+template <int Q>
+struct XCols {
+    const int8_t *xq;
+    const float *xs;
+    const int32_t *xsum;
+    uint32_t xoff[Q];
+    uint32_t moff[Q];
+};
+
+template <int Q>
+struct XBlock {
+    int x[Q][8];
+    float sx[Q];
+    int sum[Q];
+};
+
+template <bool NEED_SUM, int Q>
+__device__ __forceinline__ XBlock<Q> load_xblock(const XCols<Q> &c, int b)
+{
+    XBlock<Q> xb;
+    const sptr_i32 xq = as_scalar_i32(c.xq), xsum = as_scalar_i32(c.xsum);
+    const sptr_f32 xs = as_scalar_f32(c.xs);
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        const uint32_t xo = (c.xoff[j] + 32u * (uint32_t)b) >> 2;
+        const uint32_t mo = c.moff[j] + (uint32_t)b;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            xb.x[j][i] = xq[xo + i];
+        xb.sx[j] = xs[mo];
+        xb.sum[j] = NEED_SUM ? xsum[mo] : 0;
+    }
+    return xb;
+}
+
+// Exact per-block integer dot D for column j (codebook offset folded in).
+template <int FMT, int Q>
+__device__ __forceinline__ int block_dot(const Sel8 &sel, const XBlock<Q> &xb, int j)
+{
+    int d = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        d = __builtin_amdgcn_sdot4(sel.v[i], xb.x[j][i], d, false);
+    if (FMT == RFX_FP2 || FMT == RFX_FP3) {
+        const int off = FMT == RFX_FP2 ? 3 : 7; // v = 2c - off
+        d = 2 * d - off * xb.sum[j];
+    }
+    return d;
+}
+
+template <int FMT, int Q, int NQ>
+__device__ __forceinline__ void accumulate_block(const Sel8 &sel, float sw, const XBlock<Q> &xb,
+                                                 float (&acc)[Q])
+{
+#pragma unroll
+    for (int j = 0; j < NQ; j++)
+        acc[j] += (sw * xb.sx[j]) * (float)block_dot<FMT, Q>(sel, xb, j);
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt at
+// their maxima: wait for every outstanding vector memory operation.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+} // namespace dev
+} // namespace rfx

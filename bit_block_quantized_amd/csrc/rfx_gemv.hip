@@ -36,6 +36,7 @@
 
 #include <cstdint>
 
+#include "rfx_decode.h"
 #include "rfx_internal.h"
 
 namespace rfx {
@@ -54,22 +55,7 @@ using namespace rfx;
 
 namespace {
 
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef const int32_t __attribute__((address_space(4))) *sptr_i32;
-typedef const float __attribute__((address_space(4))) *sptr_f32;
-
-// Uniform pointer -> constant address space, so the compiler reads it with
-// scalar loads (s_load_dwordxN) into SGPRs.
-__device__ __forceinline__ sptr_i32 as_scalar_i32(const void *p)
-{
-    return (sptr_i32)(uintptr_t)p;
-}
-__device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p)
-{
-    return (sptr_f32)(uintptr_t)p;
-}
+using namespace rfx::dev;
 
 // ------------------------------------------------------------------
 // Activation quantization: one lane per element, two 32-element blocks
@@ -106,88 +92,6 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float *__restrict_
     }
 }
 
-// ------------------------------------------------------------------
-// Per-block decode + integer dots.
-// ------------------------------------------------------------------
-
-// Selector bytes of one block, computed once and shared by every column.
-struct Sel8 {
-    int v[8];
-};
-
-__device__ __forceinline__ Sel8 sel_fp2(uint32_t w0, uint32_t w1)
-{
-    Sel8 s;
-    s.v[0] = (int)(w0 & 0x03030303u);
-    s.v[1] = (int)((w0 >> 2) & 0x03030303u);
-    s.v[2] = (int)((w0 >> 4) & 0x03030303u);
-    s.v[3] = (int)((w0 >> 6) & 0x03030303u);
-    s.v[4] = (int)(w1 & 0x03030303u);
-    s.v[5] = (int)((w1 >> 2) & 0x03030303u);
-    s.v[6] = (int)((w1 >> 4) & 0x03030303u);
-    s.v[7] = (int)((w1 >> 6) & 0x03030303u);
-    return s;
-}
-
-// FP3: low two bits as FP2, high bit of weight 4i+j at bit 8j+i of h;
-// selector byte = lo | hi << 2 = the 3-bit code.
-__device__ __forceinline__ Sel8 sel_fp3(uint32_t w0, uint32_t w1, uint32_t h)
-{
-    Sel8 s = sel_fp2(w0, w1);
-    s.v[0] |= (int)((h << 2) & 0x04040404u);
-    s.v[1] |= (int)((h << 1) & 0x04040404u);
-    s.v[2] |= (int)(h & 0x04040404u);
-    s.v[3] |= (int)((h >> 1) & 0x04040404u);
-    s.v[4] |= (int)((h >> 2) & 0x04040404u);
-    s.v[5] |= (int)((h >> 3) & 0x04040404u);
-    s.v[6] |= (int)((h >> 4) & 0x04040404u);
-    s.v[7] |= (int)((h >> 5) & 0x04040404u);
-    return s;
-}
-
-// FP4: nibble codes sign<<3 | m (m = E2M1 magnitude pattern). Two v_perm
-// lookups give the positive and negative value of each byte lane; a third
-// v_perm picks per byte on the sign bit. Values: 2 x E2M1 as int8.
-constexpr uint32_t kPosLo = 0x03020100u; // 0 1 2 3
-constexpr uint32_t kPosHi = 0x0C080604u; // 4 6 8 12
-constexpr uint32_t kNegLo = 0xFDFEFF00u; // 0 -1 -2 -3
-constexpr uint32_t kNegHi = 0xF4F8FAFCu; // -4 -6 -8 -12
-
-__device__ __forceinline__ int fp4_expand(uint32_t nib_shifted_word, uint32_t sign_shifted_word)
-{
-    const uint32_t idx = nib_shifted_word & 0x07070707u;
-    const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
-    const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
-    const uint32_t msel = (sign_shifted_word & 0x04040404u) | 0x03020100u;
-    return (int)__builtin_amdgcn_perm(neg, pos, msel);
-}
-
-__device__ __forceinline__ Sel8 sel_fp4(u32x4 c)
-{
-    Sel8 s;
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-        s.v[2 * m] = fp4_expand(w[m], w[m] >> 1);
-        s.v[2 * m + 1] = fp4_expand(w[m] >> 4, w[m] >> 5);
-    }
-    return s;
-}
-
-__device__ __forceinline__ int dot8(const Sel8 &s, sptr_i32 xp)
-{
-    int d = 0;
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-        d = __builtin_amdgcn_sdot4(s.v[i], xp[i], d, false);
-    return d;
-}
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
-{
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)bits16);
-}
-
 struct GemvArgs {
     const uint8_t *W;
     int N, K, S, nb, P;
@@ -199,136 +103,29 @@ struct GemvArgs {
     unsigned *slots; // split-K exchange slots (workspace)
 };
 
-template <int FMT>
-struct TileFmt {
-    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : 8704;
-};
-
-#ifndef RFX_PREFETCH_MAX_Q
-#define RFX_PREFETCH_MAX_Q 2
-#endif
-constexpr int kPrefetchMaxQ = RFX_PREFETCH_MAX_Q;
-
-// The activation block of every column, held in SGPRs (uniform).
-template <int Q>
-struct XBlock {
-    int x[Q][8];
-    float sx[Q];
-    int sum[Q];
-};
-
-template <int FMT, int Q>
-__device__ __forceinline__ XBlock<Q> load_xblock(const GemvArgs &a, int b)
-{
-    // 32-bit element offsets from one base pointer per array keep the
-    // address arithmetic to one SGPR per load (base pair + offset).
-    XBlock<Q> xb;
-    const sptr_i32 xq = as_scalar_i32(a.xq), xsum = as_scalar_i32(a.xsum);
-    const sptr_f32 xs = as_scalar_f32(a.xs);
-#pragma unroll
-    for (int j = 0; j < Q; j++) {
-        const uint32_t xo = ((uint32_t)j * (uint32_t)a.K + 32u * (uint32_t)b) >> 2;
-        const uint32_t mo = (uint32_t)j * (uint32_t)a.nb + (uint32_t)b;
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            xb.x[j][i] = xq[xo + i];
-        xb.sx[j] = xs[mo];
-        xb.sum[j] = (FMT == RFX_FP4) ? 0 : xsum[mo];
-    }
-    return xb;
-}
-
-// Accumulate one block b of one 64-row tile into acc[Q] (or store dots).
-template <int FMT, int Q, bool DOTS>
-__device__ __forceinline__ void block_step(const Sel8 &sel, float sw, const XBlock<Q> &xb, int b, int row,
-                                           const GemvArgs &a, float (&acc)[Q])
-{
-#pragma unroll
-    for (int j = 0; j < Q; j++) {
-        int d = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            d = __builtin_amdgcn_sdot4(sel.v[i], xb.x[j][i], d, false);
-        if (FMT == RFX_FP2 || FMT == RFX_FP3) {
-            // codebook v = 2c - off: D = 2 sum(c x) - off sum(x)
-            const int off = FMT == RFX_FP2 ? 3 : 7;
-            d = 2 * d - off * xb.sum[j];
-        }
-        if (DOTS) {
-            if (row < a.N)
-                a.dots[((size_t)j * a.N + row) * a.nb + b] = d;
-        } else {
-            acc[j] += (sw * xb.sx[j]) * (float)d;
-        }
-    }
-}
-
-// Registers holding one 64-row x 8-block tile for one lane.
-template <int FMT>
-struct TileRegs {
-    static constexpr int kCode = FMT == RFX_FP2 ? 4 : FMT == RFX_FP3 ? 6 : 8; // code chunks
-    u32x4 c[kCode];
-    u32x4 sc16; // FP2/FP3: eight fp16 scales
-    u32x2 sc8;  // FP4: eight e8m0 bytes
-};
-
-template <int FMT>
-__device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ tile, int lane)
-{
-    TileRegs<FMT> t;
-    const u32x4 *tp = reinterpret_cast<const u32x4 *>(tile) + lane;
-#pragma unroll
-    for (int k = 0; k < TileRegs<FMT>::kCode; k++)
-        t.c[k] = __builtin_nontemporal_load(tp + 64 * k);
-    if (FMT == RFX_FP4)
-        t.sc8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(tile + 8 * 1024) + lane);
-    else
-        t.sc16 = __builtin_nontemporal_load(tp + 64 * TileRegs<FMT>::kCode);
-    return t;
-}
-
 template <int FMT, int Q, bool DOTS>
 __device__ __forceinline__ void compute_tile(const TileRegs<FMT> &t, int s, int row, const GemvArgs &a,
-                                             float (&acc)[Q])
+                                             const XCols<Q> &xc, float (&acc)[Q])
 {
     const int b0 = s * 8;
     const int nvalid = min(8, a.nb - b0); // blocks of this tile inside K
-    // The next block's activations are fetched while this block is decoded.
-    XBlock<Q> xcur = load_xblock<FMT, Q>(a, b0);
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
         if (bi >= nvalid)
             break;
-        // One block of prefetch fits the SGPR budget only for q <= 2; wider
-        // blocks are fetched in one batch right before use.
-        constexpr bool kPrefetch = Q <= kPrefetchMaxQ;
-        XBlock<Q> xnext = xcur;
-        if (kPrefetch && bi + 1 < nvalid)
-            xnext = load_xblock<FMT, Q>(a, b0 + bi + 1);
+        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b0 + bi);
         Sel8 sel;
         float sw;
-        if (FMT == RFX_FP4) {
-            sel = sel_fp4(t.c[bi]);
-            const uint32_t e = ((bi < 4 ? t.sc8.x : t.sc8.y) >> (8 * (bi & 3))) & 0xffu;
-            sw = ldexpf(1.0f, (int)e - 128);
-        } else {
-            const uint32_t w0 = (bi & 1) ? t.c[bi >> 1].z : t.c[bi >> 1].x;
-            const uint32_t w1 = (bi & 1) ? t.c[bi >> 1].w : t.c[bi >> 1].y;
-            if (FMT == RFX_FP3) {
-                const u32x4 h4 = t.c[4 + (bi >> 2)];
-                const uint32_t h = (bi & 3) == 0 ? h4.x : (bi & 3) == 1 ? h4.y : (bi & 3) == 2 ? h4.z : h4.w;
-                sel = sel_fp3(w0, w1, h);
-            } else {
-                sel = sel_fp2(w0, w1);
+        decode_block<FMT>(t, bi, sel, sw);
+        if (DOTS) {
+            if (row < a.N) {
+#pragma unroll
+                for (int j = 0; j < Q; j++)
+                    a.dots[((size_t)j * a.N + row) * a.nb + b0 + bi] = block_dot<FMT, Q>(sel, xb, j);
             }
-            const uint32_t sw2 = (bi >> 1) == 0 ? t.sc16.x : (bi >> 1) == 1 ? t.sc16.y : (bi >> 1) == 2 ? t.sc16.z : t.sc16.w;
-            sw = half_bits_to_float((bi & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        } else {
+            accumulate_block<FMT, Q, Q>(sel, sw, xb, acc);
         }
-        block_step<FMT, Q, DOTS>(sel, sw, xcur, b0 + bi, row, a, acc);
-        if (kPrefetch)
-            xcur = xnext;
-        else if (bi + 1 < nvalid)
-            xcur = load_xblock<FMT, Q>(a, b0 + bi + 1);
     }
 }
 
@@ -345,9 +142,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     const int g = blockIdx.y, p = blockIdx.x; // grid = (P, G)
     const int row = g * 64 + lane;
     float acc[Q];
+    XCols<Q> xc;
+    xc.xq = a.xq;
+    xc.xs = a.xs;
+    xc.xsum = a.xsum;
 #pragma unroll
-    for (int j = 0; j < Q; j++)
+    for (int j = 0; j < Q; j++) {
         acc[j] = 0.0f;
+        xc.xoff[j] = (uint32_t)j * (uint32_t)a.K;
+        xc.moff[j] = (uint32_t)j * (uint32_t)a.nb;
+    }
 
     const int nw = a.P * W, v = p * W + wave;
     const int s_begin = (int)((unsigned)(a.S * v) / (unsigned)nw);
@@ -359,7 +163,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
             TileRegs<FMT> nxt = cur;
             if (s + 1 < s_end)
                 nxt = load_tile<FMT>(gbase + (size_t)(s + 1) * TileFmt<FMT>::bytes, lane);
-            compute_tile<FMT, Q, DOTS>(cur, s, row, a, acc);
+            compute_tile<FMT, Q, DOTS>(cur, s, row, a, xc, acc);
             cur = nxt;
         }
     }
@@ -395,9 +199,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     // atomic exchange (agent scope, coherent across XCDs); the first to
     // arrive leaves its value (stored inverted so the zero-filled slot
     // means "empty"), the second adds it to its own and climbs on. Each
-    // node is one two-term fp32 sum, which is exact-order independent
-    // (a + b == b + a), so the result does not depend on arrival order.
-    // The second arriver clears the slot, leaving the workspace zeroed.
+    // node is one two-term fp32 sum, and a + b == b + a exactly, so the
+    // result does not depend on arrival order. The second arriver clears
+    // the slot, leaving the workspace zeroed for the next call.
     unsigned *slots = a.slots + (size_t)g * (a.P - 1) * Q * 64;
     bool active[Q];
 #pragma unroll

@@ -1,32 +1,879 @@
-// MoE decode layer: router (top-k + stable bucketing) and expert FFN.
-// (Placeholder entry points; the kernels follow.)
+// MoE decode layer for gfx950: router (logits, softmax, top-k, stable
+// bucketing of (token, slot) pairs by expert) and the expert FFN (fused
+// gate/up + SwiGLU + requantization, then down + shared expert + combine).
+//
+// Pages cited (title, site):
+//   [HM]  "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
+//         (hellomarvisaitoday.com), paragraphs numbered from the top.
+//   [AIN] "Token Freedom via APU: AMD Ryzen AI MAX+ 395 Runs DeepSeek V4
+//         Flash at 32 tok/s on a 284B Model" (ainomam.com), by section.
+//   [KK]  the kaikai365.com post on DeepSeek V4 Flash on Strix Halo, by
+//         section heading.
+//
+// The model has 256 routed experts plus one shared expert and activates six
+// per token ([AIN] introduction); routed gate/up are stored in FP2, down in
+// FP3, dense/sensitive projections in FP4 ([HM] para 2; [KK] ROCmFPX
+// section); routing is a TOP_K + ARGSORT step ([HM] para 3; [KK] DSpark
+// section). Expert weights stream once per decode step; every expert that
+// several tokens picked is decoded once for all of them.
+//
+// Launches per layer: route (1), gate/up (1), down + combine (1). Each
+// kernel finishes its cross-workgroup step with a last-arriver pattern
+// (agent-scope write-through stores + an arrival counter), so outputs are
+// deterministic and no extra launch is needed.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
+#include "rfx_decode.h"
 #include "rfx_internal.h"
 
 using namespace rfx;
+using namespace rfx::dev;
+
+namespace {
+
+constexpr int kMaxK = 8;
+constexpr int kMaxE = 256;
+constexpr int kMaxDecodeQ = 4;
+
+// ------------------------------------------------------------------
+// Workspace layout (bytes, 256-aligned regions). Zero-filled once by the
+// caller; counters return to zero at the end of every call.
+// ------------------------------------------------------------------
+struct MoeWs {
+    float *logits;      // [q][E]
+    unsigned *route_cnt;
+    float *h;           // [NP][I]   NP = q*k + q (pairs, then shared per token)
+    int8_t *hq;         // [NP][I]
+    float *hs;          // [NP][I/32]
+    int32_t *hsum;      // [NP][I/32]
+    float *o;           // [NP][H]
+    unsigned *comb_cnt; // [H/64]
+    size_t bytes;
+};
+
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+MoeWs carve(void *base, int q, int k, int E, int H, int I)
+{
+    MoeWs w{};
+    const size_t NP = (size_t)q * k + q;
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        size_t o = off;
+        off += align256(n);
+        return o;
+    };
+    const size_t o_logits = take((size_t)q * E * 4);
+    const size_t o_rc = take(4);
+    const size_t o_h = take(NP * I * 4);
+    const size_t o_hq = take(NP * I);
+    const size_t o_hs = take(NP * (I / 32) * 4);
+    const size_t o_hsum = take(NP * (I / 32) * 4);
+    const size_t o_o = take(NP * H * 4);
+    const size_t o_cc = take((size_t)(H / 64 + 1) * 4);
+    w.bytes = off;
+    char *b = static_cast<char *>(base);
+    if (b) {
+        w.logits = reinterpret_cast<float *>(b + o_logits);
+        w.route_cnt = reinterpret_cast<unsigned *>(b + o_rc);
+        w.h = reinterpret_cast<float *>(b + o_h);
+        w.hq = reinterpret_cast<int8_t *>(b + o_hq);
+        w.hs = reinterpret_cast<float *>(b + o_hs);
+        w.hsum = reinterpret_cast<int32_t *>(b + o_hsum);
+        w.o = reinterpret_cast<float *>(b + o_o);
+        w.comb_cnt = reinterpret_cast<unsigned *>(b + o_cc);
+    }
+    return w;
+}
+
+// ------------------------------------------------------------------
+// Shared device helpers.
+// ------------------------------------------------------------------
+
+// Activation quantization of one 32-element block held by 32 lanes
+// (lanes 0-31 or 32-63 of a wave): s = amax/127, code = clamp(rne(v/s)).
+__device__ __forceinline__ void quant32(float v, int8_t *q_out, float *s_out, int32_t *sum_out,
+                                        bool write_meta)
+{
+#pragma clang fp contract(off)
+    float a = fabsf(v);
+    for (int o = 16; o > 0; o >>= 1)
+        a = fmaxf(a, __shfl_xor(a, o, 32));
+    const float s = a / 127.0f;
+    int qv = 0;
+    if (s != 0.0f) {
+        float r = rintf(v / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        qv = (int)r;
+    }
+    int sum = qv;
+    for (int o = 16; o > 0; o >>= 1)
+        sum += __shfl_xor(sum, o, 32);
+    *q_out = (int8_t)qv;
+    if (write_meta) {
+        *s_out = s;
+        *sum_out = sum;
+    }
+}
+
+// Sum over the whole workgroup (blockDim.x threads, multiple of 64).
+__device__ __forceinline__ float block_sum(float v, float *scratch)
+{
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        scratch[wave] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int w = 0; w < nw; w++)
+        t += scratch[w];
+    return t;
+}
+
+// ------------------------------------------------------------------
+// Router (decode: q <= 4 tokens).
+// ------------------------------------------------------------------
+struct RouteArgs {
+    const float *x;  // [q][H]
+    const float *wr; // [E][H]
+    const float *wb; // [E] or null
+    int q, k, E, H;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *pairs_sorted;
+    int32_t *expert_off;
+    int8_t *xq;
+    float *xs;
+    int32_t *xsum;
+    float *logits;
+    unsigned *cnt;
+};
+
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
+{
+    __shared__ float scratch[8];
+    __shared__ int s_last;
+    __shared__ int s_idx[kMaxDecodeQ * kMaxK];
+    const int tid = threadIdx.x;
+
+    // (1) quantize the tokens for the experts (grid-stride, 32 lanes a block)
+    const int nel = a.q * a.H;
+    for (int base = blockIdx.x * 256; base < nel; base += gridDim.x * 256) {
+        const int i = base + tid;
+        const float v = i < nel ? a.x[i] : 0.0f;
+        int8_t qv;
+        float sv;
+        int32_t sm;
+        quant32(v, &qv, &sv, &sm, true);
+        if (i < nel) {
+            a.xq[i] = qv;
+            if ((tid & 31) == 0) {
+                a.xs[i >> 5] = sv;
+                a.xsum[i >> 5] = sm;
+            }
+        }
+    }
+
+    // (2) logits of this workgroup's experts, fixed summation order
+    for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
+        const float *wrow = a.wr + (size_t)e * a.H;
+        float part[kMaxDecodeQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int h = tid * 4; h < a.H; h += 1024) {
+            const float4 w4 = *reinterpret_cast<const float4 *>(wrow + h);
+            for (int t = 0; t < a.q; t++) {
+                const float4 x4 = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h);
+                part[t] += w4.x * x4.x + w4.y * x4.y + w4.z * x4.z + w4.w * x4.w;
+            }
+        }
+        for (int t = 0; t < a.q; t++) {
+            float l = block_sum(part[t], scratch);
+            if (a.wb)
+                l += a.wb[e];
+            if (tid == 0)
+                __hip_atomic_store(a.logits + (size_t)t * a.E + e, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(a.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last)
+        return;
+
+    // (3) last workgroup: softmax and top-k, one wave per token
+    const int lane = tid & 63, wave = tid >> 6;
+    if (wave < a.q) {
+        const int t = wave;
+        float l[4];
+        bool taken[4];
+        float m = -INFINITY;
+        for (int r = 0; r < 4; r++) {
+            const int e = lane + 64 * r;
+            l[r] = e < a.E ? __hip_atomic_load(a.logits + (size_t)t * a.E + e, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : -INFINITY;
+            taken[r] = e >= a.E;
+            m = fmaxf(m, l[r]);
+        }
+        for (int o = 32; o > 0; o >>= 1)
+            m = fmaxf(m, __shfl_xor(m, o, 64));
+        float z = 0.0f;
+        for (int r = 0; r < 4; r++)
+            z += (lane + 64 * r) < a.E ? expf(l[r] - m) : 0.0f;
+        for (int o = 32; o > 0; o >>= 1)
+            z += __shfl_xor(z, o, 64);
+        for (int j = 0; j < a.k; j++) {
+            // this lane's best untaken (largest logit, then lowest id)
+            float bv = -INFINITY;
+            int be = 0x7fffffff;
+            for (int r = 0; r < 4; r++) {
+                const int e = lane + 64 * r;
+                if (!taken[r] && (l[r] > bv || (l[r] == bv && e < be))) {
+                    bv = l[r];
+                    be = e;
+                }
+            }
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oe = __shfl_xor(be, o, 64);
+                if (ov > bv || (ov == bv && oe < be)) {
+                    bv = ov;
+                    be = oe;
+                }
+            }
+            for (int r = 0; r < 4; r++)
+                if (lane + 64 * r == be)
+                    taken[r] = true;
+            if (lane == 0) {
+                a.topk_idx[t * a.k + j] = be;
+                a.topk_w[t * a.k + j] = expf(bv - m) / z;
+                s_idx[t * a.k + j] = be;
+            }
+        }
+    }
+    __syncthreads();
+
+    // (4) stable bucketing of the q*k pairs by expert (pair p = t*k + j)
+    const int np = a.q * a.k;
+    int cnt_e = 0; // thread e counts pairs of expert e
+    for (int e = tid; e < a.E; e += 256) {
+        int c = 0;
+        for (int p = 0; p < np; p++)
+            c += s_idx[p] == e;
+        cnt_e = c;
+    }
+    // exclusive scan over experts (E <= 256: one value per thread)
+    __shared__ int s_scan[256];
+    s_scan[tid] = tid < a.E ? cnt_e : 0;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int v = tid >= o ? s_scan[tid - o] : 0;
+        __syncthreads();
+        s_scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < a.E)
+        a.expert_off[tid] = s_scan[tid] - cnt_e;
+    if (tid == 0)
+        a.expert_off[a.E] = np;
+    __syncthreads();
+    if (tid < np) {
+        const int e = s_idx[tid];
+        int rank = 0;
+        for (int p = 0; p < tid; p++)
+            rank += s_idx[p] == e;
+        int before = 0; // pairs of experts below e
+        for (int p = 0; p < np; p++)
+            before += s_idx[p] < e;
+        a.pairs_sorted[before + rank] = tid;
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------
+// Slot plan: slot i < n_active is the i-th expert (in id order) that has
+// pairs; slot n_active is the shared expert (when present).
+// ------------------------------------------------------------------
+struct SlotInfo {
+    int kind;   // 0 = none, 1 = routed expert, 2 = shared expert
+    int expert; // routed expert id
+    int pb, pe; // pair range in pairs_sorted
+    int n_slots;
+};
+
+__device__ __forceinline__ SlotInfo find_slot(int slot, const int32_t *__restrict__ expert_off, int E,
+                                              bool has_shared)
+{
+    __shared__ SlotInfo s_info;
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 64) {
+        // lane holds experts lane, lane+64, lane+128, lane+192
+        int act[4], c = 0;
+        for (int r = 0; r < 4; r++) {
+            const int e = lane + 64 * r;
+            act[r] = e < E && expert_off[e + 1] > expert_off[e];
+        }
+        // order experts by id: position of expert e = (# active with id < e);
+        // scan per r-row: row r covers ids 64r..64r+63
+        int total = 0, found_e = -1;
+        for (int r = 0; r < 4; r++) {
+            const unsigned long long bal = __ballot(act[r]);
+            const int rank = total + __popcll(bal & ((1ull << lane) - 1ull));
+            if (act[r] && rank == slot)
+                found_e = lane + 64 * r;
+            total += __popcll(bal);
+        }
+        // the finder lane publishes
+        const unsigned long long fb = __ballot(found_e >= 0);
+        if (lane == 0) {
+            s_info.n_slots = total + (has_shared ? 1 : 0);
+            s_info.kind = 0;
+            s_info.expert = -1;
+            s_info.pb = s_info.pe = 0;
+            if (has_shared && slot == total)
+                s_info.kind = 2;
+        }
+        if (fb) {
+            const int src = __ffsll((long long)fb) - 1;
+            const int e = __shfl(found_e, src, 64);
+            if (lane == 0) {
+                s_info.kind = 1;
+                s_info.expert = e;
+                s_info.pb = expert_off[e];
+                s_info.pe = expert_off[e + 1];
+            }
+        }
+        (void)c;
+    }
+    __syncthreads();
+    const SlotInfo r = s_info;
+    return r;
+}
+
+// ------------------------------------------------------------------
+// Expert gate/up + SwiGLU + requantization of h.
+// ------------------------------------------------------------------
+struct FfnArgs {
+    // routed stacks and shared expert (data pointers, per-matrix byte strides)
+    const uint8_t *gate, *up, *down;
+    size_t gate_stride, up_stride, down_stride;
+    const uint8_t *sh_gate, *sh_up, *sh_down;
+    int fmt_g, fmt_u, fmt_d, fmt_sg, fmt_su, fmt_sd;
+    int E, H, I, q, k;
+    bool has_shared;
+    const int8_t *xq;
+    const float *xs;
+    const int32_t *xsum;
+    const int32_t *topk_idx;
+    const float *topk_w;
+    const int32_t *pairs_sorted;
+    const int32_t *expert_off;
+    float *y; // [q][H]
+    MoeWs ws;
+};
+
+// Column j of a slot: its h / output row index and its activation token.
+template <int NE>
+struct SlotCols {
+    int out_idx[NE]; // pair id (routed) or q*k + t (shared)
+    int token[NE];
+};
+
+template <int NE>
+__device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnArgs &a)
+{
+    SlotCols<NE> c;
+    const sptr_i32 ps = as_scalar_i32(a.pairs_sorted);
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        if (si.kind == 2) {
+            c.token[j] = j;
+            c.out_idx[j] = a.q * a.k + j;
+        } else {
+            const int p = ps[si.pb + j];
+            c.token[j] = p / a.k;
+            c.out_idx[j] = p;
+        }
+    }
+    return c;
+}
+
+template <int FG, int NE>
+__device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W,
+                            float *red)
+{
+    constexpr int FU = FG;
+    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    XCols<NE> xc;
+    xc.xq = a.xq;
+    xc.xs = a.xs;
+    xc.xsum = a.xsum;
+    const int nbH = a.H / 32;
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        xc.xoff[j] = (uint32_t)cols.token[j] * (uint32_t)a.H;
+        xc.moff[j] = (uint32_t)cols.token[j] * (uint32_t)nbH;
+    }
+    const int S = (a.H + 255) / 256;
+    const uint8_t *gm, *um;
+    if (si.kind == 2) {
+        gm = a.sh_gate;
+        um = a.sh_up;
+    } else {
+        gm = a.gate + a.gate_stride * (size_t)si.expert;
+        um = a.up + a.up_stride * (size_t)si.expert;
+    }
+    gm += (size_t)g * S * TileFmt<FG>::bytes;
+    um += (size_t)g * S * TileFmt<FU>::bytes;
+    float ag[NE], au[NE];
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        ag[j] = 0.0f;
+        au[j] = 0.0f;
+    }
+    const int s_begin = (int)((unsigned)(S * wave) / (unsigned)W);
+    const int s_end = (int)((unsigned)(S * (wave + 1)) / (unsigned)W);
+    if (s_begin < s_end) {
+        TileRegs<FG> cg = load_tile<FG>(gm + (size_t)s_begin * TileFmt<FG>::bytes, lane);
+        TileRegs<FU> cu = load_tile<FU>(um + (size_t)s_begin * TileFmt<FU>::bytes, lane);
+        for (int s = s_begin; s < s_end; s++) {
+            TileRegs<FG> ng = cg;
+            TileRegs<FU> nu = cu;
+            if (s + 1 < s_end) {
+                ng = load_tile<FG>(gm + (size_t)(s + 1) * TileFmt<FG>::bytes, lane);
+                nu = load_tile<FU>(um + (size_t)(s + 1) * TileFmt<FU>::bytes, lane);
+            }
+            const int b0 = s * 8, nvalid = min(8, nbH - b0);
+#pragma unroll
+            for (int bi = 0; bi < 8; bi++) {
+                if (bi >= nvalid)
+                    break;
+                const XBlock<NE> xb = load_xblock<true, NE>(xc, b0 + bi);
+                Sel8 sel;
+                float sw;
+                decode_block<FG>(cg, bi, sel, sw);
+                accumulate_block<FG, NE, NE>(sel, sw, xb, ag);
+                decode_block<FU>(cu, bi, sel, sw);
+                accumulate_block<FU, NE, NE>(sel, sw, xb, au);
+            }
+            cg = ng;
+            cu = nu;
+        }
+    }
+    // fixed-order reduction over waves; red[w][m][j][lane], m = gate/up
+#define RED_GU(w, m, j) red[(((w) * 2 + (m)) * kMaxDecodeQ + (j)) * 64 + lane]
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        RED_GU(wave, 0, j) = ag[j];
+        RED_GU(wave, 1, j) = au[j];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    const int row = g * 64 + lane; // row of the intermediate dimension
+    const int nbI = a.I / 32;
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        float gv = RED_GU(0, 0, j), uv = RED_GU(0, 1, j);
+        for (int w = 1; w < W; w++) {
+            gv += RED_GU(w, 0, j);
+            uv += RED_GU(w, 1, j);
+        }
+        // SwiGLU: silu(g) * u
+        const float hv = row < a.I ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
+        const size_t idx = (size_t)cols.out_idx[j];
+        int8_t qv;
+        float sv;
+        int32_t sm;
+        quant32(hv, &qv, &sv, &sm, true);
+        if (row < a.I) {
+            a.ws.h[idx * a.I + row] = hv;
+            a.ws.hq[idx * a.I + row] = qv;
+            if ((lane & 31) == 0) {
+                a.ws.hs[idx * nbI + (row >> 5)] = sv;
+                a.ws.hsum[idx * nbI + (row >> 5)] = sm;
+            }
+        }
+    }
+}
+
+template <int FG, int FS>
+__global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
+{
+    __shared__ float red[8 * 2 * kMaxDecodeQ * 64];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const SlotInfo si = find_slot(blockIdx.x, a.expert_off, a.E, a.has_shared);
+    if (si.kind == 0)
+        return;
+    const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
+    if (si.kind == 2) {
+        switch (ne) {
+        case 1: gateup_body<FS, 1>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 2: gateup_body<FS, 2>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 3: gateup_body<FS, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 4: gateup_body<FS, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
+        default: break;
+        }
+    } else {
+        switch (ne) {
+        case 1: gateup_body<FG, 1>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 2: gateup_body<FG, 2>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 3: gateup_body<FG, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 4: gateup_body<FG, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
+        default: break;
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// Expert down projection, shared expert and the weighted combine.
+// ------------------------------------------------------------------
+template <int FD, int NE>
+__device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
+{
+    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    XCols<NE> xc;
+    xc.xq = a.ws.hq;
+    xc.xs = a.ws.hs;
+    xc.xsum = a.ws.hsum;
+    const int nbI = a.I / 32;
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        xc.xoff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)a.I;
+        xc.moff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)nbI;
+    }
+    const int S = (a.I + 255) / 256;
+    const uint8_t *dm = si.kind == 2 ? a.sh_down : a.down + a.down_stride * (size_t)si.expert;
+    dm += (size_t)g * S * TileFmt<FD>::bytes;
+    float ao[NE];
+#pragma unroll
+    for (int j = 0; j < NE; j++)
+        ao[j] = 0.0f;
+    const int s_begin = (int)((unsigned)(S * wave) / (unsigned)W);
+    const int s_end = (int)((unsigned)(S * (wave + 1)) / (unsigned)W);
+    if (s_begin < s_end) {
+        TileRegs<FD> cd = load_tile<FD>(dm + (size_t)s_begin * TileFmt<FD>::bytes, lane);
+        for (int s = s_begin; s < s_end; s++) {
+            TileRegs<FD> nd = cd;
+            if (s + 1 < s_end)
+                nd = load_tile<FD>(dm + (size_t)(s + 1) * TileFmt<FD>::bytes, lane);
+            const int b0 = s * 8, nvalid = min(8, nbI - b0);
+#pragma unroll
+            for (int bi = 0; bi < 8; bi++) {
+                if (bi >= nvalid)
+                    break;
+                const XBlock<NE> xb = load_xblock<FD != RFX_FP4, NE>(xc, b0 + bi);
+                Sel8 sel;
+                float sw;
+                decode_block<FD>(cd, bi, sel, sw);
+                accumulate_block<FD, NE, NE>(sel, sw, xb, ao);
+            }
+            cd = nd;
+        }
+    }
+#define RED_D(w, j) red[((w) * kMaxDecodeQ + (j)) * 64 + lane]
+#pragma unroll
+    for (int j = 0; j < NE; j++)
+        RED_D(wave, j) = ao[j];
+    __syncthreads();
+    if (wave == 0) {
+        const int row = g * 64 + lane;
+#pragma unroll
+        for (int j = 0; j < NE; j++) {
+            float v = RED_D(0, j);
+            for (int w = 1; w < W; w++)
+                v += RED_D(w, j);
+            if (row < a.H)
+                __hip_atomic_store(a.ws.o + (size_t)cols.out_idx[j] * a.H + row, v, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int FD, int FSD>
+__global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
+{
+    __shared__ float red[16 * kMaxDecodeQ * 64];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const int g = blockIdx.y;
+    const SlotInfo si = find_slot(blockIdx.x, a.expert_off, a.E, a.has_shared);
+    if (si.kind == 0)
+        return;
+    const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
+    if (si.kind == 2) {
+        switch (ne) {
+        case 1: down_body<FSD, 1>(a, si, g, lane, wave, W, red); break;
+        case 2: down_body<FSD, 2>(a, si, g, lane, wave, W, red); break;
+        case 3: down_body<FSD, 3>(a, si, g, lane, wave, W, red); break;
+        case 4: down_body<FSD, 4>(a, si, g, lane, wave, W, red); break;
+        default: break;
+        }
+    } else {
+        switch (ne) {
+        case 1: down_body<FD, 1>(a, si, g, lane, wave, W, red); break;
+        case 2: down_body<FD, 2>(a, si, g, lane, wave, W, red); break;
+        case 3: down_body<FD, 3>(a, si, g, lane, wave, W, red); break;
+        case 4: down_body<FD, 4>(a, si, g, lane, wave, W, red); break;
+        default: break;
+        }
+    }
+    // Last slot to finish this row group combines, in fixed slot order:
+    // y[t] = o_shared[t] + sum_j w[t][j] * o[t*k + j].
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    __shared__ int s_last;
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(a.ws.comb_cnt + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (unsigned)(si.n_slots - 1);
+    __syncthreads();
+    if (!s_last)
+        return;
+    const int row = g * 64 + lane;
+    if (wave == 0 && row < a.H) {
+        for (int t = 0; t < a.q; t++) {
+            float acc = a.has_shared ? __hip_atomic_load(a.ws.o + (size_t)(a.q * a.k + t) * a.H + row,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                     : 0.0f;
+            for (int j = 0; j < a.k; j++) {
+                const float w = a.topk_w[t * a.k + j];
+                const float ov = __hip_atomic_load(a.ws.o + (size_t)(t * a.k + j) * a.H + row,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc += w * ov;
+            }
+            a.y[(size_t)t * a.H + row] = acc;
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(a.ws.comb_cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------
+// Host-side helpers.
+// ------------------------------------------------------------------
+int check_layer(const rfx_moe_layer *L)
+{
+    if (!L)
+        return fail(RFX_E_INVAL, "MoE layer descriptor is NULL");
+    if (L->n_experts < 1 || L->n_experts > kMaxE)
+        return fail(RFX_E_INVAL, "n_experts=%d (must be 1..%d)", L->n_experts, kMaxE);
+    if (L->hidden < 32 || L->hidden % 32 || L->inter < 32 || L->inter % 32)
+        return fail(RFX_E_INVAL, "hidden=%d inter=%d must be positive multiples of 32", L->hidden, L->inter);
+    int st;
+    if ((st = check_qmat(&L->gate, "gate", true)) || (st = check_qmat(&L->up, "up", true)) ||
+        (st = check_qmat(&L->down, "down", true)))
+        return st;
+    if (L->gate.rows != L->inter || L->gate.cols != L->hidden || L->up.rows != L->inter ||
+        L->up.cols != L->hidden || L->down.rows != L->hidden || L->down.cols != L->inter)
+        return fail(RFX_E_INVAL, "expert matrix shapes do not match hidden=%d inter=%d", L->hidden, L->inter);
+    if (L->gate.fmt != L->up.fmt)
+        return fail(RFX_E_UNSUPPORTED, "gate and up must share a block format (fused gate/up kernel)");
+    if (L->sh_gate.data && L->sh_gate.fmt != L->sh_up.fmt)
+        return fail(RFX_E_UNSUPPORTED, "shared gate and up must share a block format");
+    if (L->gate.count != L->n_experts || L->up.count != L->n_experts || L->down.count != L->n_experts)
+        return fail(RFX_E_INVAL, "expert stacks must hold n_experts=%d matrices", L->n_experts);
+    if (L->sh_gate.data) {
+        if ((st = check_qmat(&L->sh_gate, "sh_gate", false)) || (st = check_qmat(&L->sh_up, "sh_up", false)) ||
+            (st = check_qmat(&L->sh_down, "sh_down", false)))
+            return st;
+        if (L->sh_gate.rows != L->inter || L->sh_gate.cols != L->hidden || L->sh_up.rows != L->inter ||
+            L->sh_up.cols != L->hidden || L->sh_down.rows != L->hidden || L->sh_down.cols != L->inter)
+            return fail(RFX_E_INVAL, "shared expert shapes do not match hidden/inter");
+    }
+    return check_ptr(L->router_w, 16, "router_w");
+}
+
+template <int FG>
+int launch_gateup(int fs, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st)
+{
+    switch (fs) {
+    case RFX_FP2: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP2>), grid, block, 0, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP3>), grid, block, 0, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP4>), grid, block, 0, st, a); break;
+    }
+    return hip_status("gate/up launch");
+}
+
+template <int FD>
+int launch_down(int fsd, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st)
+{
+    switch (fsd) {
+    case RFX_FP2: hipLaunchKernelGGL((down_kernel<FD, RFX_FP2>), grid, block, 0, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((down_kernel<FD, RFX_FP3>), grid, block, 0, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((down_kernel<FD, RFX_FP4>), grid, block, 0, st, a); break;
+    }
+    return hip_status("down launch");
+}
+
+int waves_for(int wgs, int tiles, int max_waves)
+{
+    const int target = 3072; // ~3 waves per SIMD over 256 CUs
+    int W = (target + wgs - 1) / wgs;
+    W = W < 1 ? 1 : W > max_waves ? max_waves : W;
+    return W > tiles ? tiles : W;
+}
+
+} // namespace
 
 extern "C" {
 
-size_t rfx_moe_workspace_bytes(const rfx_moe_layer *, int, int) { return 0; }
-
-int rfx_moe_route_topk(const rfx_moe_layer *, const float *, int, int, int32_t *, float *, int32_t *,
-                       int32_t *, int8_t *, float *, int32_t *, void *, size_t, void *)
+size_t rfx_moe_workspace_bytes(const rfx_moe_layer *L, int q, int k)
 {
-    return fail(RFX_E_UNSUPPORTED, "rfx_moe_route_topk: not built yet");
+    if (!L || q < 1 || k < 1 || L->n_experts < 1 || L->hidden < 32 || L->inter < 32)
+        return 0;
+    return carve(nullptr, q, k, L->n_experts, L->hidden, L->inter).bytes;
 }
 
-int rfx_moe_ffn(const rfx_moe_layer *, int, int, const int8_t *, const float *, const int32_t *,
-                const int32_t *, const float *, const int32_t *, const int32_t *, float *, void *,
-                size_t, void *)
+int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx,
+                       float *topk_w, int32_t *pairs_sorted, int32_t *expert_off, int8_t *xq, float *xs,
+                       int32_t *xsum, void *ws, size_t ws_bytes, void *stream)
 {
-    return fail(RFX_E_UNSUPPORTED, "rfx_moe_ffn: not built yet");
+    int st = check_layer(L);
+    if (st)
+        return st;
+    if (k < 1 || k > kMaxK || k > L->n_experts)
+        return fail(RFX_E_INVAL, "k=%d (must be 1..%d and <= n_experts)", k, kMaxK);
+    if (q < 1)
+        return fail(RFX_E_INVAL, "q=%d", q);
+    if (q > kMaxDecodeQ)
+        return fail(RFX_E_UNSUPPORTED, "rfx_moe_route_topk: q=%d > %d (prefill routing not built)", q,
+                    kMaxDecodeQ);
+    if ((st = check_ptr(x, 16, "x")) || (st = check_ptr(topk_idx, 4, "topk_idx")) ||
+        (st = check_ptr(topk_w, 4, "topk_w")) || (st = check_ptr(pairs_sorted, 4, "pairs_sorted")) ||
+        (st = check_ptr(expert_off, 4, "expert_off")) || (st = check_ptr(xq, 16, "xq")) ||
+        (st = check_ptr(xs, 4, "xs")) || (st = check_ptr(xsum, 4, "xsum")) || (st = check_ptr(ws, 256, "ws")))
+        return st;
+    if (L->router_b && (st = check_ptr(L->router_b, 4, "router_b")))
+        return st;
+    MoeWs w = carve(ws, q, k, L->n_experts, L->hidden, L->inter);
+    if (ws_bytes < w.bytes)
+        return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    RouteArgs a{};
+    a.x = x;
+    a.wr = L->router_w;
+    a.wb = L->router_b;
+    a.q = q;
+    a.k = k;
+    a.E = L->n_experts;
+    a.H = L->hidden;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.pairs_sorted = pairs_sorted;
+    a.expert_off = expert_off;
+    a.xq = xq;
+    a.xs = xs;
+    a.xsum = xsum;
+    a.logits = w.logits;
+    a.cnt = w.route_cnt;
+    const int grid = L->n_experts < 128 ? L->n_experts : 128;
+    hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+    return hip_status("route launch");
 }
 
-int rfx_moe_debug_hidden(const rfx_moe_layer *, int, int, const void *, float *, int8_t *, float *,
-                         void *)
+int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs, const int32_t *xsum,
+                const int32_t *topk_idx, const float *topk_w, const int32_t *pairs_sorted,
+                const int32_t *expert_off, float *y, void *ws, size_t ws_bytes, void *stream)
 {
-    return fail(RFX_E_UNSUPPORTED, "rfx_moe_debug_hidden: not built yet");
+    int st = check_layer(L);
+    if (st)
+        return st;
+    if (k < 1 || k > kMaxK || k > L->n_experts || q < 1)
+        return fail(RFX_E_INVAL, "q=%d k=%d", q, k);
+    if (q > kMaxDecodeQ)
+        return fail(RFX_E_UNSUPPORTED, "rfx_moe_ffn: q=%d > %d (prefill path not built)", q, kMaxDecodeQ);
+    if ((st = check_ptr(xq, 16, "xq")) || (st = check_ptr(xs, 4, "xs")) || (st = check_ptr(xsum, 4, "xsum")) ||
+        (st = check_ptr(topk_idx, 4, "topk_idx")) || (st = check_ptr(topk_w, 4, "topk_w")) ||
+        (st = check_ptr(pairs_sorted, 4, "pairs_sorted")) || (st = check_ptr(expert_off, 4, "expert_off")) ||
+        (st = check_ptr(y, 4, "y")) || (st = check_ptr(ws, 256, "ws")))
+        return st;
+    MoeWs w = carve(ws, q, k, L->n_experts, L->hidden, L->inter);
+    if (ws_bytes < w.bytes)
+        return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    FfnArgs a{};
+    a.gate = static_cast<const uint8_t *>(L->gate.data);
+    a.up = static_cast<const uint8_t *>(L->up.data);
+    a.down = static_cast<const uint8_t *>(L->down.data);
+    a.gate_stride = (size_t)rfx_qmat_bytes(L->gate.fmt, L->inter, L->hidden);
+    a.up_stride = (size_t)rfx_qmat_bytes(L->up.fmt, L->inter, L->hidden);
+    a.down_stride = (size_t)rfx_qmat_bytes(L->down.fmt, L->hidden, L->inter);
+    a.has_shared = L->sh_gate.data != nullptr;
+    a.sh_gate = static_cast<const uint8_t *>(L->sh_gate.data);
+    a.sh_up = static_cast<const uint8_t *>(L->sh_up.data);
+    a.sh_down = static_cast<const uint8_t *>(L->sh_down.data);
+    a.fmt_g = L->gate.fmt;
+    a.fmt_u = L->up.fmt;
+    a.fmt_d = L->down.fmt;
+    a.fmt_sg = a.has_shared ? L->sh_gate.fmt : L->gate.fmt;
+    a.fmt_su = a.has_shared ? L->sh_up.fmt : L->up.fmt;
+    a.fmt_sd = a.has_shared ? L->sh_down.fmt : L->down.fmt;
+    a.E = L->n_experts;
+    a.H = L->hidden;
+    a.I = L->inter;
+    a.q = q;
+    a.k = k;
+    a.xq = xq;
+    a.xs = xs;
+    a.xsum = xsum;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.pairs_sorted = pairs_sorted;
+    a.expert_off = expert_off;
+    a.y = y;
+    a.ws = w;
+    const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
+    const hipStream_t s = (hipStream_t)stream;
+    const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);
+    const int SH = (int)ceil_div(L->hidden, 256), SI = (int)ceil_div(L->inter, 256);
+    {
+        const int W = waves_for(max_slots * GI, SH, 8);
+        dim3 grid(max_slots, GI), block(64 * W);
+        switch (a.fmt_g) {
+        case RFX_FP2: st = launch_gateup<RFX_FP2>(a.fmt_sg, a, grid, block, s); break;
+        case RFX_FP3: st = launch_gateup<RFX_FP3>(a.fmt_sg, a, grid, block, s); break;
+        case RFX_FP4: st = launch_gateup<RFX_FP4>(a.fmt_sg, a, grid, block, s); break;
+        }
+        if (st)
+            return st;
+    }
+    {
+        const int W = waves_for(max_slots * GH, SI, 16);
+        dim3 grid(max_slots, GH), block(64 * W);
+        switch (a.fmt_d) {
+        case RFX_FP2: st = launch_down<RFX_FP2>(a.fmt_sd, a, grid, block, s); break;
+        case RFX_FP3: st = launch_down<RFX_FP3>(a.fmt_sd, a, grid, block, s); break;
+        case RFX_FP4: st = launch_down<RFX_FP4>(a.fmt_sd, a, grid, block, s); break;
+        }
+    }
+    return st;
+}
+
+int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, float *h, int8_t *hq, float *hs,
+                         void *stream)
+{
+    int st = check_layer(L);
+    if (st)
+        return st;
+    if (q < 1 || q > kMaxDecodeQ || k < 1 || k > kMaxK)
+        return fail(RFX_E_INVAL, "q=%d k=%d", q, k);
+    if (!ws)
+        return fail(RFX_E_INVAL, "ws is NULL");
+    MoeWs w = carve(const_cast<void *>(ws), q, k, L->n_experts, L->hidden, L->inter);
+    const size_t NP = (size_t)q * k + q;
+    const hipStream_t s = (hipStream_t)stream;
+    if (h && hipMemcpyAsync(h, w.h, NP * L->inter * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return hip_status("debug copy h");
+    if (hq && hipMemcpyAsync(hq, w.hq, NP * L->inter, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return hip_status("debug copy hq");
+    if (hs && hipMemcpyAsync(hs, w.hs, NP * (L->inter / 32) * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return hip_status("debug copy hs");
+    return RFX_OK;
 }
 
 } // extern "C"
