@@ -1,16 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused block-dequantize GEMV on one MI355X.
+"""Benchmark of the fused block-dequantize GEMV and the MoE decode layer on
+one MI355X.
 
-Step = one pass of the dense-GEMV workload: 7168 x 7168 weights in each of
-FP2 (10 B / 32 weights), FP3 (14 B) and FP4 (17 B), each run with q = 1 and
-q = 4 activation columns (six GEMVs). Weights are N(0, 0.02) with 1%
-outliers x10 (seeds 0 / 10 / 20); columns N(0, 1), seeds 1..q. Every format
-keeps R copies of its matrix at distinct addresses (R x size >= 512 MB, twice
-the 256 MB last-level cache) and each launch uses the next copy, so weights
-stream from HBM. Inputs are resident in HBM before timing starts.
+Step (the headline `value`) = one pass of the dense-GEMV workload: 7168 x
+7168 weights in each of FP2 (10 B / 32 weights), FP3 (14 B) and FP4 (17 B),
+each with q = 1 and q = 4 activation columns (six GEMVs). Weights are
+N(0, 0.02) with 1% outliers x10 (seeds 0 / 10 / 20); columns N(0, 1), seeds
+1..q. Each format keeps R copies of its matrix at distinct addresses
+(R x size >= 512 MB, twice the 256 MB last-level cache); launch i uses copy
+i mod R, so weights stream from HBM. Inputs are resident in HBM before the
+timed region; steps are replayed from a HIP graph.
 
 value = algorithmic bytes of the step (packed weights + quantized
 activations read) / step time, in GB/s.
+
+Extra fields: per-kernel timings, the MoE decode layer (256 experts, hidden
+4096, intermediate 2048, FP2 gate/up, FP3 down, FP4 shared, q = 4, top-6)
+and the 8-layer stack (top-4, Zipf(1.1) router bias, q = 1 and q = 4), the
+HBM copy reference and the CPU oracle on a bounded sample.
 
 Prints one JSON line. Only one GPU is supported.
 """
@@ -29,6 +36,11 @@ N = K = 7168
 FORMATS = (2, 3, 4)
 SEEDS = {2: 0, 3: 10, 4: 20}
 LLC_BYTES = 256 << 20
+MOE_H, MOE_I, MOE_E = 4096, 2048, 256
+
+
+def log(*a):
+    print("#", *a, file=sys.stderr, flush=True)
 
 
 def algorithmic_bytes(R, fmt, q, n=N, k=K):
@@ -37,7 +49,9 @@ def algorithmic_bytes(R, fmt, q, n=N, k=K):
     return weights, acts, q * n * 4
 
 
-def build_workload(torch, R, inputgen):
+# ------------------------------------------------------------------ GEMV
+
+def build_gemv(torch, R, inputgen):
     work = {}
     for fmt in FORMATS:
         W = inputgen.dense_weight(N, K, seed=SEEDS[fmt], outliers=True)
@@ -58,8 +72,8 @@ def build_workload(torch, R, inputgen):
         xs = torch.empty((q, K // 32), dtype=torch.float32, device="cuda")
         xsum = torch.empty((q, K // 32), dtype=torch.int32, device="cuda")
         R.quantize_act(xd, xq, xs, xsum)
-        y = torch.empty((q, N), dtype=torch.float32, device="cuda")
-        acts[q] = {"x": x, "xq": xq, "xs": xs, "xsum": xsum, "y": y}
+        acts[q] = {"xq": xq, "xs": xs, "xsum": xsum,
+                   "y": torch.empty((q, N), dtype=torch.float32, device="cuda")}
     ws = {}
     for fmt in FORMATS:
         for q in (1, 4):
@@ -69,23 +83,133 @@ def build_workload(torch, R, inputgen):
     return work, acts, ws
 
 
-def launch(R, work, acts, ws, fmt, q, i, stream):
+def gemv_launch(R, work, acts, ws, fmt, q, i):
     mats = work[fmt]["mats"]
     a = acts[q]
-    R.gemv(mats[i % len(mats)], a["xq"], a["xs"], a["xsum"], q, a["y"], ws[(fmt, q)], stream)
+    R.gemv(mats[i % len(mats)], a["xq"], a["xs"], a["xsum"], q, a["y"], ws[(fmt, q)])
 
 
-def time_kernel(torch, R, work, acts, ws, fmt, q, iters, stream):
-    for i in range(20):
-        launch(R, work, acts, ws, fmt, q, i, stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+def graph_of(torch, fn, n):
+    """Capture fn(0..n-1) into one graph (after a warm-up on a side stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(min(n, 3)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps):
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(iters):
-        launch(R, work, acts, ws, fmt, q, i, stream)
+    for _ in range(reps):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / iters  # us per launch
+    return e0.elapsed_time(e1) / reps  # ms per replay
+
+
+def time_eager(torch, fn, n):
+    for i in range(10):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+# ------------------------------------------------------------------- MoE
+
+def build_moe_layers(torch, R, inputgen, n_layers):
+    """n_layers distinct seeded layers; each carries both routers (no bias
+    for the single-layer top-6 workload, Zipf bias for the stack)."""
+    layers = []
+    for l in range(n_layers):
+        t0 = time.time()
+        wfn = (lambda layer: (lambda e, m, r, c: inputgen.expert_weight(layer, e, m, r, c)))(l)
+        dev = R.DeviceMoeLayer.build(MOE_H, MOE_I, MOE_E, wfn, inputgen.router_weight(l, MOE_E, MOE_H),
+                                     None, workers=16)
+        zb = torch.from_numpy(inputgen.zipf_router_bias(l, MOE_E)).cuda()
+        zipf = R.DeviceMoeLayer(MOE_H, MOE_I, MOE_E, dev.gate, dev.up, dev.down, dev.sh,
+                                dev.router_w, zb)
+        layers.append((dev, zipf))
+        log(f"moe layer {l} built in {time.time() - t0:.1f} s")
+    return layers
+
+
+def moe_bytes(R, layer, topk_idx, q):
+    """Algorithmic bytes of one layer call: router weights, shared expert,
+    every distinct routed expert once, token activations and h~ read."""
+    w = layer.weight_bytes(topk_idx.reshape(-1).tolist())
+    k = topk_idx.shape[1]
+    acts = q * MOE_H * 4 + q * MOE_H + (q * MOE_H // 32) * 8  # fp32 x (router) + x~
+    acts += (q * k + q) * (MOE_I + (MOE_I // 32) * 8)          # h~ into down
+    return w + acts
+
+
+def bench_moe(torch, R, inputgen, layers, reps):
+    out = {}
+    # single layer, q = 4, top-6, rotated over the distinct layers
+    q, k = 4, 6
+    bufs = [R.MoeBuffers(lay[0], q, k) for lay in layers]
+    xs = [torch.from_numpy(inputgen.tokens(l, 7, q, MOE_H)).cuda() for l in range(len(layers))]
+
+    def one(i):
+        l = i % len(layers)
+        bufs[l].run(layers[l][0], xs[l])
+
+    for l in range(len(layers)):
+        one(l)
+    torch.cuda.synchronize()
+    nbytes = [moe_bytes(R, layers[l][0], bufs[l].topk_idx.cpu().numpy(), q) for l in range(len(layers))]
+    distinct = [len(set(bufs[l].topk_idx.cpu().numpy().reshape(-1).tolist())) for l in range(len(layers))]
+    g = graph_of(torch, one, len(layers))
+    ms = time_graph(torch, g, reps) / len(layers)
+    avg_bytes = sum(nbytes) / len(nbytes)
+    out["layer_q4_top6"] = {"us": round(ms * 1e3, 2), "bytes": int(avg_bytes),
+                            "GBps": round(avg_bytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(avg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "distinct_experts": distinct, "rotated_layers": len(layers),
+                            "eager_us": round(time_eager(torch, one, 4 * len(layers)) * 1e3, 2)}
+    log(f"moe layer q=4 top-6: {ms * 1e3:.1f} us")
+    # 8-layer stack, top-4, Zipf bias, residual fused into the combine
+    for q in (1, 4):
+        k = 4
+        sb = [R.MoeBuffers(lay[1], q, k) for lay in layers]
+        x0 = torch.from_numpy(inputgen.tokens(100, 0, q, MOE_H)).cuda()
+        xbuf = [x0] + [torch.empty((q, MOE_H), dtype=torch.float32, device="cuda") for _ in layers]
+
+        def step(i):
+            for l, lay in enumerate(layers):
+                sb[l].run(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
+
+        step(0)
+        torch.cuda.synchronize()
+        nb = sum(moe_bytes(R, lay[1], sb[l].topk_idx.cpu().numpy(), q) for l, lay in enumerate(layers))
+        hist = [len(set(sb[l].topk_idx.cpu().numpy().reshape(-1).tolist())) for l in range(len(layers))]
+        g = graph_of(torch, step, 1)
+        ms = time_graph(torch, g, reps)
+        out[f"stack{len(layers)}_q{q}_top4_zipf"] = {
+            "us_per_step": round(ms * 1e3, 2), "bytes_per_step": int(nb),
+            "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "distinct_experts_per_layer": hist,
+            "steps_per_s": round(1e3 / ms, 1)}
+        log(f"moe stack q={q}: {ms * 1e3:.1f} us/step, {nb / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return out
 
 
 def hbm_reference(torch):
@@ -96,28 +220,18 @@ def hbm_reference(torch):
     a.fill_(1)
     for _ in range(3):
         b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / 10
+    ms = time_eager(torch, lambda i: b.copy_(a), 10)
     del a, b
-    return 2 * n / us / 1e3
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(R, work, rows=2048, repeats=2):
     """The CPU oracle on a bounded sample: the first `rows` rows of every
     matrix, all six (format, q) products, `repeats` times, one thread."""
+    import inputgen
     import oracle as O
     blocks = {fmt: O.quantize_matrix(fmt, work[fmt]["W"][:rows]) for fmt in FORMATS}
-    xq = {}
-    for q in (1, 4):
-        import inputgen
-        x = inputgen.activations(q, K, seed=1)
-        xq[q] = O.quantize_act(x)
+    xq = {q: O.quantize_act(inputgen.activations(q, K, seed=1)) for q in (1, 4)}
     t0 = time.perf_counter()
     nbytes = 0
     for _ in range(repeats):
@@ -129,22 +243,23 @@ def cpu_baseline(R, work, rows=2048, repeats=2):
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of each 7168x7168 matrix, FP2/FP3/FP4 x q=1,4, "
-                      f"{repeats} repeats, single thread, {dt:.1f} s"}
+                      f"{repeats} repeats, one thread, {dt:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--kernel-iters", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
+    ap.add_argument("--moe-layers", type=int, default=8, help="0 skips the MoE sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default=None, help="fmt,q: time only this GEMV (for profiling)")
-    ap.add_argument("--no-split", action="store_true",
-                    help="run without a workspace (no split of K across workgroups)")
+    ap.add_argument("--moe-only", action="store_true", help="skip the GEMV step (profiling the MoE path)")
+    ap.add_argument("--only", default=None,
+                    help="fmt,q: launch only this GEMV, eagerly, --steps x copies times (profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the hot path has no multi-GPU part); "
+        print("bench.py: this build measures one GPU only (the decode path has no multi-GPU part); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
@@ -155,48 +270,54 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()
-    stream = torch.cuda.current_stream()
-    work, acts, ws = build_workload(torch, R, inputgen)
-    if args.no_split:
-        ws = {k: None for k in ws}
-    print(f"# workload ready: copies {[len(work[f]['mats']) for f in FORMATS]}", file=sys.stderr, flush=True)
+    if args.moe_only:
+        layers = build_moe_layers(torch, R, inputgen, max(1, args.moe_layers))
+        print(json.dumps({"moe": bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))}),
+              flush=True)
+        return
+    work, acts, ws = build_gemv(torch, R, inputgen)
+    log(f"gemv workload ready: copies {[len(work[f]['mats']) for f in FORMATS]}")
 
     if args.only:
         fmt, q = (int(v) for v in args.only.split(","))
-        us = time_kernel(torch, R, work, acts, ws, fmt, q, args.kernel_iters, stream)
+        n = args.steps * len(work[fmt]["mats"])
+        ms = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), n)
         w, a, _ = algorithmic_bytes(R, fmt, q)
-        print(json.dumps({"only": [fmt, q], "us": us, "GBps": (w + a) / us / 1e3}), flush=True)
+        print(json.dumps({"only": [fmt, q], "launches": n, "us": round(ms * 1e3, 3),
+                          "GBps": round((w + a) / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
 
     per = []
     for fmt in FORMATS:
         for q in (1, 4):
-            us = time_kernel(torch, R, work, acts, ws, fmt, q, args.kernel_iters, stream)
+            copies = len(work[fmt]["mats"])
+            g = graph_of(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), copies)
+            us = time_graph(torch, g, args.kernel_reps) * 1e3 / copies
+            us_eager = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), 4 * copies) * 1e3
             w, a, wr = algorithmic_bytes(R, fmt, q)
-            per.append({"fmt": f"FP{fmt}", "q": q, "us": round(us, 3), "weight_bytes": w,
-                        "act_bytes": a, "write_bytes": wr, "GBps": round((w + a) / us / 1e3, 1),
+            per.append({"fmt": f"FP{fmt}", "q": q, "us": round(us, 3), "eager_us": round(us_eager, 3),
+                        "weight_bytes": w, "act_bytes": a, "write_bytes": wr,
+                        "GBps": round((w + a) / us / 1e3, 1),
                         "frac_hbm": round((w + a) / us / 1e3 / HBM_PEAK_GBPS, 4)})
-            print(f"# FP{fmt} q={q}: {us:.2f} us  {(w + a) / us / 1e3:.0f} GB/s", file=sys.stderr, flush=True)
+            log(f"FP{fmt} q={q}: {us:.2f} us (eager {us_eager:.2f})  {(w + a) / us / 1e3:.0f} GB/s")
+            del g
 
-    # whole step: the six GEMVs back to back
+    # whole step: the six GEMVs back to back, one graph holding `rot` steps
     step_bytes = sum(p["weight_bytes"] + p["act_bytes"] for p in per)
+    rot = max(len(work[f]["mats"]) for f in FORMATS)
 
     def step(i):
         for fmt in FORMATS:
             for q in (1, 4):
-                launch(R, work, acts, ws, fmt, q, i, stream)
+                gemv_launch(R, work, acts, ws, fmt, q, i)
 
-    for i in range(args.warmup):
-        step(i)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    g = graph_of(torch, step, rot)
+    for _ in range(args.warmup):
+        g.replay()
+    reps = max(1, -(-args.steps // rot))
+    ms = time_graph(torch, g, reps) / rot
     value = step_bytes / (ms * 1e-3) / 1e9
+    del g
 
     dom = max(per, key=lambda p: p["us"])
     ach = (dom["weight_bytes"] + dom["act_bytes"]) / dom["us"] / 1e3
@@ -205,7 +326,7 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": reps * rot,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -215,21 +336,31 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense GEMV 7168x7168, FP2/FP3/FP4 x q=1,4 per step, rotated copies",
                    "rows": N, "cols": K, "formats": ["FP2", "FP3", "FP4"], "q": [1, 4],
-                   "copies": {f"FP{f}": len(work[f]["mats"]) for f in FORMATS}},
+                   "copies": {f"FP{f}": len(work[f]["mats"]) for f in FORMATS},
+                   "timing": "HIP graph replay"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": f"gemv FP{dom['fmt'][-1]} q={dom['q']}",
+        "roofline": {"bound": "hbm", "kernel": f"gemv_kernel<FP{dom['fmt'][-1]}, q={dom['q']}>",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": dom["weight_bytes"] + dom["act_bytes"],
                      "avg_launch_us": dom["us"]},
         "per_kernel": per,
     }
+    del work
+    torch.cuda.empty_cache()
+    if args.moe_layers > 0:
+        layers = build_moe_layers(torch, R, inputgen, args.moe_layers)
+        out["moe"] = bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))
+        del layers
+        torch.cuda.empty_cache()
     try:
         out["hbm_copy_GBps"] = round(hbm_reference(torch), 1)
     except Exception as e:  # pragma: no cover
         out["hbm_copy_GBps"] = f"failed: {e}"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(R, work)
+        import inputgen as ig
+        wk = {f: {"W": ig.dense_weight(N, K, seed=SEEDS[f], outliers=True)} for f in FORMATS}
+        out["cpu_baseline"] = cpu_baseline(R, wk)
     print(json.dumps(out), flush=True)
 
 

@@ -72,7 +72,7 @@ _SIGS = {
     "rfx_debug_block_dots": ([_P, _P, _P, _I, _P, _P], _I),
     "rfx_moe_workspace_bytes": ([_P, _I, _I], _SZ),
     "rfx_moe_route_topk": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
-    "rfx_moe_ffn": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "rfx_moe_ffn": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_moe_debug_hidden": ([_P, _I, _I, _P, _P, _P, _P, _P], _I),
 }
 
@@ -262,10 +262,10 @@ def moe_route_topk(layer, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, x
 
 
 def moe_ffn(layer, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_off, y, ws,
-            stream=None):
+            resid=None, stream=None):
     _check(lib().rfx_moe_ffn(layer.ref(), q, k, _dptr(xq), _dptr(xs), _dptr(xsum), _dptr(topk_idx),
-                             _dptr(topk_w), _dptr(pairs_sorted), _dptr(expert_off), _dptr(y),
-                             _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                             _dptr(topk_w), _dptr(pairs_sorted), _dptr(expert_off), _dptr(resid),
+                             _dptr(y), _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_debug_hidden(layer, q, k, ws, h=None, hq=None, hs=None, stream=None):

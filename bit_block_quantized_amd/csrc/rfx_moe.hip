@@ -118,22 +118,6 @@ __device__ __forceinline__ void quant32(float v, int8_t *q_out, float *s_out, in
     }
 }
 
-// Sum over the whole workgroup (blockDim.x threads, multiple of 64).
-__device__ __forceinline__ float block_sum(float v, float *scratch)
-{
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        scratch[wave] = v;
-    __syncthreads();
-    float t = 0.0f;
-    for (int w = 0; w < nw; w++)
-        t += scratch[w];
-    return t;
-}
-
 // ------------------------------------------------------------------
 // Router (decode: q <= 4 tokens).
 // ------------------------------------------------------------------
@@ -155,47 +139,75 @@ struct RouteArgs {
 
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 {
-    __shared__ float scratch[8];
     __shared__ int s_last;
     __shared__ int s_idx[kMaxDecodeQ * kMaxK];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // (1) quantize the tokens for the experts (grid-stride, 32 lanes a block)
-    const int nel = a.q * a.H;
-    for (int base = blockIdx.x * 256; base < nel; base += gridDim.x * 256) {
-        const int i = base + tid;
-        const float v = i < nel ? a.x[i] : 0.0f;
+    // (1) quantize the tokens for the experts: 32 lanes per 32-element
+    // block, blocks spread over all workgroups
+    const int nblk = a.q * (a.H / 32);
+    for (int base = (blockIdx.x * 4 + wave) * 2; base < nblk; base += gridDim.x * 8) {
+        const int blk = base + (lane >> 5);
+        const bool valid = blk < nblk;
+        const int i = blk * 32 + (lane & 31);
+        const float v = valid ? a.x[i] : 0.0f;
         int8_t qv;
         float sv;
         int32_t sm;
         quant32(v, &qv, &sv, &sm, true);
-        if (i < nel) {
+        if (valid) {
             a.xq[i] = qv;
-            if ((tid & 31) == 0) {
-                a.xs[i >> 5] = sv;
-                a.xsum[i >> 5] = sm;
+            if ((lane & 31) == 0) {
+                a.xs[blk] = sv;
+                a.xsum[blk] = sm;
             }
         }
     }
 
-    // (2) logits of this workgroup's experts, fixed summation order
+    // (2) one workgroup per expert row: each thread takes up to 8 float4
+    //     columns (h = 4 tid + 1024 i), every load issued before the sums;
+    //     fixed-order reduction (lane butterfly, then waves in order)
+    __shared__ float s_part[4][kMaxDecodeQ];
     for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
         const float *wrow = a.wr + (size_t)e * a.H;
-        float part[kMaxDecodeQ] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int h = tid * 4; h < a.H; h += 1024) {
-            const float4 w4 = *reinterpret_cast<const float4 *>(wrow + h);
-            for (int t = 0; t < a.q; t++) {
-                const float4 x4 = *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h);
-                part[t] += w4.x * x4.x + w4.y * x4.y + w4.z * x4.z + w4.w * x4.w;
+        float4 w4[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int h = tid * 4 + 1024 * i;
+            w4[i] = h < a.H ? *reinterpret_cast<const float4 *>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float part[kMaxDecodeQ];
+#pragma unroll
+        for (int t = 0; t < kMaxDecodeQ; t++) {
+            part[t] = 0.0f;
+            if (t < a.q) {
+                float4 x4[8];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const int h = tid * 4 + 1024 * i;
+                    x4[i] = h < a.H ? *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    part[t] += w4[i].x * x4[i].x + w4[i].y * x4[i].y + w4[i].z * x4[i].z + w4[i].w * x4[i].w;
             }
+            for (int o = 32; o > 0; o >>= 1)
+                part[t] += __shfl_xor(part[t], o, 64);
         }
-        for (int t = 0; t < a.q; t++) {
-            float l = block_sum(part[t], scratch);
-            if (a.wb)
-                l += a.wb[e];
-            if (tid == 0)
-                __hip_atomic_store(a.logits + (size_t)t * a.E + e, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < kMaxDecodeQ; t++)
+                s_part[wave][t] = part[t];
         }
+        __syncthreads();
+        if (tid < a.q) {
+            const float l = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+            __hip_atomic_store(a.logits + (size_t)tid * a.E + e, a.wb ? l + a.wb[e] : l, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -206,7 +218,6 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
         return;
 
     // (3) last workgroup: softmax and top-k, one wave per token
-    const int lane = tid & 63, wave = tid >> 6;
     if (wave < a.q) {
         const int t = wave;
         float l[4];
@@ -313,43 +324,39 @@ __device__ __forceinline__ SlotInfo find_slot(int slot, const int32_t *__restric
     __shared__ SlotInfo s_info;
     const int tid = threadIdx.x, lane = tid & 63;
     if (tid < 64) {
-        // lane holds experts lane, lane+64, lane+128, lane+192
-        int act[4], c = 0;
+        // lane holds experts lane + 64 r (r < 4); all eight offsets are
+        // loaded at once (clamped indices, no branches) and kept, so the
+        // found expert's pair range needs no second round trip
+        int lo[4], hi[4];
+#pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int e = lane + 64 * r;
-            act[r] = e < E && expert_off[e + 1] > expert_off[e];
+            const int e = min(lane + 64 * r, E);
+            lo[r] = expert_off[e];
+            hi[r] = expert_off[min(e + 1, E)];
         }
-        // order experts by id: position of expert e = (# active with id < e);
-        // scan per r-row: row r covers ids 64r..64r+63
-        int total = 0, found_e = -1;
+        int total = 0, found_r = -1;
+#pragma unroll
         for (int r = 0; r < 4; r++) {
-            const unsigned long long bal = __ballot(act[r]);
+            const bool act = (lane + 64 * r) < E && hi[r] > lo[r];
+            const unsigned long long bal = __ballot(act);
             const int rank = total + __popcll(bal & ((1ull << lane) - 1ull));
-            if (act[r] && rank == slot)
-                found_e = lane + 64 * r;
+            if (act && rank == slot)
+                found_r = r;
             total += __popcll(bal);
         }
-        // the finder lane publishes
-        const unsigned long long fb = __ballot(found_e >= 0);
         if (lane == 0) {
             s_info.n_slots = total + (has_shared ? 1 : 0);
-            s_info.kind = 0;
+            s_info.kind = (has_shared && slot == total) ? 2 : 0;
             s_info.expert = -1;
             s_info.pb = s_info.pe = 0;
-            if (has_shared && slot == total)
-                s_info.kind = 2;
         }
-        if (fb) {
-            const int src = __ffsll((long long)fb) - 1;
-            const int e = __shfl(found_e, src, 64);
-            if (lane == 0) {
-                s_info.kind = 1;
-                s_info.expert = e;
-                s_info.pb = expert_off[e];
-                s_info.pe = expert_off[e + 1];
-            }
+        __builtin_amdgcn_wave_barrier();
+        if (found_r >= 0) { // exactly one lane
+            s_info.kind = 1;
+            s_info.expert = lane + 64 * found_r;
+            s_info.pb = found_r == 0 ? lo[0] : found_r == 1 ? lo[1] : found_r == 2 ? lo[2] : lo[3];
+            s_info.pe = found_r == 0 ? hi[0] : found_r == 1 ? hi[1] : found_r == 2 ? hi[2] : hi[3];
         }
-        (void)c;
     }
     __syncthreads();
     const SlotInfo r = s_info;
@@ -374,7 +381,8 @@ struct FfnArgs {
     const float *topk_w;
     const int32_t *pairs_sorted;
     const int32_t *expert_off;
-    float *y; // [q][H]
+    const float *resid; // [q][H] or null
+    float *y;           // [q][H]
     MoeWs ws;
 };
 
@@ -410,15 +418,21 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
 {
     constexpr int FU = FG;
     const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const int nbH = a.H / 32;
+    uint32_t goff[NE], moff[NE];
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        goff[j] = (uint32_t)cols.token[j] * (uint32_t)a.H;
+        moff[j] = (uint32_t)cols.token[j] * (uint32_t)nbH;
+    }
     XCols<NE> xc;
     xc.xq = a.xq;
     xc.xs = a.xs;
     xc.xsum = a.xsum;
-    const int nbH = a.H / 32;
 #pragma unroll
     for (int j = 0; j < NE; j++) {
-        xc.xoff[j] = (uint32_t)cols.token[j] * (uint32_t)a.H;
-        xc.moff[j] = (uint32_t)cols.token[j] * (uint32_t)nbH;
+        xc.xoff[j] = goff[j];
+        xc.moff[j] = moff[j];
     }
     const int S = (a.H + 255) / 256;
     const uint8_t *gm, *um;
@@ -539,15 +553,21 @@ template <int FD, int NE>
 __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
 {
     const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const int nbI = a.I / 32;
+    uint32_t goff[NE], moff[NE];
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        goff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)a.I;
+        moff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)nbI;
+    }
     XCols<NE> xc;
     xc.xq = a.ws.hq;
     xc.xs = a.ws.hs;
     xc.xsum = a.ws.hsum;
-    const int nbI = a.I / 32;
 #pragma unroll
     for (int j = 0; j < NE; j++) {
-        xc.xoff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)a.I;
-        xc.moff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)nbI;
+        xc.xoff[j] = goff[j];
+        xc.moff[j] = moff[j];
     }
     const int S = (a.I + 255) / 256;
     const uint8_t *dm = si.kind == 2 ? a.sh_down : a.down + a.down_stride * (size_t)si.expert;
@@ -642,6 +662,8 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
             float acc = a.has_shared ? __hip_atomic_load(a.ws.o + (size_t)(a.q * a.k + t) * a.H + row,
                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                      : 0.0f;
+            if (a.resid)
+                acc = a.resid[(size_t)t * a.H + row] + acc;
             for (int j = 0; j < a.k; j++) {
                 const float w = a.topk_w[t * a.k + j];
                 const float ov = __hip_atomic_load(a.ws.o + (size_t)(t * a.k + j) * a.H + row,
@@ -693,10 +715,11 @@ int check_layer(const rfx_moe_layer *L)
 template <int FG>
 int launch_gateup(int fs, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st)
 {
+    const size_t lds = 0;
     switch (fs) {
-    case RFX_FP2: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP2>), grid, block, 0, st, a); break;
-    case RFX_FP3: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP3>), grid, block, 0, st, a); break;
-    case RFX_FP4: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP4>), grid, block, 0, st, a); break;
+    case RFX_FP2: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP2>), grid, block, lds, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP3>), grid, block, lds, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP4>), grid, block, lds, st, a); break;
     }
     return hip_status("gate/up launch");
 }
@@ -704,10 +727,11 @@ int launch_gateup(int fs, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t s
 template <int FD>
 int launch_down(int fsd, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st)
 {
+    const size_t lds = 0;
     switch (fsd) {
-    case RFX_FP2: hipLaunchKernelGGL((down_kernel<FD, RFX_FP2>), grid, block, 0, st, a); break;
-    case RFX_FP3: hipLaunchKernelGGL((down_kernel<FD, RFX_FP3>), grid, block, 0, st, a); break;
-    case RFX_FP4: hipLaunchKernelGGL((down_kernel<FD, RFX_FP4>), grid, block, 0, st, a); break;
+    case RFX_FP2: hipLaunchKernelGGL((down_kernel<FD, RFX_FP2>), grid, block, lds, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((down_kernel<FD, RFX_FP3>), grid, block, lds, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((down_kernel<FD, RFX_FP4>), grid, block, lds, st, a); break;
     }
     return hip_status("down launch");
 }
@@ -772,14 +796,17 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
     a.xsum = xsum;
     a.logits = w.logits;
     a.cnt = w.route_cnt;
-    const int grid = L->n_experts < 128 ? L->n_experts : 128;
+    if (L->hidden > 8192)
+        return fail(RFX_E_UNSUPPORTED, "router: hidden=%d > 8192", L->hidden);
+    const int grid = L->n_experts; // one workgroup per expert row
     hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
     return hip_status("route launch");
 }
 
 int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs, const int32_t *xsum,
                 const int32_t *topk_idx, const float *topk_w, const int32_t *pairs_sorted,
-                const int32_t *expert_off, float *y, void *ws, size_t ws_bytes, void *stream)
+                const int32_t *expert_off, const float *resid, float *y, void *ws, size_t ws_bytes,
+                void *stream)
 {
     int st = check_layer(L);
     if (st)
@@ -825,8 +852,11 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.topk_w = topk_w;
     a.pairs_sorted = pairs_sorted;
     a.expert_off = expert_off;
+    a.resid = resid;
     a.y = y;
     a.ws = w;
+    if (resid && (st = check_ptr(resid, 4, "resid")))
+        return st;
     const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
     const hipStream_t s = (hipStream_t)stream;
     const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);

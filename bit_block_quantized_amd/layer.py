@@ -108,11 +108,13 @@ class MoeBuffers:
         self.y = torch.empty((q, H), dtype=torch.float32, device=device)
         self.ws = torch.zeros(moe_workspace_bytes(layer, q, k), dtype=torch.uint8, device=device)
 
-    def run(self, layer: DeviceMoeLayer, x, stream=None):
-        """route + FFN for x (device fp32 [q][hidden]); result in self.y."""
+    def run(self, layer: DeviceMoeLayer, x, resid=None, out=None, stream=None):
+        """route + FFN for x (device fp32 [q][hidden]); y = resid + MoE(x)
+        lands in `out` (default self.y)."""
         from . import moe_ffn, moe_route_topk
+        y = self.y if out is None else out
         moe_route_topk(layer, x, self.q, self.k, self.topk_idx, self.topk_w, self.pairs_sorted,
                        self.expert_off, self.xq, self.xs, self.xsum, self.ws, stream)
         moe_ffn(layer, self.q, self.k, self.xq, self.xs, self.xsum, self.topk_idx, self.topk_w,
-                self.pairs_sorted, self.expert_off, self.y, self.ws, stream)
-        return self.y
+                self.pairs_sorted, self.expert_off, y, self.ws, resid, stream)
+        return y

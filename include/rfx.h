@@ -206,12 +206,14 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
 
 /* Expert FFN and combine. For every pair (t, j) with expert e: g = G_e.x~_t,
  * u = U_e.x~_t, h = silu(g) * u, h~ = activation-quantized h, o = D_e.h~;
- * shared expert likewise with weight 1; y_t = o_shared + sum_j w_tj o_tj in
- * slot order (deterministic, no float atomics). y fp32 [q][H]. */
+ * shared expert likewise with weight 1; y_t = resid_t + o_shared + sum_j
+ * w_tj o_tj in slot order (deterministic, no float atomics). resid fp32
+ * [q][H] or NULL (no residual; it may alias neither y nor ws); y fp32
+ * [q][H]. ws: the workspace given to rfx_moe_route_topk may be reused. */
 int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
                 const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
-                const int32_t *pairs_sorted, const int32_t *expert_off, float *y, void *ws,
-                size_t ws_bytes, void *stream);
+                const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid,
+                float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* Test hook: after rfx_moe_ffn with the same workspace, copy out the
  * intermediate activations of the last call: h fp32 [(q*k)+q][I] (pairs in
