@@ -120,18 +120,43 @@ struct TileRegs {
     u32x2 sc8;  // FP4: eight e8m0 bytes
 };
 
+// Issue order = use order: the scales first, then the code chunks in the
+// order blocks 0..7 need them, so that with straight-line code the compiler's
+// partial vmcnt waits let block 0 start while later chunks are in flight.
+// Issue order = use order: the scales first, then the code chunks in the
+// order blocks 0..7 need them, so that with straight-line code the compiler's
+// partial vmcnt waits let block 0 start while later chunks are in flight.
+// The scheduling barriers keep the machine scheduler from reordering them.
 template <int FMT>
 __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ tile, int lane)
 {
     TileRegs<FMT> t;
     const u32x4 *tp = reinterpret_cast<const u32x4 *>(tile) + lane;
+#define RFX_LD(dst, ptr)                                                                                      \
+    do {                                                                                                      \
+        dst = __builtin_nontemporal_load(ptr);                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                                    \
+    } while (0)
+    if (FMT == RFX_FP4) {
+        RFX_LD(t.sc8, reinterpret_cast<const u32x2 *>(tile + 8 * 1024) + lane);
 #pragma unroll
-    for (int k = 0; k < TileFmt<FMT>::code_chunks; k++)
-        t.c[k] = __builtin_nontemporal_load(tp + 64 * k);
-    if (FMT == RFX_FP4)
-        t.sc8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(tile + 8 * 1024) + lane);
-    else
-        t.sc16 = __builtin_nontemporal_load(tp + 64 * TileFmt<FMT>::code_chunks);
+        for (int k = 0; k < 8; k++)
+            RFX_LD(t.c[k], tp + 64 * k);
+    } else if (FMT == RFX_FP3) {
+        RFX_LD(t.sc16, tp + 64 * 6);
+        RFX_LD(t.c[4], tp + 64 * 4); // high bits, blocks 0..3
+        RFX_LD(t.c[0], tp);
+        RFX_LD(t.c[1], tp + 64);
+        RFX_LD(t.c[5], tp + 64 * 5); // high bits, blocks 4..7
+        RFX_LD(t.c[2], tp + 64 * 2);
+        RFX_LD(t.c[3], tp + 64 * 3);
+    } else {
+        RFX_LD(t.sc16, tp + 64 * 4);
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            RFX_LD(t.c[k], tp + 64 * k);
+    }
+#undef RFX_LD
     return t;
 }
 
@@ -220,6 +245,56 @@ __device__ __forceinline__ void accumulate_block(const Sel8 &sel, float sw, cons
 #pragma unroll
     for (int j = 0; j < NQ; j++)
         acc[j] += (sw * xb.sx[j]) * (float)block_dot<FMT, Q>(sel, xb, j);
+}
+
+// All blocks of one tile (blocks b0 .. b0 + 7 of the row) against one set of
+// activation columns. FULL: every tile lies inside K (K % 256 == 0), chosen
+// per launch. Otherwise the blocks past K are computed too, with the
+// activation index clamped into range and the weight scale forced to zero.
+// Either way the code is straight-line: every chunk load is used on every
+// path, so the compiler keeps them in flight instead of sinking each into a
+// branch, and waits for each block's chunks just before that block.
+template <int FMT, int Q, int NQ, bool FULL>
+__device__ __forceinline__ void tile_blocks(const TileRegs<FMT> &t, int b0, int nb, const XCols<Q> &xc,
+                                            float (&acc)[Q])
+{
+#pragma unroll
+    for (int bi = 0; bi < 8; bi++) {
+        const int b = FULL ? b0 + bi : min(b0 + bi, nb - 1);
+        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b);
+        Sel8 sel;
+        float sw;
+        decode_block<FMT>(t, bi, sel, sw);
+        if (!FULL)
+            sw = b0 + bi < nb ? sw : 0.0f;
+        accumulate_block<FMT, Q, NQ>(sel, sw, xb, acc);
+        // keep each block's work after its own chunk wait (the scheduler
+        // would otherwise hoist the decodes and wait for the whole tile)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// A gate tile and the matching up tile against the same activation blocks.
+template <int FG, int FU, int Q, bool FULL>
+__device__ __forceinline__ void tile_blocks2(const TileRegs<FG> &tg, const TileRegs<FU> &tu, int b0, int nb,
+                                             const XCols<Q> &xc, float (&ag)[Q], float (&au)[Q])
+{
+#pragma unroll
+    for (int bi = 0; bi < 8; bi++) {
+        const int b = FULL ? b0 + bi : min(b0 + bi, nb - 1);
+        const XBlock<Q> xb = load_xblock<true, Q>(xc, b);
+        Sel8 sel;
+        float sw;
+        decode_block<FG>(tg, bi, sel, sw);
+        if (!FULL)
+            sw = b0 + bi < nb ? sw : 0.0f;
+        accumulate_block<FG, Q, Q>(sel, sw, xb, ag);
+        decode_block<FU>(tu, bi, sel, sw);
+        if (!FULL)
+            sw = b0 + bi < nb ? sw : 0.0f;
+        accumulate_block<FU, Q, Q>(sel, sw, xb, au);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt at

@@ -37,6 +37,7 @@
 #include <cstdint>
 
 #include "rfx_decode.h"
+#include "rfx_xtile.h"
 #include "rfx_internal.h"
 
 namespace rfx {
@@ -103,28 +104,86 @@ struct GemvArgs {
     unsigned *slots; // split-K exchange slots (workspace)
 };
 
-template <int FMT, int Q, bool DOTS>
-__device__ __forceinline__ void compute_tile(const TileRegs<FMT> &t, int s, int row, const GemvArgs &a,
+// Activations per block come either from SGPRs (scalar loads per block) or,
+// with BC, from a per-tile VGPR copy broadcast by DPP (vector loads issued
+// with the weight tile). Scalar loads complete out of order, so each block
+// waits for all of its activation loads: at q >= 2 that wait dominates and
+// BC wins; at q = 1 the scalar path is as fast and needs fewer VGPRs. The
+// multi-tile loop (double-buffered tiles) always takes the scalar path to
+// stay within the register budget of a 1024-thread workgroup.
+template <int Q>
+constexpr bool use_bcast()
+{
+    return Q >= 2;
+}
+
+// A weight tile and, in broadcast mode, the matching activation slice.
+template <int FMT, int Q>
+struct WTile {
+    TileRegs<FMT> w;
+    XTile<Q> x;
+};
+
+template <int FMT, int Q, bool FULL, bool BC>
+__device__ __forceinline__ WTile<FMT, Q> load_wtile(const uint8_t *gbase, int s, int lane, const XCols<Q> &xc,
+                                                    int nb)
+{
+    WTile<FMT, Q> t;
+    if (BC) // issued first: block 0 needs it together with the first chunk
+        t.x = load_xtile<FMT, Q, FULL>(xc, s, nb, lane);
+    t.w = load_tile<FMT>(gbase + (size_t)s * TileFmt<FMT>::bytes, lane);
+    return t;
+}
+
+template <int FMT, int Q, bool FULL, int... BI>
+__device__ __forceinline__ void store_dots_bcast(const WTile<FMT, Q> &t, int b0, int row, const GemvArgs &a,
+                                                 std::integer_sequence<int, BI...>)
+{
+    // the dots run with every lane active (the DPP broadcast reads other
+    // lanes); only the stores are predicated
+    (
+        [&] {
+            int d[Q];
+#pragma unroll
+            for (int j = 0; j < Q; j++)
+                d[j] = tile_block_dot_bcast<FMT, Q, BI>(t.w, t.x, j);
+            if (b0 + BI < a.nb && row < a.N) {
+#pragma unroll
+                for (int j = 0; j < Q; j++)
+                    a.dots[((size_t)j * a.N + row) * a.nb + b0 + BI] = d[j];
+            }
+        }(),
+        ...);
+}
+
+template <int FMT, int Q, bool DOTS, bool FULL, bool BC>
+__device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int row, const GemvArgs &a,
                                              const XCols<Q> &xc, float (&acc)[Q])
 {
     const int b0 = s * 8;
-    const int nvalid = min(8, a.nb - b0); // blocks of this tile inside K
+    if (!DOTS) {
+        if (BC)
+            tile_blocks_bcast<FMT, Q, FULL>(t.w, t.x, b0, a.nb, acc);
+        else
+            tile_blocks<FMT, Q, Q, FULL>(t.w, b0, a.nb, xc, acc);
+        return;
+    }
+    // debug path: per-block dots of the blocks inside K
+    if (BC) {
+        store_dots_bcast<FMT, Q, FULL>(t, b0, row, a, std::make_integer_sequence<int, 8>{});
+        return;
+    }
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
-        if (bi >= nvalid)
-            break;
-        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b0 + bi);
+        const int b = min(b0 + bi, a.nb - 1);
+        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b);
         Sel8 sel;
         float sw;
-        decode_block<FMT>(t, bi, sel, sw);
-        if (DOTS) {
-            if (row < a.N) {
+        decode_block<FMT>(t.w, bi, sel, sw);
+        if (b0 + bi < a.nb && row < a.N) {
 #pragma unroll
-                for (int j = 0; j < Q; j++)
-                    a.dots[((size_t)j * a.N + row) * a.nb + b0 + bi] = block_dot<FMT, Q>(sel, xb, j);
-            }
-        } else {
-            accumulate_block<FMT, Q, Q>(sel, sw, xb, acc);
+            for (int j = 0; j < Q; j++)
+                a.dots[((size_t)j * a.N + row) * a.nb + b0 + bi] = block_dot<FMT, Q>(sel, xb, j);
         }
     }
 }
@@ -132,7 +191,7 @@ __device__ __forceinline__ void compute_tile(const TileRegs<FMT> &t, int s, int 
 // One workgroup = W waves on one 64-row group; its tiles [s_begin, s_end)
 // are split into contiguous runs, one per wave. Each wave keeps the next
 // tile's loads in flight while it decodes the current one.
-template <int FMT, int Q, bool DOTS>
+template <int FMT, int Q, bool DOTS, bool FULL>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 {
     // wave index is uniform per wave; say so, so the tile index, the
@@ -154,17 +213,30 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     }
 
     const int nw = a.P * W, v = p * W + wave;
-    const int s_begin = (int)((unsigned)(a.S * v) / (unsigned)nw);
-    const int s_end = (int)((unsigned)(a.S * (v + 1)) / (unsigned)nw);
+    // the division runs on the vector unit; pin its uniform result to SGPRs
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * v) / (unsigned)nw));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * (v + 1)) / (unsigned)nw));
     const uint8_t *gbase = a.W + (size_t)g * a.S * TileFmt<FMT>::bytes;
-    if (s_begin < s_end) {
-        TileRegs<FMT> cur = load_tile<FMT>(gbase + (size_t)s_begin * TileFmt<FMT>::bytes, lane);
-        for (int s = s_begin; s < s_end; s++) {
-            TileRegs<FMT> nxt = cur;
+    if (s_end - s_begin == 1) {
+        // the common case: one tile per wave, straight-line code, so each
+        // block waits only for its own chunks
+        constexpr bool BC = use_bcast<Q>();
+        const WTile<FMT, Q> t = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb);
+        compute_tile<FMT, Q, DOTS, FULL, BC>(t, s_begin, row, a, xc, acc);
+    } else if (s_begin < s_end) {
+        // two tile buffers used in turn (no register copies, which would
+        // wait for the loads they copy): tile s + 1 in flight while s is
+        // computed
+        WTile<FMT, Q> ta = load_wtile<FMT, Q, FULL, false>(gbase, s_begin, lane, xc, a.nb), tb;
+        for (int s = s_begin; s < s_end; s += 2) {
             if (s + 1 < s_end)
-                nxt = load_tile<FMT>(gbase + (size_t)(s + 1) * TileFmt<FMT>::bytes, lane);
-            compute_tile<FMT, Q, DOTS>(cur, s, row, a, xc, acc);
-            cur = nxt;
+                tb = load_wtile<FMT, Q, FULL, false>(gbase, s + 1, lane, xc, a.nb);
+            compute_tile<FMT, Q, DOTS, FULL, false>(ta, s, row, a, xc, acc);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end)
+                ta = load_wtile<FMT, Q, FULL, false>(gbase, s + 2, lane, xc, a.nb);
+            compute_tile<FMT, Q, DOTS, FULL, false>(tb, s + 1, row, a, xc, acc);
         }
     }
     if (DOTS)
@@ -266,15 +338,15 @@ size_t workspace_for(int G, int P, int q)
     return (size_t)G * (P - 1) * q * 64 * sizeof(unsigned);
 }
 
-template <int FMT, bool DOTS>
-int launch_fmt(const GemvArgs &a, int q, int G, int W, hipStream_t st)
+template <int FMT, bool DOTS, bool FULL>
+int launch_q(const GemvArgs &a, int q, int G, int W, hipStream_t st)
 {
     dim3 grid(a.P, G), block(64 * W);
     switch (q) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, 1, DOTS>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, 2, DOTS>), grid, block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((gemv_kernel<FMT, 3, DOTS>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, 4, DOTS>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, 1, DOTS, FULL>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, 2, DOTS, FULL>), grid, block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<FMT, 3, DOTS, FULL>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, 4, DOTS, FULL>), grid, block, 0, st, a); break;
     default: return fail(RFX_E_INVAL, "q must be 1..4");
     }
     return hip_status("gemv launch");
@@ -283,10 +355,11 @@ int launch_fmt(const GemvArgs &a, int q, int G, int W, hipStream_t st)
 template <bool DOTS>
 int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
 {
+    const bool full = a.K % kTileCols == 0; // no partial tiles
     switch (fmt) {
-    case RFX_FP2: return launch_fmt<RFX_FP2, DOTS>(a, q, G, W, st);
-    case RFX_FP3: return launch_fmt<RFX_FP3, DOTS>(a, q, G, W, st);
-    case RFX_FP4: return launch_fmt<RFX_FP4, DOTS>(a, q, G, W, st);
+    case RFX_FP2: return full ? launch_q<RFX_FP2, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2, DOTS, false>(a, q, G, W, st);
+    case RFX_FP3: return full ? launch_q<RFX_FP3, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP3, DOTS, false>(a, q, G, W, st);
+    case RFX_FP4: return full ? launch_q<RFX_FP4, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP4, DOTS, false>(a, q, G, W, st);
     }
     return fail(RFX_E_INVAL, "unknown format");
 }

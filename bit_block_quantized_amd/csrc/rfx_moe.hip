@@ -412,6 +412,13 @@ __device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnA
     return c;
 }
 
+template <int FG, int FU, int NE>
+__device__ __forceinline__ void gateup_tile(const TileRegs<FG> &tg, const TileRegs<FU> &tu, int s, int nbH,
+                                            const XCols<NE> &xc, float (&ag)[NE], float (&au)[NE])
+{
+    tile_blocks2<FG, FU, NE, false>(tg, tu, s * 8, nbH, xc, ag, au);
+}
+
 template <int FG, int NE>
 __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W,
                             float *red)
@@ -451,33 +458,26 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
         ag[j] = 0.0f;
         au[j] = 0.0f;
     }
-    const int s_begin = (int)((unsigned)(S * wave) / (unsigned)W);
-    const int s_end = (int)((unsigned)(S * (wave + 1)) / (unsigned)W);
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
+    // two buffers per stream used in turn: tile s + 1 in flight while s is
+    // computed, with no register copies (which would wait for the loads)
     if (s_begin < s_end) {
-        TileRegs<FG> cg = load_tile<FG>(gm + (size_t)s_begin * TileFmt<FG>::bytes, lane);
-        TileRegs<FU> cu = load_tile<FU>(um + (size_t)s_begin * TileFmt<FU>::bytes, lane);
-        for (int s = s_begin; s < s_end; s++) {
-            TileRegs<FG> ng = cg;
-            TileRegs<FU> nu = cu;
+        TileRegs<FG> ga = load_tile<FG>(gm + (size_t)s_begin * TileFmt<FG>::bytes, lane), gb;
+        TileRegs<FU> ua = load_tile<FU>(um + (size_t)s_begin * TileFmt<FU>::bytes, lane), ub;
+        for (int s = s_begin; s < s_end; s += 2) {
             if (s + 1 < s_end) {
-                ng = load_tile<FG>(gm + (size_t)(s + 1) * TileFmt<FG>::bytes, lane);
-                nu = load_tile<FU>(um + (size_t)(s + 1) * TileFmt<FU>::bytes, lane);
+                gb = load_tile<FG>(gm + (size_t)(s + 1) * TileFmt<FG>::bytes, lane);
+                ub = load_tile<FU>(um + (size_t)(s + 1) * TileFmt<FU>::bytes, lane);
             }
-            const int b0 = s * 8, nvalid = min(8, nbH - b0);
-#pragma unroll
-            for (int bi = 0; bi < 8; bi++) {
-                if (bi >= nvalid)
-                    break;
-                const XBlock<NE> xb = load_xblock<true, NE>(xc, b0 + bi);
-                Sel8 sel;
-                float sw;
-                decode_block<FG>(cg, bi, sel, sw);
-                accumulate_block<FG, NE, NE>(sel, sw, xb, ag);
-                decode_block<FU>(cu, bi, sel, sw);
-                accumulate_block<FU, NE, NE>(sel, sw, xb, au);
+            gateup_tile<FG, FU, NE>(ga, ua, s, nbH, xc, ag, au);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end) {
+                ga = load_tile<FG>(gm + (size_t)(s + 2) * TileFmt<FG>::bytes, lane);
+                ua = load_tile<FU>(um + (size_t)(s + 2) * TileFmt<FU>::bytes, lane);
             }
-            cg = ng;
-            cu = nu;
+            gateup_tile<FG, FU, NE>(gb, ub, s + 1, nbH, xc, ag, au);
         }
     }
     // fixed-order reduction over waves; red[w][m][j][lane], m = gate/up
@@ -550,6 +550,13 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
 // Expert down projection, shared expert and the weighted combine.
 // ------------------------------------------------------------------
 template <int FD, int NE>
+__device__ __forceinline__ void down_tile(const TileRegs<FD> &t, int s, int nbI, const XCols<NE> &xc,
+                                          float (&ao)[NE])
+{
+    tile_blocks<FD, NE, NE, false>(t, s * 8, nbI, xc, ao);
+}
+
+template <int FD, int NE>
 __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
 {
     const SlotCols<NE> cols = slot_cols<NE>(si, a);
@@ -576,26 +583,19 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
 #pragma unroll
     for (int j = 0; j < NE; j++)
         ao[j] = 0.0f;
-    const int s_begin = (int)((unsigned)(S * wave) / (unsigned)W);
-    const int s_end = (int)((unsigned)(S * (wave + 1)) / (unsigned)W);
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
     if (s_begin < s_end) {
-        TileRegs<FD> cd = load_tile<FD>(dm + (size_t)s_begin * TileFmt<FD>::bytes, lane);
-        for (int s = s_begin; s < s_end; s++) {
-            TileRegs<FD> nd = cd;
+        TileRegs<FD> da = load_tile<FD>(dm + (size_t)s_begin * TileFmt<FD>::bytes, lane), db;
+        for (int s = s_begin; s < s_end; s += 2) {
             if (s + 1 < s_end)
-                nd = load_tile<FD>(dm + (size_t)(s + 1) * TileFmt<FD>::bytes, lane);
-            const int b0 = s * 8, nvalid = min(8, nbI - b0);
-#pragma unroll
-            for (int bi = 0; bi < 8; bi++) {
-                if (bi >= nvalid)
-                    break;
-                const XBlock<NE> xb = load_xblock<FD != RFX_FP4, NE>(xc, b0 + bi);
-                Sel8 sel;
-                float sw;
-                decode_block<FD>(cd, bi, sel, sw);
-                accumulate_block<FD, NE, NE>(sel, sw, xb, ao);
-            }
-            cd = nd;
+                db = load_tile<FD>(dm + (size_t)(s + 1) * TileFmt<FD>::bytes, lane);
+            down_tile<FD, NE>(da, s, nbI, xc, ao);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end)
+                da = load_tile<FD>(dm + (size_t)(s + 2) * TileFmt<FD>::bytes, lane);
+            down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
         }
     }
 #define RED_D(w, j) red[((w) * kMaxDecodeQ + (j)) * 64 + lane]

@@ -1,0 +1,209 @@
+// Activation tiles held in VGPRs and broadcast to the wave with DPP (gfx950).
+//
+// Pages cited (title, site):
+//   [HM] "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
+//        (hellomarvisaitoday.com), paragraphs numbered from the top.
+//
+// [HM] para 3: one decoded weight block feeds integer dot products for every
+// activation column. Every lane of a wave (one output row each) needs the
+// same 32 activation bytes per block. Scalar loads give them as SGPR
+// operands, but scalar loads complete out of order, so every use waits for
+// all of them: at q = 4 that is several full memory round trips per block.
+// Here the activation slice of a whole tile (q columns x 256 bytes, plus the
+// eight block scales and sums per column) is read with ordinary vector loads,
+// issued together with the weight tile, and each of the four 16-lane rows of
+// the wave holds a full copy. A v_dot4c_i32_i8 with the DPP control
+// row_newbcast:n reads the activation dword held by lane n of its row, so
+// the broadcast costs no instruction. Vector loads complete in order, so
+// block b waits only for its own data.
+#pragma once
+
+#include "rfx_decode.h"
+
+#include <utility>
+
+namespace rfx {
+namespace dev {
+
+// Per-lane part of one tile's activations. Lane n of a row (n = lane & 15)
+// holds bytes [16n, 16n + 16) of column j's 256-byte slice in code[j], the
+// fp32 scale of block n & 7 in sx[j] and, for FP2/FP3, -off * (block sum)
+// in nsum[j] (off = 3 or 7: the codebook offset folded out of the dot).
+template <int Q>
+struct XTile {
+    u32x4 code[Q];
+    float sx[Q];
+    int nsum[Q];
+};
+
+template <int FMT, int Q, bool FULL>
+__device__ __forceinline__ XTile<Q> load_xtile(const XCols<Q> &xc, int s, int nb, int lane)
+{
+    XTile<Q> xt;
+    const int n = lane & 15;
+    // in a tile that ends past K the missing blocks read a valid block (the
+    // last one); their weight scale is forced to zero by the caller
+    const int bc = FULL ? s * 8 + (n >> 1) : min(s * 8 + (n >> 1), nb - 1);
+    const int bs = FULL ? s * 8 + (n & 7) : min(s * 8 + (n & 7), nb - 1);
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        xt.code[j] = *reinterpret_cast<const u32x4 *>(xc.xq + xc.xoff[j] + (uint32_t)bc * 32u + (uint32_t)(n & 1) * 16u);
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
+    if (FMT != RFX_FP4) {
+        constexpr int off = FMT == RFX_FP2 ? 3 : 7;
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            xt.nsum[j] = -off * xc.xsum[xc.moff[j] + (uint32_t)bs];
+    }
+    return xt;
+}
+
+// Selector bytes equal to 2c (twice the code) for FP2 / FP3, so that with
+// v = 2c - off the block dot is sum(2c * x) + (-off * sum(x)): the second
+// term starts the accumulator and needs no instruction after the dots.
+__device__ __forceinline__ Sel8 sel2_fp2(uint32_t w0, uint32_t w1)
+{
+    Sel8 s;
+    s.v[0] = (int)((w0 << 1) & 0x06060606u);
+    s.v[1] = (int)((w0 >> 1) & 0x06060606u);
+    s.v[2] = (int)((w0 >> 3) & 0x06060606u);
+    s.v[3] = (int)((w0 >> 5) & 0x06060606u);
+    s.v[4] = (int)((w1 << 1) & 0x06060606u);
+    s.v[5] = (int)((w1 >> 1) & 0x06060606u);
+    s.v[6] = (int)((w1 >> 3) & 0x06060606u);
+    s.v[7] = (int)((w1 >> 5) & 0x06060606u);
+    return s;
+}
+
+// FP3: the high code bit of weight 4i + j sits at bit 8j + i of h; in 2c it
+// has weight 8.
+__device__ __forceinline__ Sel8 sel2_fp3(uint32_t w0, uint32_t w1, uint32_t h)
+{
+    Sel8 s = sel2_fp2(w0, w1);
+    s.v[0] |= (int)((h << 3) & 0x08080808u);
+    s.v[1] |= (int)((h << 2) & 0x08080808u);
+    s.v[2] |= (int)((h << 1) & 0x08080808u);
+    s.v[3] |= (int)(h & 0x08080808u);
+    s.v[4] |= (int)((h >> 1) & 0x08080808u);
+    s.v[5] |= (int)((h >> 2) & 0x08080808u);
+    s.v[6] |= (int)((h >> 3) & 0x08080808u);
+    s.v[7] |= (int)((h >> 4) & 0x08080808u);
+    return s;
+}
+
+// Selector bytes (2c for FP2/FP3, signed values for FP4) and the weight
+// scale of block BI of a tile.
+template <int FMT, int BI>
+__device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel, float &sw)
+{
+    if (FMT == RFX_FP4) {
+        sel = sel_fp4(t.c[BI]);
+        const uint32_t e = ((BI < 4 ? t.sc8.x : t.sc8.y) >> (8 * (BI & 3))) & 0xffu;
+        sw = ldexpf(1.0f, (int)e - 128);
+    } else {
+        const uint32_t w0 = (BI & 1) ? t.c[BI >> 1].z : t.c[BI >> 1].x;
+        const uint32_t w1 = (BI & 1) ? t.c[BI >> 1].w : t.c[BI >> 1].y;
+        if (FMT == RFX_FP3) {
+            const u32x4 h4 = t.c[4 + (BI >> 2)];
+            const uint32_t h = (BI & 3) == 0 ? h4.x : (BI & 3) == 1 ? h4.y : (BI & 3) == 2 ? h4.z : h4.w;
+            sel = sel2_fp3(w0, w1, h);
+        } else {
+            sel = sel2_fp2(w0, w1);
+        }
+        const uint32_t sw2 = (BI >> 1) == 0 ? t.sc16.x : (BI >> 1) == 1 ? t.sc16.y : (BI >> 1) == 2 ? t.sc16.z : t.sc16.w;
+        sw = half_bits_to_float((BI & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+    }
+}
+
+// d += sum over the block's 8 activation dwords of dot4(x, sel[i]); dword i
+// of block BI is component i & 3 of x, held by lane 2 * BI + (i >> 2) of
+// each row. Must run with every lane of the wave active: a DPP read of an
+// inactive lane does not return that lane's register. The compiler sees
+// neither the DPP nor the dot inside the asm, so the asm carries its own
+// wait states: the leading s_nop covers the two a DPP read needs after a
+// VALU write of its source, the trailing one the three that must pass
+// before another instruction reads a v_dot4c result (measured on gfx950:
+// with fewer, the reader gets the accumulator's old value; chained dots on
+// the same accumulator are not affected).
+template <int BI>
+__device__ __forceinline__ int dot_block_bcast(int d, u32x4 x, const Sel8 &s)
+{
+    asm("s_nop 1\n\t"
+        "v_dot4c_i32_i8_dpp %0, %1, %5 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %3, %7 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %8 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %1, %9 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %2, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %3, %11 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot4c_i32_i8_dpp %0, %4, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 2"
+        : "+v"(d)
+        : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(s.v[0]), "v"(s.v[1]), "v"(s.v[2]), "v"(s.v[3]),
+          "v"(s.v[4]), "v"(s.v[5]), "v"(s.v[6]), "v"(s.v[7]), "n"(2 * BI), "n"(2 * BI + 1));
+    return d;
+}
+
+// Broadcast lane N of each 16-lane row (a DPP move the compiler folds into
+// the consuming VALU instruction where it can).
+template <int N>
+__device__ __forceinline__ int bcast_row(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x150 + N, 0xF, 0xF, true);
+}
+
+// Exact block dot D for column j of block BI.
+template <int FMT, int Q, int BI>
+__device__ __forceinline__ int block_dot_bcast(const Sel8 &sel, const XTile<Q> &xt, int j)
+{
+    const int d0 = FMT == RFX_FP4 ? 0 : bcast_row<BI>(xt.nsum[j]);
+    return dot_block_bcast<BI>(d0, xt.code[j], sel);
+}
+
+template <int FMT, int Q, int BI, bool FULL>
+__device__ __forceinline__ void tile_block_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
+                                                 float (&acc)[Q])
+{
+    Sel8 sel;
+    float sw;
+    decode_block2<FMT, BI>(t, sel, sw);
+    if (!FULL)
+        sw = b0 + BI < nb ? sw : 0.0f;
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+        acc[j] += (sw * sxb) * (float)block_dot_bcast<FMT, Q, BI>(sel, xt, j);
+    }
+    // keep each block's work after its own chunk wait
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int Q, bool FULL, int... BI>
+__device__ __forceinline__ void tile_blocks_bcast_seq(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
+                                                      float (&acc)[Q], std::integer_sequence<int, BI...>)
+{
+    (tile_block_bcast<FMT, Q, BI, FULL>(t, xt, b0, nb, acc), ...);
+}
+
+// All 8 blocks of one tile, activations broadcast from the lanes.
+template <int FMT, int Q, bool FULL>
+__device__ __forceinline__ void tile_blocks_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
+                                                  float (&acc)[Q])
+{
+    tile_blocks_bcast_seq<FMT, Q, FULL>(t, xt, b0, nb, acc, std::make_integer_sequence<int, 8>{});
+}
+
+// The per-block dots themselves (debug path), block BI, column j.
+template <int FMT, int Q, int BI>
+__device__ __forceinline__ int tile_block_dot_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int j)
+{
+    Sel8 sel;
+    float sw;
+    decode_block2<FMT, BI>(t, sel, sw);
+    return block_dot_bcast<FMT, Q, BI>(sel, xt, j);
+}
+
+} // namespace dev
+} // namespace rfx
