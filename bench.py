@@ -212,6 +212,39 @@ def bench_moe(torch, R, inputgen, layers, reps):
     return out
 
 
+GEMV_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_xtile.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(GEMV_SOURCES):
+        with open(os.path.join(ROOT, "bit_block_quantized_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(fmt, q):
+    """HBM bytes per launch of the GEMV kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when there is none for this
+    kernel or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gemv_fp{fmt}_q{q}_{N}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def hbm_reference(torch):
     """Device-to-device copy of 2 GiB: (read + write) bytes / time."""
     n = 1 << 31
@@ -255,6 +288,8 @@ def main():
     ap.add_argument("--moe-layers", type=int, default=8, help="0 skips the MoE sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--moe-only", action="store_true", help="skip the GEMV step (profiling the MoE path)")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="with --only: then run 3 plain device copies of this many MiB (counter scaling)")
     ap.add_argument("--only", default=None,
                     help="fmt,q: launch only this GEMV, eagerly, --steps x copies times (profiling)")
     args = ap.parse_args()
@@ -283,8 +318,19 @@ def main():
         n = args.steps * len(work[fmt]["mats"])
         ms = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), n)
         w, a, _ = algorithmic_bytes(R, fmt, q)
-        print(json.dumps({"only": [fmt, q], "launches": n, "us": round(ms * 1e3, 3),
-                          "GBps": round((w + a) / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        out = {"only": [fmt, q], "launches": n, "us": round(ms * 1e3, 3),
+               "GBps": round((w + a) / (ms * 1e-3) / 1e9, 1)}
+        if args.copy_ref_mib:
+            # a plain device copy of known size, so that byte counters read
+            # in the same run can be scaled to bytes
+            nb = args.copy_ref_mib << 20
+            src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            out["copy_ref_bytes"] = nb
+        print(json.dumps(out), flush=True)
         return
 
     per = []
@@ -341,7 +387,8 @@ def main():
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": f"gemv_kernel<FP{dom['fmt'][-1]}, q={dom['q']}>",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(int(dom["fmt"][-1]), dom["q"]),
                      "bytes_per_launch": dom["weight_bytes"] + dom["act_bytes"],
                      "avg_launch_us": dom["us"]},
         "per_kernel": per,
