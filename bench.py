@@ -28,6 +28,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -212,6 +214,37 @@ def bench_moe(torch, R, inputgen, layers, reps):
     return out
 
 
+def bench_prefill(torch, R, inputgen, layer, reps, tokens=2048, k=6):
+    """The prefill-sized layer: 2048 tokens N(0,1), top-6 over 256 experts,
+    shared expert, grouped int8-MFMA FFN. Reports the whole layer's time,
+    tokens/s, int8 MFMA throughput (2 ops per MAC, of the block dots) and
+    the packed-weight stream."""
+    buf = R.MoeBuffers(layer, tokens, k)
+    x = torch.from_numpy(inputgen.tokens(0, 1000, tokens, MOE_H)).cuda()
+
+    def one(i):
+        buf.run(layer, x)
+
+    one(0)
+    torch.cuda.synchronize()
+    idx = buf.topk_idx.cpu().numpy()
+    g = graph_of(torch, one, 1)
+    ms = time_graph(torch, g, reps)
+    n_pairs = tokens * k
+    macs = (n_pairs + tokens) * 3 * MOE_I * MOE_H  # gate, up, down per (token, expert)
+    wbytes = layer.weight_bytes(idx.reshape(-1).tolist())
+    counts = np.bincount(idx.reshape(-1), minlength=MOE_E)
+    log(f"prefill {tokens} tokens top-{k}: {ms * 1e3:.1f} us, {2 * macs / (ms * 1e-3) / 1e12:.1f} int8 TOP/s")
+    return {"us": round(ms * 1e3, 1), "tokens": tokens, "k": k,
+            "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "int8_ops": 2 * macs, "int8_TOPs": round(2 * macs / (ms * 1e-3) / 1e12, 2),
+            "frac_int8_mfma_peak": round(2 * macs / (ms * 1e-3) / 5.0e15, 4),
+            "weight_bytes": int(wbytes), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "tokens_per_expert": {"min": int(counts.min()), "mean": round(float(counts.mean()), 1),
+                                  "max": int(counts.max())},
+            "timing": "HIP graph replay of route + FFN"}
+
+
 GEMV_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_xtile.h")
 
 
@@ -307,8 +340,8 @@ def main():
     R.lib()
     if args.moe_only:
         layers = build_moe_layers(torch, R, inputgen, max(1, args.moe_layers))
-        print(json.dumps({"moe": bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))}),
-              flush=True)
+        print(json.dumps({"moe": bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5)),
+                          "prefill": bench_prefill(torch, R, inputgen, layers[0][0], reps=5)}), flush=True)
         return
     work, acts, ws = build_gemv(torch, R, inputgen)
     log(f"gemv workload ready: copies {[len(work[f]['mats']) for f in FORMATS]}")
@@ -398,6 +431,7 @@ def main():
     if args.moe_layers > 0:
         layers = build_moe_layers(torch, R, inputgen, args.moe_layers)
         out["moe"] = bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))
+        out["prefill"] = bench_prefill(torch, R, inputgen, layers[0][0], reps=5)
         del layers
         torch.cuda.empty_cache()
     try:

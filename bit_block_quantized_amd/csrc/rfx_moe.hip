@@ -27,66 +27,12 @@
 
 #include "rfx_decode.h"
 #include "rfx_internal.h"
+#include "rfx_moe_ws.h"
 
 using namespace rfx;
 using namespace rfx::dev;
 
 namespace {
-
-constexpr int kMaxK = 8;
-constexpr int kMaxE = 256;
-constexpr int kMaxDecodeQ = 4;
-
-// ------------------------------------------------------------------
-// Workspace layout (bytes, 256-aligned regions). Zero-filled once by the
-// caller; counters return to zero at the end of every call.
-// ------------------------------------------------------------------
-struct MoeWs {
-    float *logits;      // [q][E]
-    unsigned *route_cnt;
-    float *h;           // [NP][I]   NP = q*k + q (pairs, then shared per token)
-    int8_t *hq;         // [NP][I]
-    float *hs;          // [NP][I/32]
-    int32_t *hsum;      // [NP][I/32]
-    float *o;           // [NP][H]
-    unsigned *comb_cnt; // [H/64]
-    size_t bytes;
-};
-
-inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
-
-MoeWs carve(void *base, int q, int k, int E, int H, int I)
-{
-    MoeWs w{};
-    const size_t NP = (size_t)q * k + q;
-    size_t off = 0;
-    auto take = [&](size_t n) {
-        size_t o = off;
-        off += align256(n);
-        return o;
-    };
-    const size_t o_logits = take((size_t)q * E * 4);
-    const size_t o_rc = take(4);
-    const size_t o_h = take(NP * I * 4);
-    const size_t o_hq = take(NP * I);
-    const size_t o_hs = take(NP * (I / 32) * 4);
-    const size_t o_hsum = take(NP * (I / 32) * 4);
-    const size_t o_o = take(NP * H * 4);
-    const size_t o_cc = take((size_t)(H / 64 + 1) * 4);
-    w.bytes = off;
-    char *b = static_cast<char *>(base);
-    if (b) {
-        w.logits = reinterpret_cast<float *>(b + o_logits);
-        w.route_cnt = reinterpret_cast<unsigned *>(b + o_rc);
-        w.h = reinterpret_cast<float *>(b + o_h);
-        w.hq = reinterpret_cast<int8_t *>(b + o_hq);
-        w.hs = reinterpret_cast<float *>(b + o_hs);
-        w.hsum = reinterpret_cast<int32_t *>(b + o_hsum);
-        w.o = reinterpret_cast<float *>(b + o_o);
-        w.comb_cnt = reinterpret_cast<unsigned *>(b + o_cc);
-    }
-    return w;
-}
 
 // ------------------------------------------------------------------
 // Shared device helpers.
@@ -766,9 +712,8 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
         return fail(RFX_E_INVAL, "k=%d (must be 1..%d and <= n_experts)", k, kMaxK);
     if (q < 1)
         return fail(RFX_E_INVAL, "q=%d", q);
-    if (q > kMaxDecodeQ)
-        return fail(RFX_E_UNSUPPORTED, "rfx_moe_route_topk: q=%d > %d (prefill routing not built)", q,
-                    kMaxDecodeQ);
+    if (q > kMaxPrefillQ)
+        return fail(RFX_E_UNSUPPORTED, "rfx_moe_route_topk: q=%d > %d", q, kMaxPrefillQ);
     if ((st = check_ptr(x, 16, "x")) || (st = check_ptr(topk_idx, 4, "topk_idx")) ||
         (st = check_ptr(topk_w, 4, "topk_w")) || (st = check_ptr(pairs_sorted, 4, "pairs_sorted")) ||
         (st = check_ptr(expert_off, 4, "expert_off")) || (st = check_ptr(xq, 16, "xq")) ||
@@ -779,6 +724,9 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
     MoeWs w = carve(ws, q, k, L->n_experts, L->hidden, L->inter);
     if (ws_bytes < w.bytes)
         return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    if (q > kMaxDecodeQ) // many tokens: the prefill router and bucketing
+        return prefill_route(L, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, w,
+                             (hipStream_t)stream);
     RouteArgs a{};
     a.x = x;
     a.wr = L->router_w;
@@ -813,8 +761,8 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
         return st;
     if (k < 1 || k > kMaxK || k > L->n_experts || q < 1)
         return fail(RFX_E_INVAL, "q=%d k=%d", q, k);
-    if (q > kMaxDecodeQ)
-        return fail(RFX_E_UNSUPPORTED, "rfx_moe_ffn: q=%d > %d (prefill path not built)", q, kMaxDecodeQ);
+    if (q > kMaxPrefillQ)
+        return fail(RFX_E_UNSUPPORTED, "rfx_moe_ffn: q=%d > %d", q, kMaxPrefillQ);
     if ((st = check_ptr(xq, 16, "xq")) || (st = check_ptr(xs, 4, "xs")) || (st = check_ptr(xsum, 4, "xsum")) ||
         (st = check_ptr(topk_idx, 4, "topk_idx")) || (st = check_ptr(topk_w, 4, "topk_w")) ||
         (st = check_ptr(pairs_sorted, 4, "pairs_sorted")) || (st = check_ptr(expert_off, 4, "expert_off")) ||
@@ -823,6 +771,10 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     MoeWs w = carve(ws, q, k, L->n_experts, L->hidden, L->inter);
     if (ws_bytes < w.bytes)
         return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    if (resid && (st = check_ptr(resid, 16, "resid")))
+        return st;
+    if (q > kMaxDecodeQ) // many tokens: grouped int8 MFMA path
+        return prefill_ffn(L, q, k, xq, xs, topk_w, pairs_sorted, expert_off, resid, y, w, (hipStream_t)stream);
     FfnArgs a{};
     a.gate = static_cast<const uint8_t *>(L->gate.data);
     a.up = static_cast<const uint8_t *>(L->up.data);
@@ -855,8 +807,6 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.resid = resid;
     a.y = y;
     a.ws = w;
-    if (resid && (st = check_ptr(resid, 4, "resid")))
-        return st;
     const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
     const hipStream_t s = (hipStream_t)stream;
     const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);
@@ -890,10 +840,12 @@ int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, f
     int st = check_layer(L);
     if (st)
         return st;
-    if (q < 1 || q > kMaxDecodeQ || k < 1 || k > kMaxK)
+    if (q < 1 || q > kMaxPrefillQ || k < 1 || k > kMaxK)
         return fail(RFX_E_INVAL, "q=%d k=%d", q, k);
     if (!ws)
         return fail(RFX_E_INVAL, "ws is NULL");
+    if (h && q > kMaxDecodeQ)
+        return fail(RFX_E_UNSUPPORTED, "rfx_moe_debug_hidden: h (fp32) is not kept for q > %d", kMaxDecodeQ);
     MoeWs w = carve(const_cast<void *>(ws), q, k, L->n_experts, L->hidden, L->inter);
     const size_t NP = (size_t)q * k + q;
     const hipStream_t s = (hipStream_t)stream;
