@@ -25,19 +25,37 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # Packed fp32 VALU ops (v_pk_*_f32) stay off: scalar fp32 only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE-exact fp32 division and sqrt (the quantizers depend on it).
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA results in ordinary VGPRs (the epilogues read them with VALU ops;
+    # accumulation registers would need a copy per element).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
 
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+
+def _compile(src: str, extra, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return obj
+
 
 def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", OUT + ".tmp"]
+    """Compile every source (in parallel, one process each) and link."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra, verbose), srcs))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", OUT + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
