@@ -169,7 +169,7 @@ int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsu
                          int32_t *dots, void *stream);
 
 /* ------------------------------------------------------------------ */
-/* MoE decode layer.                                                   */
+/* MoE layer: decode (q <= 4 tokens) and prefill (q > 4).               */
 /* ------------------------------------------------------------------ */
 /* Routed experts: gate and up (rows = inter, cols = hidden) and down
  * (rows = hidden, cols = inter), `n_experts` stacked each ([HM] para 2 and
@@ -198,8 +198,12 @@ size_t rfx_moe_workspace_bytes(const rfx_moe_layer *L, int q, int k);
  * [E+1] (exclusive prefix sum of per-expert counts). The tokens are also
  * quantized for the experts (as rfx_quantize_act).
  * x fp32 [q][H]; topk_idx int32 [q][k]; topk_w fp32 [q][k]; 1 <= k <= 8.
- * q in 1..4 here (decode and speculative verification); larger q is the
- * prefill path. */
+ * q in 1..4 (decode and speculative verification): one launch, every
+ * expert row of Wr read once for all q tokens. q in 5..65536 (prefill):
+ * act quant, a router with one workgroup per 8 tokens, and a one-workgroup
+ * stable bucketing that also writes the FFN's work items (chunks of up to
+ * 64 tokens of one expert) into ws; rfx_moe_ffn must then get the same ws,
+ * q and k. */
 int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx,
                        float *topk_w, int32_t *pairs_sorted, int32_t *expert_off, int8_t *xq,
                        float *xs, int32_t *xsum, void *ws, size_t ws_bytes, void *stream);
@@ -209,7 +213,14 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
  * shared expert likewise with weight 1; y_t = resid_t + o_shared + sum_j
  * w_tj o_tj in slot order (deterministic, no float atomics). resid fp32
  * [q][H] or NULL (no residual; it may alias neither y nor ws); y fp32
- * [q][H]. ws: the workspace given to rfx_moe_route_topk may be reused. */
+ * [q][H]. ws: the workspace given to rfx_moe_route_topk may be reused.
+ * q <= 4: block-dequant GEMV kernels, each active expert streamed once for
+ * its tokens. q > 4 (prefill, needs the ws written by rfx_moe_route_topk):
+ * per work item and 32 / 64 rows, the packed blocks are expanded through
+ * their codebooks into int8 tiles and multiplied on v_mfma_i32_16x16x32_i8,
+ * one MFMA K step per 32-weight block, so each int32 result is the exact
+ * block dot, then scaled by the weight and activation block scales in
+ * fp32 ([HM] para 3: integer dot products over the packed codes). */
 int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
                 const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid,
@@ -218,7 +229,8 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
 /* Test hook: after rfx_moe_ffn with the same workspace, copy out the
  * intermediate activations of the last call: h fp32 [(q*k)+q][I] (pairs in
  * pair order, then the shared expert per token), h~ int8 and its scales.
- * Any output pointer may be NULL. */
+ * Any output pointer may be NULL. The prefill path (q > 4) does not keep
+ * the fp32 h: h must be NULL there (RFX_E_UNSUPPORTED otherwise). */
 int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, float *h,
                          int8_t *hq, float *hs, void *stream);
 
