@@ -291,7 +291,7 @@ def hbm_reference(torch):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(R, work, rows=2048, repeats=2):
+def cpu_baseline(R, work, rows=N, repeats=8):
     """The CPU oracle on a bounded sample: the first `rows` rows of every
     matrix, all six (format, q) products, `repeats` times, one thread."""
     import inputgen
