@@ -83,6 +83,104 @@ struct RouteArgs {
     unsigned *cnt;
 };
 
+// Wave-wide reductions through DPP row shifts and row broadcasts (no LDS
+// traffic); the result is read from lane 63, where the prefix completes.
+// Lanes a DPP step does not reach take the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t identity, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t identity, Op op)
+{
+    v = op(v, dpp_u32<0x111, 0xF>(identity, v)); // row_shr:1
+    v = op(v, dpp_u32<0x112, 0xF>(identity, v)); // row_shr:2
+    v = op(v, dpp_u32<0x114, 0xF>(identity, v)); // row_shr:4
+    v = op(v, dpp_u32<0x118, 0xF>(identity, v)); // row_shr:8
+    v = op(v, dpp_u32<0x142, 0xA>(identity, v)); // row_bcast:15 into rows 1, 3
+    v = op(v, dpp_u32<0x143, 0xC>(identity, v)); // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
+{
+    return wave_reduce_u32(v, 0u, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v)
+{
+    return wave_reduce_u32(v, 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+
+__device__ __forceinline__ float wave_fsum(float v)
+{
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(v), 0u, [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    }));
+}
+
+// Total order of fp32 logits as unsigned keys (larger logit, larger key).
+__device__ __forceinline__ uint32_t logit_key(float l)
+{
+    const uint32_t u = __float_as_uint(l);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave: softmax over the E logits of token t held 4 per lane (expert
+// lane + 64 r) and the top k by logit, equal logits to the lower id: k
+// rounds of (largest key, then lowest id holding it). Writes topk_idx /
+// topk_w and s_idx[t*k + j].
+__device__ void wave_topk(const float (&l)[4], int E, int k, int t, int lane, int32_t *topk_idx, float *topk_w,
+                          int *s_idx)
+{
+    uint32_t key[4];
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        live[r] = lane + 64 * r < E;
+        key[r] = live[r] ? logit_key(l[r]) : 0u; // 0 is below every finite logit
+    }
+    float m = 0.0f, z = 0.0f;
+    for (int j = 0; j < k; j++) {
+        uint32_t loc = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            loc = (live[r] && key[r] > loc) ? key[r] : loc;
+        const uint32_t best = wave_umax(loc);
+        uint32_t id = 0xFFFFFFFFu;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (live[r] && key[r] == best)
+                id = min(id, (uint32_t)(lane + 64 * r));
+        const int e = (int)wave_umin(id);
+        float le = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (lane + 64 * r == e) {
+                live[r] = false;
+                le = l[r];
+            }
+        le = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(le), e & 63));
+        if (j == 0) {
+            m = le; // the largest logit
+            float zz = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                zz += lane + 64 * r < E ? expf(l[r] - m) : 0.0f;
+            z = wave_fsum(zz);
+        }
+        if (lane == 0) {
+            topk_idx[t * k + j] = e;
+            topk_w[t * k + j] = expf(le - m) / z;
+            s_idx[t * k + j] = e;
+        }
+    }
+}
+
+// Router for q <= 4 tokens: one workgroup per expert row of Wr; the last
+// workgroup to finish picks the top k per token and buckets the pairs.
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 {
     __shared__ int s_last;
@@ -167,87 +265,34 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
     if (wave < a.q) {
         const int t = wave;
         float l[4];
-        bool taken[4];
-        float m = -INFINITY;
+#pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int e = lane + 64 * r;
-            l[r] = e < a.E ? __hip_atomic_load(a.logits + (size_t)t * a.E + e, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT)
-                           : -INFINITY;
-            taken[r] = e >= a.E;
-            m = fmaxf(m, l[r]);
+            const int ee = lane + 64 * r;
+            l[r] = ee < a.E ? __hip_atomic_load(a.logits + (size_t)t * a.E + ee, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : -INFINITY;
         }
-        for (int o = 32; o > 0; o >>= 1)
-            m = fmaxf(m, __shfl_xor(m, o, 64));
-        float z = 0.0f;
-        for (int r = 0; r < 4; r++)
-            z += (lane + 64 * r) < a.E ? expf(l[r] - m) : 0.0f;
-        for (int o = 32; o > 0; o >>= 1)
-            z += __shfl_xor(z, o, 64);
-        for (int j = 0; j < a.k; j++) {
-            // this lane's best untaken (largest logit, then lowest id)
-            float bv = -INFINITY;
-            int be = 0x7fffffff;
-            for (int r = 0; r < 4; r++) {
-                const int e = lane + 64 * r;
-                if (!taken[r] && (l[r] > bv || (l[r] == bv && e < be))) {
-                    bv = l[r];
-                    be = e;
-                }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oe = __shfl_xor(be, o, 64);
-                if (ov > bv || (ov == bv && oe < be)) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            for (int r = 0; r < 4; r++)
-                if (lane + 64 * r == be)
-                    taken[r] = true;
-            if (lane == 0) {
-                a.topk_idx[t * a.k + j] = be;
-                a.topk_w[t * a.k + j] = expf(bv - m) / z;
-                s_idx[t * a.k + j] = be;
-            }
-        }
+        wave_topk(l, a.E, a.k, t, lane, a.topk_idx, a.topk_w, s_idx);
     }
     __syncthreads();
 
-    // (4) stable bucketing of the q*k pairs by expert (pair p = t*k + j)
+    // (4) stable bucketing of the q*k <= 32 pairs by expert (pair p = t*k+j):
+    //     position = pairs of lower experts + earlier pairs of the same one
     const int np = a.q * a.k;
-    int cnt_e = 0; // thread e counts pairs of expert e
-    for (int e = tid; e < a.E; e += 256) {
-        int c = 0;
-        for (int p = 0; p < np; p++)
-            c += s_idx[p] == e;
-        cnt_e = c;
-    }
-    // exclusive scan over experts (E <= 256: one value per thread)
-    __shared__ int s_scan[256];
-    s_scan[tid] = tid < a.E ? cnt_e : 0;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int v = tid >= o ? s_scan[tid - o] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    if (tid < a.E)
-        a.expert_off[tid] = s_scan[tid] - cnt_e;
-    if (tid == 0)
-        a.expert_off[a.E] = np;
-    __syncthreads();
     if (tid < np) {
-        const int e = s_idx[tid];
-        int rank = 0;
-        for (int p = 0; p < tid; p++)
-            rank += s_idx[p] == e;
-        int before = 0; // pairs of experts below e
+        const int ep = s_idx[tid];
+        int pos = 0;
+        for (int p = 0; p < np; p++) {
+            const int eo = s_idx[p];
+            pos += (eo < ep || (eo == ep && p < tid)) ? 1 : 0;
+        }
+        a.pairs_sorted[pos] = tid;
+    }
+    for (int ee = tid; ee <= a.E; ee += 256) {
+        int before = 0;
         for (int p = 0; p < np; p++)
-            before += s_idx[p] < e;
-        a.pairs_sorted[before + rank] = tid;
+            before += s_idx[p] < ee ? 1 : 0;
+        a.expert_off[ee] = before;
     }
     if (tid == 0)
         __hip_atomic_store(a.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -744,8 +789,8 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
     a.xsum = xsum;
     a.logits = w.logits;
     a.cnt = w.route_cnt;
-    if (L->hidden > 8192)
-        return fail(RFX_E_UNSUPPORTED, "router: hidden=%d > 8192", L->hidden);
+    if (L->hidden > 8192) // one workgroup reads a row as 8 float4 per thread
+        return fail(RFX_E_UNSUPPORTED, "router: hidden=%d > 8192 for q <= 4", L->hidden);
     const int grid = L->n_experts; // one workgroup per expert row
     hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
     return hip_status("route launch");
