@@ -4,12 +4,13 @@ one MI355X.
 
 Step (the headline `value`) = one pass of the dense-GEMV workload: 7168 x
 7168 weights in each of FP2 (10 B / 32 weights), FP3 (14 B) and FP4 (17 B),
-each with q = 1 and q = 4 activation columns (six GEMVs). Weights are
-N(0, 0.02) with 1% outliers x10 (seeds 0 / 10 / 20); columns N(0, 1), seeds
-1..q. Each format keeps R copies of its matrix at distinct addresses
-(R x size >= 512 MB, twice the 256 MB last-level cache); launch i uses copy
-i mod R, so weights stream from HBM. Inputs are resident in HBM before the
-timed region; steps are replayed from a HIP graph.
+each with q = 1 and q = 4 activation columns (six GEMVs), run as one
+grouped launch (rfx_gemv_grouped). Weights are N(0, 0.02) with 1% outliers
+x10 (seeds 0 / 10 / 20); columns N(0, 1), seeds 1..q. Each format keeps R
+copies of its matrix at distinct addresses (R x size >= 512 MB, twice the
+256 MB last-level cache); step i uses copy i mod R, so weights stream from
+HBM. Inputs are resident in HBM before the timed region; steps are replayed
+from a HIP graph. The same step as six separate launches is reported too.
 
 value = algorithmic bytes of the step (packed weights + quantized
 activations read) / step time, in GB/s.
@@ -89,6 +90,25 @@ def gemv_launch(R, work, acts, ws, fmt, q, i):
     mats = work[fmt]["mats"]
     a = acts[q]
     R.gemv(mats[i % len(mats)], a["xq"], a["xs"], a["xsum"], q, a["y"], ws[(fmt, q)])
+
+
+def grouped_step_jobs(torch, R, work, acts):
+    """Job arrays of the grouped step, one per rotation index, and their
+    (shared, zero-filled) workspace. Each job writes its own output."""
+    rot = max(len(work[f]["mats"]) for f in FORMATS)
+    ys = {(f, q): torch.empty((q, N), dtype=torch.float32, device="cuda") for f in FORMATS for q in (1, 4)}
+    arrs = []
+    for i in range(rot):
+        jobs = []
+        for fmt in FORMATS:
+            mats = work[fmt]["mats"]
+            for q in (1, 4):
+                a = acts[q]
+                jobs.append((mats[i % len(mats)], q, a["xq"], a["xs"], a["xsum"], ys[(fmt, q)]))
+        arrs.append(R.gemv_jobs(jobs))
+    n = R.gemv_grouped_workspace_bytes(arrs[0])
+    gws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
+    return arrs, gws, ys
 
 
 def graph_of(torch, fn, n):
@@ -257,11 +277,12 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(fmt, q):
-    """HBM bytes per launch of the GEMV kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when there is none for this
-    kernel or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"gemv_fp{fmt}_q{q}_{N}_pmc.txt")
+def measured_traffic(kernel):
+    """HBM bytes per launch of a GEMV kernel ("grouped", or "fp4_q4" and the
+    like) from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or
+    None when there is none for it or the kernel sources changed since it
+    was taken."""
+    path = os.path.join(ROOT, "profiles", f"gemv_{kernel}_{N}_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -324,7 +345,8 @@ def main():
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="with --only: then run 3 plain device copies of this many MiB (counter scaling)")
     ap.add_argument("--only", default=None,
-                    help="fmt,q: launch only this GEMV, eagerly, --steps x copies times (profiling)")
+                    help="fmt,q (or 'grouped': the grouped step): launch only this, eagerly, "
+                         "--steps x copies times (profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the decode path has no multi-GPU part); "
@@ -346,13 +368,21 @@ def main():
     work, acts, ws = build_gemv(torch, R, inputgen)
     log(f"gemv workload ready: copies {[len(work[f]['mats']) for f in FORMATS]}")
 
+    garrs, gws, _ = grouped_step_jobs(torch, R, work, acts)
+    step_bytes = sum(sum(algorithmic_bytes(R, f, q)[:2]) for f in FORMATS for q in (1, 4))
     if args.only:
-        fmt, q = (int(v) for v in args.only.split(","))
-        n = args.steps * len(work[fmt]["mats"])
-        ms = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), n)
-        w, a, _ = algorithmic_bytes(R, fmt, q)
-        out = {"only": [fmt, q], "launches": n, "us": round(ms * 1e3, 3),
-               "GBps": round((w + a) / (ms * 1e-3) / 1e9, 1)}
+        if args.only == "grouped":
+            n = args.steps * len(garrs)
+            ms = time_eager(torch, lambda i: R.gemv_grouped(garrs[i % len(garrs)], gws), n)
+            out = {"only": "grouped", "launches": n, "us": round(ms * 1e3, 3),
+                   "GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1)}
+        else:
+            fmt, q = (int(v) for v in args.only.split(","))
+            n = args.steps * len(work[fmt]["mats"])
+            ms = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), n)
+            w, a, _ = algorithmic_bytes(R, fmt, q)
+            out = {"only": [fmt, q], "launches": n, "us": round(ms * 1e3, 3),
+                   "GBps": round((w + a) / (ms * 1e-3) / 1e9, 1)}
         if args.copy_ref_mib:
             # a plain device copy of known size, so that byte counters read
             # in the same run can be scaled to bytes
@@ -381,25 +411,30 @@ def main():
             log(f"FP{fmt} q={q}: {us:.2f} us (eager {us_eager:.2f})  {(w + a) / us / 1e3:.0f} GB/s")
             del g
 
-    # whole step: the six GEMVs back to back, one graph holding `rot` steps
-    step_bytes = sum(p["weight_bytes"] + p["act_bytes"] for p in per)
-    rot = max(len(work[f]["mats"]) for f in FORMATS)
+    # whole step: the six GEMVs as one grouped launch (the headline) and,
+    # for comparison, as six launches back to back; one graph holds `rot`
+    # steps
+    assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per)
+    rot = len(garrs)
 
-    def step(i):
+    def step_six(i):
         for fmt in FORMATS:
             for q in (1, 4):
                 gemv_launch(R, work, acts, ws, fmt, q, i)
 
-    g = graph_of(torch, step, rot)
+    g = graph_of(torch, step_six, rot)
+    ms_six = time_graph(torch, g, max(1, -(-args.steps // rot))) / rot
+    del g
+    g = graph_of(torch, lambda i: R.gemv_grouped(garrs[i], gws), rot)
     for _ in range(args.warmup):
         g.replay()
     reps = max(1, -(-args.steps // rot))
     ms = time_graph(torch, g, reps) / rot
     value = step_bytes / (ms * 1e-3) / 1e9
     del g
+    log(f"step: grouped {ms * 1e3:.2f} us ({value:.0f} GB/s), six launches {ms_six * 1e3:.2f} us")
 
-    dom = max(per, key=lambda p: p["us"])
-    ach = (dom["weight_bytes"] + dom["act_bytes"]) / dom["us"] / 1e3
+    ach = value  # one launch per step: the step is the dominant kernel
     out = {
         "metric": "packed-weight GB/s & % HBM peak for q=1/q=4 GEMV and MoE decode layer",
         "value": round(value, 1),
@@ -416,14 +451,17 @@ def main():
         "config": {"workload": "dense GEMV 7168x7168, FP2/FP3/FP4 x q=1,4 per step, rotated copies",
                    "rows": N, "cols": K, "formats": ["FP2", "FP3", "FP4"], "q": [1, 4],
                    "copies": {f"FP{f}": len(work[f]["mats"]) for f in FORMATS},
-                   "timing": "HIP graph replay"},
+                   "timing": "HIP graph replay, one grouped launch per step"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": f"gemv_kernel<FP{dom['fmt'][-1]}, q={dom['q']}>",
+        "roofline": {"bound": "hbm", "kernel": "gemv_grouped_kernel (FP2/FP3/FP4 x q=1,4, 7168x7168)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(int(dom["fmt"][-1]), dom["q"]),
-                     "bytes_per_launch": dom["weight_bytes"] + dom["act_bytes"],
-                     "avg_launch_us": dom["us"]},
+                     "traffic": measured_traffic("grouped"),
+                     "bytes_per_launch": step_bytes,
+                     "avg_launch_us": round(ms * 1e3, 3)},
+        "step_six_launches": {"us": round(ms_six * 1e3, 3),
+                              "GBps": round(step_bytes / (ms_six * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(step_bytes / (ms_six * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "per_kernel": per,
     }
     del work

@@ -38,6 +38,15 @@ class QMat(ctypes.Structure):
                 ("count", ctypes.c_int32), ("data", ctypes.c_void_p)]
 
 
+class GemvJob(ctypes.Structure):
+    _fields_ = [("W", QMat), ("q", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("xq", ctypes.c_void_p), ("xs", ctypes.c_void_p), ("xsum", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
+
+
+MAX_GEMV_JOBS = 16
+
+
 class MoeLayerC(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -69,6 +78,8 @@ _SIGS = {
     "rfx_gemv": ([_P, _P, _P, _P, _I, _P, _P, _SZ, _P], _I),
     "rfx_gemv_q1": ([_P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_gemv_q4": ([_P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "rfx_gemv_grouped_workspace_bytes": ([_P, _I], _SZ),
+    "rfx_gemv_grouped": ([_P, _I, _P, _SZ, _P], _I),
     "rfx_debug_block_dots": ([_P, _P, _P, _I, _P, _P], _I),
     "rfx_moe_workspace_bytes": ([_P, _I, _I], _SZ),
     "rfx_moe_route_topk": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
@@ -240,6 +251,27 @@ def gemv_q4(W: DeviceQMat, xq, xs, xsum, y, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().rfx_gemv_q4(W.ref(), _dptr(xq), _dptr(xs), _dptr(xsum), _dptr(y), _dptr(ws),
                              ws_bytes, _stream(stream)))
+
+
+def gemv_jobs(jobs):
+    """[(W: DeviceQMat, q, xq, xs, xsum, y), ...] -> ctypes array of rfx_gemv_job."""
+    arr = (GemvJob * len(jobs))()
+    for i, (W, q, xq, xs, xsum, y) in enumerate(jobs):
+        arr[i] = GemvJob(W.c, q, 0, _dptr(xq), _dptr(xs), _dptr(xsum), _dptr(y))
+    return arr
+
+
+def gemv_grouped_workspace_bytes(jobs) -> int:
+    arr = jobs if isinstance(jobs, ctypes.Array) else gemv_jobs(jobs)
+    return int(lib().rfx_gemv_grouped_workspace_bytes(arr, len(arr)))
+
+
+def gemv_grouped(jobs, ws=None, stream=None):
+    """Several independent GEMVs in one launch; jobs as for gemv_jobs (or
+    its result, reusable across calls)."""
+    arr = jobs if isinstance(jobs, ctypes.Array) else gemv_jobs(jobs)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().rfx_gemv_grouped(arr, len(arr), _dptr(ws), ws_bytes, _stream(stream)))
 
 
 def debug_block_dots(W: DeviceQMat, xq, xsum, q, dots, stream=None):

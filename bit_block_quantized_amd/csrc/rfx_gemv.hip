@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
 
 #include "rfx_decode.h"
 #include "rfx_xtile.h"
@@ -191,14 +192,15 @@ __device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int 
 // One workgroup = W waves on one 64-row group; its tiles [s_begin, s_end)
 // are split into contiguous runs, one per wave. Each wave keeps the next
 // tile's loads in flight while it decodes the current one.
+//
+// Workgroup p (of P) of row group g; red holds W x Q x 64 floats of LDS.
 template <int FMT, int Q, bool DOTS, bool FULL>
-__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
+__device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float *red)
 {
     // wave index is uniform per wave; say so, so the tile index, the
     // activation addresses and the loop bounds live in SGPRs.
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const int g = blockIdx.y, p = blockIdx.x; // grid = (P, G)
     const int row = g * 64 + lane;
     float acc[Q];
     XCols<Q> xc;
@@ -243,21 +245,22 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         return;
 
     // Fixed-order reduction over the waves of this workgroup.
-    __shared__ float red[16][Q][64];
+#define RED(w, j) red[((w) * Q + (j)) * 64 + lane]
 #pragma unroll
     for (int j = 0; j < Q; j++)
-        red[wave][j][lane] = acc[j];
+        RED(wave, j) = acc[j];
     __syncthreads();
     if (wave != 0)
         return;
     float val[Q];
 #pragma unroll
     for (int j = 0; j < Q; j++) {
-        float t = red[0][j][lane];
+        float t = RED(0, j);
         for (int w = 1; w < W; w++)
-            t += red[w][j][lane];
+            t += RED(w, j);
         val[j] = t;
     }
+#undef RED
     if (a.P == 1) {
         if (row < a.N) {
 #pragma unroll
@@ -306,6 +309,50 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
             if (active[j])
                 a.y[(size_t)j * a.N + row] = val[j];
     }
+}
+
+// One GEMV; grid = (P, G).
+template <int FMT, int Q, bool DOTS, bool FULL>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
+{
+    __shared__ float red[16 * Q * 64];
+    gemv_body<FMT, Q, DOTS, FULL>(a, blockIdx.x, blockIdx.y, red);
+}
+
+// Several independent GEMVs in one launch: job j owns the workgroups
+// [wg_begin[j], wg_begin[j + 1]), ordered by row group then split index,
+// so one job's last workgroups run while the next job's first tiles stream
+// and only the final job's tail is exposed.
+constexpr int kMaxJobs = RFX_MAX_GEMV_JOBS;
+
+struct GroupArgs {
+    GemvArgs job[kMaxJobs];
+    int kind[kMaxJobs]; // 8 * fmt + q
+    int wg_begin[kMaxJobs + 1];
+    int n;
+};
+
+template <bool FULL>
+__global__ __launch_bounds__(1024) void gemv_grouped_kernel(GroupArgs ga)
+{
+    __shared__ float red[16 * 4 * 64];
+    const int bid = blockIdx.x;
+    int j = 0;
+    while (j + 1 < ga.n && bid >= ga.wg_begin[j + 1])
+        j++;
+    j = __builtin_amdgcn_readfirstlane(j);
+    const GemvArgs &a = ga.job[j];
+    const int local = bid - ga.wg_begin[j];
+    const int p = local & (a.P - 1), g = local / a.P;
+#define RFX_JOB(F, QQ)                                                                                        \
+    case 8 * F + QQ: gemv_body<F, QQ, false, FULL>(a, p, g, red); break;
+    switch (ga.kind[j]) {
+        RFX_JOB(RFX_FP2, 1) RFX_JOB(RFX_FP2, 2) RFX_JOB(RFX_FP2, 3) RFX_JOB(RFX_FP2, 4)
+        RFX_JOB(RFX_FP3, 1) RFX_JOB(RFX_FP3, 2) RFX_JOB(RFX_FP3, 3) RFX_JOB(RFX_FP3, 4)
+        RFX_JOB(RFX_FP4, 1) RFX_JOB(RFX_FP4, 2) RFX_JOB(RFX_FP4, 3) RFX_JOB(RFX_FP4, 4)
+    default: break;
+    }
+#undef RFX_JOB
 }
 
 struct LaunchShape {
@@ -363,6 +410,28 @@ int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
     }
     return fail(RFX_E_INVAL, "unknown format");
 }
+
+// Grouped launches: every job runs W waves per workgroup (one block size
+// per launch); job j splits its S tiles over P workgroups, the smallest
+// power of two with P * W >= S (at most kGroupPMax).
+#ifndef RFX_GROUP_W
+#define RFX_GROUP_W 4
+#endif
+#ifndef RFX_GROUP_PMAX
+#define RFX_GROUP_PMAX 8
+#endif
+constexpr int kGroupW = RFX_GROUP_W;
+constexpr int kGroupPMax = RFX_GROUP_PMAX;
+
+int grouped_P(int S)
+{
+    int P = 1;
+    while (P < kGroupPMax && P * kGroupW < S)
+        P <<= 1;
+    return P;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int check_act(const int8_t *xq, const float *xs, const int32_t *xsum, bool need_xs)
 {
@@ -454,6 +523,100 @@ int rfx_gemv_q4(const rfx_qmat *W, const int8_t *xq, const float *xs, const int3
                 void *ws, size_t ws_bytes, void *stream)
 {
     return rfx_gemv(W, xq, xs, xsum, 4, y, ws, ws_bytes, stream);
+}
+
+size_t rfx_gemv_grouped_workspace_bytes(const rfx_gemv_job *jobs, int n_jobs)
+{
+    if (!jobs || n_jobs < 1 || n_jobs > kMaxJobs)
+        return 0;
+    size_t total = 0;
+    for (int j = 0; j < n_jobs; j++) {
+        const rfx_qmat &W = jobs[j].W;
+        if (!fmt_ok(W.fmt) || W.rows < 1 || W.cols < 32 || jobs[j].q < 1 || jobs[j].q > 4)
+            return 0;
+        const int G = (int)ceil_div(W.rows, kTileRows), S = (int)ceil_div(W.cols, kTileCols);
+        total += align256(workspace_for(G, grouped_P(S), jobs[j].q));
+    }
+    return total;
+}
+
+int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!jobs)
+        return fail(RFX_E_INVAL, "rfx_gemv_grouped: jobs is NULL");
+    if (n_jobs < 1 || n_jobs > kMaxJobs)
+        return fail(RFX_E_INVAL, "rfx_gemv_grouped: n_jobs=%d (must be 1..%d)", n_jobs, kMaxJobs);
+    // Longest work first: jobs whose workgroups take longest (most VALU per
+    // block, see the block decoders) start first and the short ones fill
+    // the end of the launch. Only the launch order changes; each job still
+    // writes its own outputs.
+    int order[kMaxJobs];
+    for (int j = 0; j < n_jobs; j++)
+        order[j] = j;
+    auto cost = [&](int j) {
+        const int f = jobs[j].W.fmt, q = jobs[j].q;
+        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : 75;
+        return base + 12 * q;
+    };
+    for (int i = 1; i < n_jobs; i++) // stable insertion sort, n <= 16
+        for (int k = i; k > 0 && cost(order[k]) > cost(order[k - 1]); k--) {
+            const int t = order[k];
+            order[k] = order[k - 1];
+            order[k - 1] = t;
+        }
+    GroupArgs ga{};
+    ga.n = n_jobs;
+    bool full = true;
+    size_t ws_off = 0;
+    int wgs = 0;
+    for (int jj = 0; jj < n_jobs; jj++) {
+        const int j = order[jj];
+        const rfx_gemv_job &jb = jobs[j];
+        char name[32];
+        snprintf(name, sizeof name, "jobs[%d].W", j);
+        int st = check_qmat(&jb.W, name, false);
+        if (st)
+            return st;
+        if (jb.q < 1 || jb.q > 4)
+            return fail(RFX_E_INVAL, "rfx_gemv_grouped: jobs[%d].q=%d (must be 1..4)", j, jb.q);
+        if ((st = check_act(jb.xq, jb.xs, jb.xsum, true)) || (st = check_ptr(jb.y, 4, "y")))
+            return fail(st, "rfx_gemv_grouped: jobs[%d]: %s", j, rfx_last_error());
+        const int G = (int)ceil_div(jb.W.rows, kTileRows), S = (int)ceil_div(jb.W.cols, kTileCols);
+        const int P = grouped_P(S);
+        GemvArgs &a = ga.job[jj];
+        a.W = static_cast<const uint8_t *>(jb.W.data);
+        a.N = jb.W.rows;
+        a.K = jb.W.cols;
+        a.S = S;
+        a.nb = jb.W.cols / 32;
+        a.P = P;
+        a.xq = jb.xq;
+        a.xs = jb.xs;
+        a.xsum = jb.xsum;
+        a.y = jb.y;
+        const size_t need = workspace_for(G, P, jb.q);
+        a.slots = need ? reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ws) + ws_off) : nullptr;
+        ws_off += align256(need);
+        ga.kind[jj] = 8 * jb.W.fmt + jb.q;
+        ga.wg_begin[jj] = wgs;
+        wgs += G * P;
+        full = full && jb.W.cols % kTileCols == 0;
+    }
+    ga.wg_begin[n_jobs] = wgs;
+    if (ws_off) {
+        if (!ws || ws_bytes < ws_off)
+            return fail(RFX_E_WORKSPACE, "rfx_gemv_grouped: workspace %zu < %zu bytes", ws ? ws_bytes : (size_t)0,
+                        ws_off);
+        int st = check_ptr(ws, 256, "ws");
+        if (st)
+            return st;
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    if (full)
+        hipLaunchKernelGGL(gemv_grouped_kernel<true>, dim3(wgs), dim3(64 * kGroupW), 0, st, ga);
+    else
+        hipLaunchKernelGGL(gemv_grouped_kernel<false>, dim3(wgs), dim3(64 * kGroupW), 0, st, ga);
+    return hip_status("grouped gemv launch");
 }
 
 int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,

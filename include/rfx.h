@@ -163,6 +163,34 @@ int rfx_gemv_q1(const rfx_qmat *W, const int8_t *xq, const float *xs, const int3
 int rfx_gemv_q4(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum,
                 float *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Several independent GEMVs in one launch (up to RFX_MAX_GEMV_JOBS), each
+ * with its own matrix, q and activation / output buffers, computing exactly
+ * what rfx_gemv computes for it. One job's last workgroups overlap the next
+ * job's weight stream, so a batch of projections that do not depend on one
+ * another (a decode step's query / key / value, or gate and up) pays the
+ * launch and reduction tail once instead of once per matrix. Jobs may mix
+ * formats, shapes and q; whatever their order in `jobs`, the ones with the
+ * most decode work per workgroup start first. Each job's result depends
+ * only on its own shape (fixed-order reduction), so it is deterministic,
+ * though not bit-identical to a lone rfx_gemv (its K split may differ).
+ * Field rules are rfx_gemv's; output buffers must not overlap.
+ * ws: zero-filled workspace of rfx_gemv_grouped_workspace_bytes(jobs,
+ * n_jobs) bytes (NULL allowed when that is 0); left zeroed on return.
+ * Errors: RFX_E_INVAL (n_jobs outside 1..RFX_MAX_GEMV_JOBS, or a bad job:
+ * the message names its index), RFX_E_ALIGN, RFX_E_WORKSPACE, RFX_E_HIP. */
+#define RFX_MAX_GEMV_JOBS 16
+typedef struct rfx_gemv_job {
+    rfx_qmat W;          /* count must be 1 */
+    int32_t q;           /* 1..4 */
+    int32_t reserved;
+    const int8_t *xq;    /* [q][W.cols] */
+    const float *xs;     /* [q][W.cols / 32] */
+    const int32_t *xsum; /* [q][W.cols / 32] */
+    float *y;            /* [q][W.rows] */
+} rfx_gemv_job;
+size_t rfx_gemv_grouped_workspace_bytes(const rfx_gemv_job *jobs, int n_jobs);
+int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_bytes, void *stream);
+
 /* Test hook: the same decode path, storing every per-block integer dot
  * D[j][n][b] (int32 [q][N][K/32]) instead of the scaled sum. */
 int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,

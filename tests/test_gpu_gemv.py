@@ -131,3 +131,63 @@ def test_gemv_deterministic_and_columns_independent(fmt):
         y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
         R.gemv(dW, xq[j:j + 1], xs[j:j + 1], xsum[j:j + 1], 1, y1, ws1)
         assert rel_err(y1.cpu().numpy()[0], outs[0][j]) <= 1e-6
+
+
+# ---------------------------------------------------------- grouped gemv
+
+def _grouped(torch, specs, seed, big=False):
+    """specs [(fmt, q, N, K)] through one rfx_gemv_grouped launch, twice on
+    the same workspace; returns [(y_gpu_call1, y_gpu_call2, y_oracle)]."""
+    jobs, refs = [], []
+    for i, (fmt, q, N, K) in enumerate(specs):
+        if big:
+            W, blocks = _big(fmt)
+        else:
+            W = inputgen.dense_weight(N, K, seed=seed + i, outliers=True)
+            blocks = O.quantize_matrix(fmt, W)
+        x = inputgen.activations(q, K, seed=seed + 100 + i)
+        xq, xs, xsum = quantize_on_gpu(torch, x)
+        y = torch.full((q, N), float("nan"), dtype=torch.float32, device="cuda")
+        jobs.append((upload_matrix(torch, fmt, W), q, xq, xs, xsum, y))
+        oq, os_ = O.quantize_act(x)
+        refs.append(O.gemv(fmt, blocks, oq, os_))
+    arr = R.gemv_jobs(jobs)
+    ws = workspace(torch, R.gemv_grouped_workspace_bytes(arr))
+    R.gemv_grouped(arr, ws)
+    _sync(torch)
+    first = [j[5].cpu().numpy().copy() for j in jobs]
+    for j in jobs:
+        j[5].fill_(float("nan"))
+    R.gemv_grouped(arr, ws)  # the workspace must come back zeroed
+    _sync(torch)
+    if ws is not None:
+        assert int(ws.count_nonzero()) == 0
+    return [(a, j[5].cpu().numpy(), r) for a, j, r in zip(first, jobs, refs)]
+
+
+@pytest.mark.parametrize("specs", [
+    # mixed formats and q, ragged N and K (partial tiles: K % 256 != 0)
+    [(2, 1, 200, 544), (3, 4, 65, 288), (4, 2, 130, 2080), (2, 3, 1, 32), (4, 4, 64, 256)],
+    # every K a multiple of 256 (the straight-line full-tile code), split K
+    [(4, 1, 1024, 1024), (2, 4, 300, 4096), (3, 2, 77, 2048), (4, 3, 512, 768)],
+    # a single job
+    [(3, 4, 640, 1536)],
+])
+def test_gemv_grouped_small(specs):
+    torch = need_gpu()
+    say(f"gemv grouped {specs}")
+    for i, (a, b, ref) in enumerate(_grouped(torch, specs, seed=40)):
+        assert np.array_equal(a, b), i  # deterministic
+        assert rel_err(a, ref) <= TOL, (i, specs[i], rel_err(a, ref))
+
+
+def test_gemv_grouped_7168_six_jobs():
+    """The 7168 x 7168 workload as the benchmark runs it: FP2/FP3/FP4 x
+    q = 1, 4 in one launch."""
+    torch = need_gpu()
+    say("gemv grouped 7168 x 6")
+    specs = [(fmt, q, 7168, 7168) for fmt in FMTS for q in (1, 4)]
+    for i, (a, b, ref) in enumerate(_grouped(torch, specs, seed=60, big=True)):
+        err = rel_err(a, ref)
+        say(f"  job {specs[i][:2]} rel err {err:.3e}")
+        assert np.array_equal(a, b) and err <= TOL, i

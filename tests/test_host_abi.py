@@ -172,6 +172,28 @@ def test_device_entry_validation_without_gpu():
     st = L.rfx_gemv(ctypes.byref(big), _fake(good), _fake(good), _fake(good), 4, _fake(good),
                     _fake(good), need - 4, null)
     assert st == -5
+    # grouped GEMV: job count, a bad job (named by index), workspace size
+    f = _fake(good).value
+    jobs = (R.GemvJob * 3)(*[R.GemvJob(R.QMat(fmt, 7168, 7168, 1, good), q, 0, f, f, f, f)
+                             for fmt, q in ((2, 1), (3, 4), (4, 2))])
+    assert L.rfx_gemv_grouped(jobs, 0, null, 0, null) == -1
+    assert L.rfx_gemv_grouped(jobs, 17, null, 0, null) == -1
+    assert L.rfx_gemv_grouped(None, 1, null, 0, null) == -1
+    need = L.rfx_gemv_grouped_workspace_bytes(jobs, 3)
+    assert need >= 3 * 256 and need % 256 == 0
+    assert L.rfx_gemv_grouped(jobs, 3, _fake(good), need - 256, null) == -5
+    assert L.rfx_gemv_grouped(jobs, 3, None, need, null) == -5
+    jobs[1].q = 5
+    assert L.rfx_gemv_grouped(jobs, 3, _fake(good), need, null) == -1
+    assert b"jobs[1]" in L.rfx_last_error()
+    jobs[1].q = 4
+    jobs[2].xq = good + 4
+    assert L.rfx_gemv_grouped(jobs, 3, _fake(good), need, null) == -2
+    assert b"jobs[2]" in L.rfx_last_error()
+    jobs[2].xq = f
+    jobs[0].W.cols = 7000
+    assert L.rfx_gemv_grouped(jobs, 3, _fake(good), need, null) == -1
+    assert b"jobs[0]" in L.rfx_last_error()
     assert L.rfx_quantize_act(_fake(good), 1, 40, _fake(good), _fake(good), _fake(good), null) == -1
     assert L.rfx_quantize_act(None, 1, 64, _fake(good), _fake(good), _fake(good), null) == -1
     assert L.rfx_debug_block_dots(ctypes.byref(W), _fake(good), _fake(good), 0, _fake(good), null) == -1
