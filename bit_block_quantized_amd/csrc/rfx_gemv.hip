@@ -189,78 +189,21 @@ __device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int 
     }
 }
 
-// One workgroup = W waves on one 64-row group; its tiles [s_begin, s_end)
-// are split into contiguous runs, one per wave. Each wave keeps the next
-// tile's loads in flight while it decodes the current one.
-//
-// Workgroup p (of P) of row group g; red holds W x Q x 64 floats of LDS.
-template <int FMT, int Q, bool DOTS, bool FULL>
-__device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float *red)
+// Wave 0 of a workgroup: sum the W waves' partials (fixed order) and
+// either store y or climb the split-K exchange tree.
+template <int Q>
+__device__ __forceinline__ void gemv_finish(const GemvArgs &a, int p, int g, int W, const float *red)
 {
-    // wave index is uniform per wave; say so, so the tile index, the
-    // activation addresses and the loop bounds live in SGPRs.
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int W = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int row = g * 64 + lane;
-    float acc[Q];
-    XCols<Q> xc;
-    xc.xq = a.xq;
-    xc.xs = a.xs;
-    xc.xsum = a.xsum;
-#pragma unroll
-    for (int j = 0; j < Q; j++) {
-        acc[j] = 0.0f;
-        xc.xoff[j] = (uint32_t)j * (uint32_t)a.K;
-        xc.moff[j] = (uint32_t)j * (uint32_t)a.nb;
-    }
-
-    const int nw = a.P * W, v = p * W + wave;
-    // the division runs on the vector unit; pin its uniform result to SGPRs
-    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * v) / (unsigned)nw));
-    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * (v + 1)) / (unsigned)nw));
-    const uint8_t *gbase = a.W + (size_t)g * a.S * TileFmt<FMT>::bytes;
-    if (s_end - s_begin == 1) {
-        // the common case: one tile per wave, straight-line code, so each
-        // block waits only for its own chunks
-        constexpr bool BC = use_bcast<Q>();
-        const WTile<FMT, Q> t = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb);
-        compute_tile<FMT, Q, DOTS, FULL, BC>(t, s_begin, row, a, xc, acc);
-    } else if (s_begin < s_end) {
-        // two tile buffers used in turn (no register copies, which would
-        // wait for the loads they copy): tile s + 1 in flight while s is
-        // computed
-        WTile<FMT, Q> ta = load_wtile<FMT, Q, FULL, false>(gbase, s_begin, lane, xc, a.nb), tb;
-        for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end)
-                tb = load_wtile<FMT, Q, FULL, false>(gbase, s + 1, lane, xc, a.nb);
-            compute_tile<FMT, Q, DOTS, FULL, false>(ta, s, row, a, xc, acc);
-            if (s + 1 >= s_end)
-                break;
-            if (s + 2 < s_end)
-                ta = load_wtile<FMT, Q, FULL, false>(gbase, s + 2, lane, xc, a.nb);
-            compute_tile<FMT, Q, DOTS, FULL, false>(tb, s + 1, row, a, xc, acc);
-        }
-    }
-    if (DOTS)
-        return;
-
-    // Fixed-order reduction over the waves of this workgroup.
-#define RED(w, j) red[((w) * Q + (j)) * 64 + lane]
-#pragma unroll
-    for (int j = 0; j < Q; j++)
-        RED(wave, j) = acc[j];
-    __syncthreads();
-    if (wave != 0)
-        return;
     float val[Q];
 #pragma unroll
     for (int j = 0; j < Q; j++) {
-        float t = RED(0, j);
+        float t = red[j * 64 + lane];
         for (int w = 1; w < W; w++)
-            t += RED(w, j);
+            t += red[(w * Q + j) * 64 + lane];
         val[j] = t;
     }
-#undef RED
     if (a.P == 1) {
         if (row < a.N) {
 #pragma unroll
@@ -311,6 +254,74 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float
     }
 }
 
+// One workgroup = W waves on one 64-row group; its tiles [s_begin, s_end)
+// are split into contiguous runs, one per wave. Each wave keeps the next
+// tile's loads in flight while it decodes the current one.
+//
+// Workgroup p (of P) of row group g; red holds W x Q x 64 floats of LDS.
+// LBC: the multi-tile loop takes the broadcast path too (two activation
+// slices in registers; affordable below 1024 threads per workgroup).
+template <int FMT, int Q, bool DOTS, bool FULL, bool LBC = false>
+__device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float *red)
+{
+    // wave index is uniform per wave; say so, so the tile index, the
+    // activation addresses and the loop bounds live in SGPRs.
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const int row = g * 64 + lane;
+    float acc[Q];
+    XCols<Q> xc;
+    xc.xq = a.xq;
+    xc.xs = a.xs;
+    xc.xsum = a.xsum;
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        acc[j] = 0.0f;
+        xc.xoff[j] = (uint32_t)j * (uint32_t)a.K;
+        xc.moff[j] = (uint32_t)j * (uint32_t)a.nb;
+    }
+
+    const int nw = a.P * W, v = p * W + wave;
+    // the division runs on the vector unit; pin its uniform result to SGPRs
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * v) / (unsigned)nw));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * (v + 1)) / (unsigned)nw));
+    const uint8_t *gbase = a.W + (size_t)g * a.S * TileFmt<FMT>::bytes;
+    if (s_end - s_begin == 1) {
+        // the common case: one tile per wave, straight-line code, so each
+        // block waits only for its own chunks
+        constexpr bool BC = use_bcast<Q>();
+        const WTile<FMT, Q> t = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb);
+        compute_tile<FMT, Q, DOTS, FULL, BC>(t, s_begin, row, a, xc, acc);
+    } else if (s_begin < s_end) {
+        // two tile buffers used in turn (no register copies, which would
+        // wait for the loads they copy): tile s + 1 in flight while s is
+        // computed
+        constexpr bool BC = LBC && use_bcast<Q>();
+        WTile<FMT, Q> ta = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb), tb;
+        for (int s = s_begin; s < s_end; s += 2) {
+            if (s + 1 < s_end)
+                tb = load_wtile<FMT, Q, FULL, BC>(gbase, s + 1, lane, xc, a.nb);
+            compute_tile<FMT, Q, DOTS, FULL, BC>(ta, s, row, a, xc, acc);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end)
+                ta = load_wtile<FMT, Q, FULL, BC>(gbase, s + 2, lane, xc, a.nb);
+            compute_tile<FMT, Q, DOTS, FULL, BC>(tb, s + 1, row, a, xc, acc);
+        }
+    }
+    if (DOTS)
+        return;
+
+    // Fixed-order reduction over the waves of this workgroup: every wave
+    // leaves its partials in LDS, wave 0 sums and finishes.
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        red[(wave * Q + j) * 64 + lane] = acc[j];
+    __syncthreads();
+    if (wave == 0)
+        gemv_finish<Q>(a, p, g, W, red);
+}
+
 // One GEMV; grid = (P, G).
 template <int FMT, int Q, bool DOTS, bool FULL>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
@@ -319,23 +330,38 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     gemv_body<FMT, Q, DOTS, FULL>(a, blockIdx.x, blockIdx.y, red);
 }
 
-// Several independent GEMVs in one launch: job j owns the workgroups
-// [wg_begin[j], wg_begin[j + 1]), ordered by row group then split index,
-// so one job's last workgroups run while the next job's first tiles stream
-// and only the final job's tail is exposed.
+// Several independent GEMVs in one launch. The workgroups are the jobs'
+// (row group, K split) pairs, numbered job by job with the longest work
+// first, so the heavy jobs' workgroups are placed first and the light
+// ones fill in after them; one job's last workgroups run while the next
+// job's weights stream, and only the launch's end is a tail.
 constexpr int kMaxJobs = RFX_MAX_GEMV_JOBS;
+
+// Every job runs W waves per workgroup (one block size per launch), each
+// wave a contiguous run of tiles with the next tile in flight. K is split
+// over P workgroups only as far as needed to give the launch about two
+// waves per SIMD: a launch of several large matrices runs one workgroup
+// per row group (no exchange at all, every workgroup resident at once); a
+// lone small matrix still fills the chip.
+#ifndef RFX_GROUP_W
+#define RFX_GROUP_W 4
+#endif
+#ifndef RFX_GROUP_LBC
+#define RFX_GROUP_LBC 0
+#endif
+constexpr int kGroupW = RFX_GROUP_W;
 
 struct GroupArgs {
     GemvArgs job[kMaxJobs];
-    int kind[kMaxJobs]; // 8 * fmt + q
-    int wg_begin[kMaxJobs + 1];
+    int kind[kMaxJobs];         // 8 * fmt + q
+    int wg_begin[kMaxJobs + 1]; // job j: workgroups [wg_begin[j], wg_begin[j + 1])
     int n;
 };
 
 template <bool FULL>
-__global__ __launch_bounds__(1024) void gemv_grouped_kernel(GroupArgs ga)
+__global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga)
 {
-    __shared__ float red[16 * 4 * 64];
+    __shared__ float red[kGroupW * 4 * 64];
     const int bid = blockIdx.x;
     int j = 0;
     while (j + 1 < ga.n && bid >= ga.wg_begin[j + 1])
@@ -345,7 +371,7 @@ __global__ __launch_bounds__(1024) void gemv_grouped_kernel(GroupArgs ga)
     const int local = bid - ga.wg_begin[j];
     const int p = local & (a.P - 1), g = local / a.P;
 #define RFX_JOB(F, QQ)                                                                                        \
-    case 8 * F + QQ: gemv_body<F, QQ, false, FULL>(a, p, g, red); break;
+    case 8 * F + QQ: gemv_body<F, QQ, false, FULL, RFX_GROUP_LBC>(a, p, g, red); break;
     switch (ga.kind[j]) {
         RFX_JOB(RFX_FP2, 1) RFX_JOB(RFX_FP2, 2) RFX_JOB(RFX_FP2, 3) RFX_JOB(RFX_FP2, 4)
         RFX_JOB(RFX_FP3, 1) RFX_JOB(RFX_FP3, 2) RFX_JOB(RFX_FP3, 3) RFX_JOB(RFX_FP3, 4)
@@ -411,24 +437,25 @@ int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
     return fail(RFX_E_INVAL, "unknown format");
 }
 
-// Grouped launches: every job runs W waves per workgroup (one block size
-// per launch); job j splits its S tiles over P workgroups, the smallest
-// power of two with P * W >= S (at most kGroupPMax).
-#ifndef RFX_GROUP_W
-#define RFX_GROUP_W 4
-#endif
-#ifndef RFX_GROUP_PMAX
-#define RFX_GROUP_PMAX 8
-#endif
-constexpr int kGroupW = RFX_GROUP_W;
-constexpr int kGroupPMax = RFX_GROUP_PMAX;
-
-int grouped_P(int S)
+// P per job (a power of two, at most 8, and no more than its tiles need).
+void grouped_shape(const rfx_gemv_job *jobs, int n, int *P)
 {
-    int P = 1;
-    while (P < kGroupPMax && P * kGroupW < S)
-        P <<= 1;
-    return P;
+    const int target_waves = 2048; // 1024 SIMDs x 2
+    for (int cap = 1;; cap <<= 1) {
+        long waves = 0;
+        bool can_split = false;
+        for (int j = 0; j < n; j++) {
+            const int G = (int)ceil_div(jobs[j].W.rows, kTileRows), S = (int)ceil_div(jobs[j].W.cols, kTileCols);
+            int p = 1;
+            while (p < cap && p * kGroupW < S)
+                p <<= 1;
+            P[j] = p;
+            can_split = can_split || (p == cap && p * kGroupW < S);
+            waves += (long)G * p * kGroupW;
+        }
+        if (waves >= target_waves || !can_split || cap >= 8)
+            return;
+    }
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -529,14 +556,16 @@ size_t rfx_gemv_grouped_workspace_bytes(const rfx_gemv_job *jobs, int n_jobs)
 {
     if (!jobs || n_jobs < 1 || n_jobs > kMaxJobs)
         return 0;
-    size_t total = 0;
     for (int j = 0; j < n_jobs; j++) {
         const rfx_qmat &W = jobs[j].W;
         if (!fmt_ok(W.fmt) || W.rows < 1 || W.cols < 32 || jobs[j].q < 1 || jobs[j].q > 4)
             return 0;
-        const int G = (int)ceil_div(W.rows, kTileRows), S = (int)ceil_div(W.cols, kTileCols);
-        total += align256(workspace_for(G, grouped_P(S), jobs[j].q));
     }
+    int P[kMaxJobs];
+    grouped_shape(jobs, n_jobs, P);
+    size_t total = 0;
+    for (int j = 0; j < n_jobs; j++)
+        total += align256(workspace_for((int)ceil_div(jobs[j].W.rows, kTileRows), P[j], jobs[j].q));
     return total;
 }
 
@@ -564,6 +593,8 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
             order[k] = order[k - 1];
             order[k - 1] = t;
         }
+    int Pj[kMaxJobs];
+    grouped_shape(jobs, n_jobs, Pj);
     GroupArgs ga{};
     ga.n = n_jobs;
     bool full = true;
@@ -582,7 +613,7 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         if ((st = check_act(jb.xq, jb.xs, jb.xsum, true)) || (st = check_ptr(jb.y, 4, "y")))
             return fail(st, "rfx_gemv_grouped: jobs[%d]: %s", j, rfx_last_error());
         const int G = (int)ceil_div(jb.W.rows, kTileRows), S = (int)ceil_div(jb.W.cols, kTileCols);
-        const int P = grouped_P(S);
+        const int P = Pj[j];
         GemvArgs &a = ga.job[jj];
         a.W = static_cast<const uint8_t *>(jb.W.data);
         a.N = jb.W.rows;
@@ -611,11 +642,11 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         if (st)
             return st;
     }
-    const hipStream_t st = (hipStream_t)stream;
+    const hipStream_t hs = (hipStream_t)stream;
     if (full)
-        hipLaunchKernelGGL(gemv_grouped_kernel<true>, dim3(wgs), dim3(64 * kGroupW), 0, st, ga);
+        hipLaunchKernelGGL(gemv_grouped_kernel<true>, dim3(wgs), dim3(64 * kGroupW), 0, hs, ga);
     else
-        hipLaunchKernelGGL(gemv_grouped_kernel<false>, dim3(wgs), dim3(64 * kGroupW), 0, st, ga);
+        hipLaunchKernelGGL(gemv_grouped_kernel<false>, dim3(wgs), dim3(64 * kGroupW), 0, hs, ga);
     return hip_status("grouped gemv launch");
 }
 

@@ -175,7 +175,8 @@ int rfx_gemv_q4(const rfx_qmat *W, const int8_t *xq, const float *xs, const int3
  * though not bit-identical to a lone rfx_gemv (its K split may differ).
  * Field rules are rfx_gemv's; output buffers must not overlap.
  * ws: zero-filled workspace of rfx_gemv_grouped_workspace_bytes(jobs,
- * n_jobs) bytes (NULL allowed when that is 0); left zeroed on return.
+ * n_jobs) bytes, 256-B aligned (NULL allowed when that is 0); left zeroed
+ * on return. Launches that share a workspace must not overlap.
  * Errors: RFX_E_INVAL (n_jobs outside 1..RFX_MAX_GEMV_JOBS, or a bad job:
  * the message names its index), RFX_E_ALIGN, RFX_E_WORKSPACE, RFX_E_HIP. */
 #define RFX_MAX_GEMV_JOBS 16
