@@ -84,12 +84,22 @@ constexpr uint32_t kPosHi = 0x0C080604u; // 4 6 8 12
 constexpr uint32_t kNegLo = 0xFDFEFF00u; // 0 -1 -2 -3
 constexpr uint32_t kNegHi = 0xF4F8FAFCu; // -4 -6 -8 -12
 
-__device__ __forceinline__ int fp4_expand(uint32_t nib_shifted_word, uint32_t sign_shifted_word)
+// A constant materialized in a VGPR. VOP3 instructions on gfx9 take no
+// literal and read at most one SGPR, so (x & a) | b with two constants
+// only becomes one v_and_or_b32 when one of them sits in a VGPR.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c)
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+__device__ __forceinline__ int fp4_expand(uint32_t nib_shifted_word, uint32_t sign_shifted_word, uint32_t k4)
 {
     const uint32_t idx = nib_shifted_word & 0x07070707u;
     const uint32_t pos = __builtin_amdgcn_perm(kPosHi, kPosLo, idx);
     const uint32_t neg = __builtin_amdgcn_perm(kNegHi, kNegLo, idx);
-    const uint32_t msel = (sign_shifted_word & 0x04040404u) | 0x03020100u;
+    const uint32_t msel = (sign_shifted_word & k4) | 0x03020100u; // one v_and_or_b32
     return (int)__builtin_amdgcn_perm(neg, pos, msel);
 }
 
@@ -97,10 +107,11 @@ __device__ __forceinline__ Sel8 sel_fp4(u32x4 c)
 {
     Sel8 s;
     const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t k4 = vgpr_const(0x04040404u);
 #pragma unroll
     for (int m = 0; m < 4; m++) {
-        s.v[2 * m] = fp4_expand(w[m], w[m] >> 1);
-        s.v[2 * m + 1] = fp4_expand(w[m] >> 4, w[m] >> 5);
+        s.v[2 * m] = fp4_expand(w[m], w[m] >> 1, k4);
+        s.v[2 * m + 1] = fp4_expand(w[m] >> 4, w[m] >> 5, k4);
     }
     return s;
 }

@@ -118,11 +118,26 @@ constexpr bool use_bcast()
     return Q >= 2;
 }
 
+// With BC the column dots run on the matrix core (v_mfma_i32_4x4x4_16b_i8,
+// activations broadcast from one 4-lane group) rather than as q DPP
+// v_dot4 chains per block: the VALU keeps only the decode and the fp32
+// scaling.
+#ifndef RFX_XMFMA
+#define RFX_XMFMA 1
+#endif
+#if RFX_XMFMA
+template <int Q>
+using XSlice = XTileM<Q>;
+#else
+template <int Q>
+using XSlice = XTile<Q>;
+#endif
+
 // A weight tile and, in broadcast mode, the matching activation slice.
 template <int FMT, int Q>
 struct WTile {
     TileRegs<FMT> w;
-    XTile<Q> x;
+    XSlice<Q> x;
 };
 
 template <int FMT, int Q, bool FULL, bool BC>
@@ -130,8 +145,13 @@ __device__ __forceinline__ WTile<FMT, Q> load_wtile(const uint8_t *gbase, int s,
                                                     int nb)
 {
     WTile<FMT, Q> t;
-    if (BC) // issued first: block 0 needs it together with the first chunk
+    if (BC) { // issued first: block 0 needs it together with the first chunk
+#if RFX_XMFMA
+        t.x = load_xtile_m<FMT, Q, FULL>(xc, s, nb, lane);
+#else
         t.x = load_xtile<FMT, Q, FULL>(xc, s, nb, lane);
+#endif
+    }
     t.w = load_tile<FMT>(gbase + (size_t)s * TileFmt<FMT>::bytes, lane);
     return t;
 }
@@ -140,14 +160,21 @@ template <int FMT, int Q, bool FULL, int... BI>
 __device__ __forceinline__ void store_dots_bcast(const WTile<FMT, Q> &t, int b0, int row, const GemvArgs &a,
                                                  std::integer_sequence<int, BI...>)
 {
-    // the dots run with every lane active (the DPP broadcast reads other
+    // the dots run with every lane active (the broadcasts read other
     // lanes); only the stores are predicated
     (
         [&] {
             int d[Q];
+#if RFX_XMFMA
+            const i32x4 dm = tile_block_dots_mfma<FMT, Q, BI>(t.w, t.x);
+#pragma unroll
+            for (int j = 0; j < Q; j++)
+                d[j] = dm[j];
+#else
 #pragma unroll
             for (int j = 0; j < Q; j++)
                 d[j] = tile_block_dot_bcast<FMT, Q, BI>(t.w, t.x, j);
+#endif
             if (b0 + BI < a.nb && row < a.N) {
 #pragma unroll
                 for (int j = 0; j < Q; j++)
@@ -163,9 +190,13 @@ __device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int 
 {
     const int b0 = s * 8;
     if (!DOTS) {
-        if (BC)
+        if (BC) {
+#if RFX_XMFMA
+            tile_blocks_mfma<FMT, Q, FULL>(t.w, t.x, b0, a.nb, acc);
+#else
             tile_blocks_bcast<FMT, Q, FULL>(t.w, t.x, b0, a.nb, acc);
-        else
+#endif
+        } else
             tile_blocks<FMT, Q, Q, FULL>(t.w, b0, a.nb, xc, acc);
         return;
     }

@@ -330,12 +330,10 @@ __device__ __forceinline__ void expand_block(const uint8_t *tile, int tr, int b,
 {
     if (FMT == RFX_FP4) {
         const u32x4 c = *reinterpret_cast<const u32x4 *>(tile + b * 1024 + tr * 16);
-        const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+        const Sel8 sv = sel_fp4(c);
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            v[2 * m] = (uint32_t)fp4_expand(w[m], w[m] >> 1);
-            v[2 * m + 1] = (uint32_t)fp4_expand(w[m] >> 4, w[m] >> 5);
-        }
+        for (int d = 0; d < 8; d++)
+            v[d] = (uint32_t)sv.v[d];
         const uint32_t e = tile[8192 + tr * 8 + b];
         sw = ldexpf(1.0f, (int)e - 128);
     } else {

@@ -205,5 +205,127 @@ __device__ __forceinline__ int tile_block_dot_bcast(const TileRegs<FMT> &t, cons
     return block_dot_bcast<FMT, Q, BI>(sel, xt, j);
 }
 
+// ------------------------------------------------------------------
+// Matrix-core variant for q >= 2: the q column dots of a block run as
+// v_mfma_i32_4x4x4_16b_i8 with the decoded weights as the B operand (lane
+// l = row l, four int8 weights per K step) and the activations as the A
+// operand. For that MFMA, output lane l, register v is the dot of B's lane
+// l with A's lane 4 * abid + v when cbsz = 4 broadcasts one 4-lane group to
+// all sixteen (measured on gfx950). So lane l holds the 16-byte chunk l / 4
+// of column l % 4's 256-byte tile slice, and K step s of block b takes its
+// activations from group 2b + s / 4, component s % 4: one vector load per
+// tile feeds every column, and each lane ends with its own row's q dots.
+// ------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int Q>
+struct XTileM {
+    u32x4 code;  // bytes [16 (l / 4), 16 (l / 4) + 16) of column min(l % 4, Q - 1)
+    float sx[Q]; // as XTile: lane n of a row holds column j's scale of block n & 7
+    int nsum[Q]; // as XTile: -off * (block sum), FP2 / FP3
+};
+
+template <int FMT, int Q, bool FULL>
+__device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int nb, int lane)
+{
+    XTileM<Q> xt;
+    const int n = lane & 15, chunk = lane >> 2;
+    const int bc = FULL ? s * 8 + (chunk >> 1) : min(s * 8 + (chunk >> 1), nb - 1);
+    const int bs = FULL ? s * 8 + (n & 7) : min(s * 8 + (n & 7), nb - 1);
+    // column offset of this lane as a sum of steps (a select between the
+    // offsets themselves would be turned into a lane-indexed private array)
+    uint32_t xo = xc.xoff[0];
+#pragma unroll
+    for (int j = 1; j < Q; j++)
+        xo += (lane & 3) >= j ? xc.xoff[j] - xc.xoff[j - 1] : 0u;
+    xt.code = *reinterpret_cast<const u32x4 *>(xc.xq + xo + (uint32_t)bc * 32u + (uint32_t)(chunk & 1) * 16u);
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
+    if (FMT != RFX_FP4) {
+        constexpr int off = FMT == RFX_FP2 ? 3 : 7;
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            xt.nsum[j] = -off * xc.xsum[xc.moff[j] + (uint32_t)bs];
+    }
+    return xt;
+}
+
+// One K step of block BI: four weights per lane against group 2 BI + S / 4.
+template <int BI, int S>
+__device__ __forceinline__ i32x4 mfma_step(i32x4 d, const u32x4 &x, int w)
+{
+    const uint32_t xa = (S & 3) == 0 ? x.x : (S & 3) == 1 ? x.y : (S & 3) == 2 ? x.z : x.w;
+    return __builtin_amdgcn_mfma_i32_4x4x4i8((int)xa, w, d, 4, 2 * BI + (S >> 2), 0);
+}
+
+// Exact block dots of block BI for the four column slots (slot j is
+// column j for j < Q). Two accumulation chains of four steps each, so
+// consecutive matrix ops do not wait on one another; FP2 / FP3 start the
+// first chain at -off * sum(x) (the codebook offset).
+template <int FMT, int Q, int BI>
+__device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt)
+{
+    i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+    if (FMT != RFX_FP4) {
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            d0[j] = bcast_row<BI>(xt.nsum[j]);
+    }
+    d0 = mfma_step<BI, 0>(d0, xt.code, sel.v[0]);
+    d1 = mfma_step<BI, 4>(d1, xt.code, sel.v[4]);
+    d0 = mfma_step<BI, 1>(d0, xt.code, sel.v[1]);
+    d1 = mfma_step<BI, 5>(d1, xt.code, sel.v[5]);
+    d0 = mfma_step<BI, 2>(d0, xt.code, sel.v[2]);
+    d1 = mfma_step<BI, 6>(d1, xt.code, sel.v[6]);
+    d0 = mfma_step<BI, 3>(d0, xt.code, sel.v[3]);
+    d1 = mfma_step<BI, 7>(d1, xt.code, sel.v[7]);
+    return d0 + d1;
+}
+
+template <int FMT, int Q, int BI, bool FULL>
+__device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
+                                                float (&acc)[Q])
+{
+    Sel8 sel;
+    float sw;
+    decode_block2<FMT, BI>(t, sel, sw);
+    if (!FULL)
+        sw = b0 + BI < nb ? sw : 0.0f;
+    const i32x4 d = block_dots_mfma<FMT, Q, BI>(sel, xt);
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+        acc[j] += (sw * sxb) * (float)d[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int Q, bool FULL, int... BI>
+__device__ __forceinline__ void tile_blocks_mfma_seq(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
+                                                     float (&acc)[Q], std::integer_sequence<int, BI...>)
+{
+    (tile_block_mfma<FMT, Q, BI, FULL>(t, xt, b0, nb, acc), ...);
+}
+
+// All 8 blocks of one tile on the matrix core. Every lane must be active
+// (the scale broadcasts read other lanes).
+template <int FMT, int Q, bool FULL>
+__device__ __forceinline__ void tile_blocks_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
+                                                 float (&acc)[Q])
+{
+    tile_blocks_mfma_seq<FMT, Q, FULL>(t, xt, b0, nb, acc, std::make_integer_sequence<int, 8>{});
+}
+
+// The per-block dots themselves (debug path), block BI.
+template <int FMT, int Q, int BI>
+__device__ __forceinline__ i32x4 tile_block_dots_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt)
+{
+    Sel8 sel;
+    float sw;
+    decode_block2<FMT, BI>(t, sel, sw);
+    return block_dots_mfma<FMT, Q, BI>(sel, xt);
+}
+
 } // namespace dev
 } // namespace rfx
