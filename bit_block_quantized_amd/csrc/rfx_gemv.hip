@@ -112,10 +112,13 @@ struct GemvArgs {
 // BC wins; at q = 1 the scalar path is as fast and needs fewer VGPRs. The
 // multi-tile loop (double-buffered tiles) always takes the scalar path to
 // stay within the register budget of a 1024-thread workgroup.
+#ifndef RFX_BC_MINQ
+#define RFX_BC_MINQ 2
+#endif
 template <int Q>
 constexpr bool use_bcast()
 {
-    return Q >= 2;
+    return Q >= RFX_BC_MINQ;
 }
 
 // With BC the column dots run on the matrix core (v_mfma_i32_4x4x4_16b_i8,
@@ -378,7 +381,7 @@ constexpr int kMaxJobs = RFX_MAX_GEMV_JOBS;
 #define RFX_GROUP_W 4
 #endif
 #ifndef RFX_GROUP_LBC
-#define RFX_GROUP_LBC 0
+#define RFX_GROUP_LBC 1
 #endif
 constexpr int kGroupW = RFX_GROUP_W;
 
