@@ -457,6 +457,10 @@ def main():
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("grouped"),
+                     "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy; for "
+                                     "this kernel the read counter gives 0.70 x the unique weight bytes "
+                                     "(L2 hits on long streams without counted DRAM reads; lone GEMV "
+                                     "launches read 1.01 x): profiles/gemv_grouped_7168_pmc.txt",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(ms * 1e3, 3)},
         "step_six_launches": {"us": round(ms_six * 1e3, 3),
