@@ -28,6 +28,7 @@
 #include "rfx_decode.h"
 #include "rfx_internal.h"
 #include "rfx_moe_ws.h"
+#include "rfx_xtile.h"
 
 using namespace rfx;
 using namespace rfx::dev;
@@ -403,11 +404,35 @@ __device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnA
     return c;
 }
 
-template <int FG, int FU, int NE>
-__device__ __forceinline__ void gateup_tile(const TileRegs<FG> &tg, const TileRegs<FU> &tu, int s, int nbH,
-                                            const XCols<NE> &xc, float (&ag)[NE], float (&au)[NE])
+// A gate tile, the matching up tile and, for two or more columns, the
+// activation slice for the matrix-core dots (one column keeps the
+// scalar-operand v_dot4 path).
+template <int FG, int NE>
+struct GUTile {
+    TileRegs<FG> g, u;
+    XTileM<NE> x;
+};
+
+template <int FG, int NE>
+__device__ __forceinline__ GUTile<FG, NE> load_gu(const uint8_t *gm, const uint8_t *um, int s, int nbH,
+                                                  const XCols<NE> &xc, int lane)
 {
-    tile_blocks2<FG, FU, NE, false>(tg, tu, s * 8, nbH, xc, ag, au);
+    GUTile<FG, NE> t;
+    if (NE >= 2)
+        t.x = load_xtile_m<FG, NE, false>(xc, s, nbH, lane);
+    t.g = load_tile<FG>(gm + (size_t)s * TileFmt<FG>::bytes, lane);
+    t.u = load_tile<FG>(um + (size_t)s * TileFmt<FG>::bytes, lane);
+    return t;
+}
+
+template <int FG, int NE>
+__device__ __forceinline__ void gateup_tile(const GUTile<FG, NE> &t, int s, int nbH, const XCols<NE> &xc,
+                                            float (&ag)[NE], float (&au)[NE])
+{
+    if (NE >= 2)
+        tile_blocks2_mfma<FG, NE, false>(t.g, t.u, t.x, s * 8, nbH, ag, au);
+    else
+        tile_blocks2<FG, FG, NE, false>(t.g, t.u, s * 8, nbH, xc, ag, au);
 }
 
 template <int FG, int NE>
@@ -443,6 +468,7 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
     }
     gm += (size_t)g * S * TileFmt<FG>::bytes;
     um += (size_t)g * S * TileFmt<FU>::bytes;
+    static_assert(FU == FG, "gate and up share a format");
     float ag[NE], au[NE];
 #pragma unroll
     for (int j = 0; j < NE; j++) {
@@ -454,21 +480,16 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
     // two buffers per stream used in turn: tile s + 1 in flight while s is
     // computed, with no register copies (which would wait for the loads)
     if (s_begin < s_end) {
-        TileRegs<FG> ga = load_tile<FG>(gm + (size_t)s_begin * TileFmt<FG>::bytes, lane), gb;
-        TileRegs<FU> ua = load_tile<FU>(um + (size_t)s_begin * TileFmt<FU>::bytes, lane), ub;
+        GUTile<FG, NE> ta = load_gu<FG, NE>(gm, um, s_begin, nbH, xc, lane), tb;
         for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end) {
-                gb = load_tile<FG>(gm + (size_t)(s + 1) * TileFmt<FG>::bytes, lane);
-                ub = load_tile<FU>(um + (size_t)(s + 1) * TileFmt<FU>::bytes, lane);
-            }
-            gateup_tile<FG, FU, NE>(ga, ua, s, nbH, xc, ag, au);
+            if (s + 1 < s_end)
+                tb = load_gu<FG, NE>(gm, um, s + 1, nbH, xc, lane);
+            gateup_tile<FG, NE>(ta, s, nbH, xc, ag, au);
             if (s + 1 >= s_end)
                 break;
-            if (s + 2 < s_end) {
-                ga = load_tile<FG>(gm + (size_t)(s + 2) * TileFmt<FG>::bytes, lane);
-                ua = load_tile<FU>(um + (size_t)(s + 2) * TileFmt<FU>::bytes, lane);
-            }
-            gateup_tile<FG, FU, NE>(gb, ub, s + 1, nbH, xc, ag, au);
+            if (s + 2 < s_end)
+                ta = load_gu<FG, NE>(gm, um, s + 2, nbH, xc, lane);
+            gateup_tile<FG, NE>(tb, s + 1, nbH, xc, ag, au);
         }
     }
     // fixed-order reduction over waves; red[w][m][j][lane], m = gate/up
@@ -541,10 +562,29 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
 // Expert down projection, shared expert and the weighted combine.
 // ------------------------------------------------------------------
 template <int FD, int NE>
-__device__ __forceinline__ void down_tile(const TileRegs<FD> &t, int s, int nbI, const XCols<NE> &xc,
+struct DTile {
+    TileRegs<FD> w;
+    XTileM<NE> x;
+};
+
+template <int FD, int NE>
+__device__ __forceinline__ DTile<FD, NE> load_dn(const uint8_t *dm, int s, int nbI, const XCols<NE> &xc, int lane)
+{
+    DTile<FD, NE> t;
+    if (NE >= 2)
+        t.x = load_xtile_m<FD, NE, false>(xc, s, nbI, lane);
+    t.w = load_tile<FD>(dm + (size_t)s * TileFmt<FD>::bytes, lane);
+    return t;
+}
+
+template <int FD, int NE>
+__device__ __forceinline__ void down_tile(const DTile<FD, NE> &t, int s, int nbI, const XCols<NE> &xc,
                                           float (&ao)[NE])
 {
-    tile_blocks<FD, NE, NE, false>(t, s * 8, nbI, xc, ao);
+    if (NE >= 2)
+        tile_blocks_mfma<FD, NE, false>(t.w, t.x, s * 8, nbI, ao);
+    else
+        tile_blocks<FD, NE, NE, false>(t.w, s * 8, nbI, xc, ao);
 }
 
 template <int FD, int NE>
@@ -577,15 +617,15 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
     const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
     const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
     if (s_begin < s_end) {
-        TileRegs<FD> da = load_tile<FD>(dm + (size_t)s_begin * TileFmt<FD>::bytes, lane), db;
+        DTile<FD, NE> da = load_dn<FD, NE>(dm, s_begin, nbI, xc, lane), db;
         for (int s = s_begin; s < s_end; s += 2) {
             if (s + 1 < s_end)
-                db = load_tile<FD>(dm + (size_t)(s + 1) * TileFmt<FD>::bytes, lane);
+                db = load_dn<FD, NE>(dm, s + 1, nbI, xc, lane);
             down_tile<FD, NE>(da, s, nbI, xc, ao);
             if (s + 1 >= s_end)
                 break;
             if (s + 2 < s_end)
-                da = load_tile<FD>(dm + (size_t)(s + 2) * TileFmt<FD>::bytes, lane);
+                da = load_dn<FD, NE>(dm, s + 2, nbI, xc, lane);
             down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
         }
     }

@@ -317,6 +317,50 @@ __device__ __forceinline__ void tile_blocks_mfma(const TileRegs<FMT> &t, const X
     tile_blocks_mfma_seq<FMT, Q, FULL>(t, xt, b0, nb, acc, std::make_integer_sequence<int, 8>{});
 }
 
+// A gate tile and the matching up tile (same format) against one
+// activation slice: block BI of both.
+template <int F, int Q, int BI, bool FULL>
+__device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const TileRegs<F> &tu, const XTileM<Q> &xt,
+                                                 int b0, int nb, float (&ag)[Q], float (&au)[Q])
+{
+    float sxb[Q];
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        sxb[j] = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+    Sel8 sel;
+    float sw;
+    decode_block2<F, BI>(tg, sel, sw);
+    if (!FULL)
+        sw = b0 + BI < nb ? sw : 0.0f;
+    i32x4 d = block_dots_mfma<F, Q, BI>(sel, xt);
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        ag[j] += (sw * sxb[j]) * (float)d[j];
+    decode_block2<F, BI>(tu, sel, sw);
+    if (!FULL)
+        sw = b0 + BI < nb ? sw : 0.0f;
+    d = block_dots_mfma<F, Q, BI>(sel, xt);
+#pragma unroll
+    for (int j = 0; j < Q; j++)
+        au[j] += (sw * sxb[j]) * (float)d[j];
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int F, int Q, bool FULL, int... BI>
+__device__ __forceinline__ void tile_blocks2_mfma_seq(const TileRegs<F> &tg, const TileRegs<F> &tu,
+                                                      const XTileM<Q> &xt, int b0, int nb, float (&ag)[Q],
+                                                      float (&au)[Q], std::integer_sequence<int, BI...>)
+{
+    (tile_block2_mfma<F, Q, BI, FULL>(tg, tu, xt, b0, nb, ag, au), ...);
+}
+
+template <int F, int Q, bool FULL>
+__device__ __forceinline__ void tile_blocks2_mfma(const TileRegs<F> &tg, const TileRegs<F> &tu, const XTileM<Q> &xt,
+                                                  int b0, int nb, float (&ag)[Q], float (&au)[Q])
+{
+    tile_blocks2_mfma_seq<F, Q, FULL>(tg, tu, xt, b0, nb, ag, au, std::make_integer_sequence<int, 8>{});
+}
+
 // The per-block dots themselves (debug path), block BI.
 template <int FMT, int Q, int BI>
 __device__ __forceinline__ i32x4 tile_block_dots_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt)
