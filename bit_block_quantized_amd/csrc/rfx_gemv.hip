@@ -106,41 +106,25 @@ struct GemvArgs {
 };
 
 // Activations per block come either from SGPRs (scalar loads per block) or,
-// with BC, from a per-tile VGPR copy broadcast by DPP (vector loads issued
-// with the weight tile). Scalar loads complete out of order, so each block
-// waits for all of its activation loads: at q >= 2 that wait dominates and
+// with BC, from a per-tile VGPR slice loaded together with the weight tile,
+// and the column dots then run on the matrix core (v_mfma_i32_4x4x4_16b_i8
+// with the activations broadcast from one 4-lane group). Scalar loads
+// complete out of order, so each block waits for all of its activation
+// loads: at q >= 2 that wait and the q v_dot4 chains per block dominate and
 // BC wins; at q = 1 the scalar path is as fast and needs fewer VGPRs. The
-// multi-tile loop (double-buffered tiles) always takes the scalar path to
-// stay within the register budget of a 1024-thread workgroup.
-#ifndef RFX_BC_MINQ
-#define RFX_BC_MINQ 2
-#endif
+// multi-tile loop of a lone GEMV (double-buffered tiles) takes the scalar
+// path to stay within the register budget of a 1024-thread workgroup.
 template <int Q>
 constexpr bool use_bcast()
 {
-    return Q >= RFX_BC_MINQ;
+    return Q >= 2;
 }
-
-// With BC the column dots run on the matrix core (v_mfma_i32_4x4x4_16b_i8,
-// activations broadcast from one 4-lane group) rather than as q DPP
-// v_dot4 chains per block: the VALU keeps only the decode and the fp32
-// scaling.
-#ifndef RFX_XMFMA
-#define RFX_XMFMA 1
-#endif
-#if RFX_XMFMA
-template <int Q>
-using XSlice = XTileM<Q>;
-#else
-template <int Q>
-using XSlice = XTile<Q>;
-#endif
 
 // A weight tile and, in broadcast mode, the matching activation slice.
 template <int FMT, int Q>
 struct WTile {
     TileRegs<FMT> w;
-    XSlice<Q> x;
+    XTileM<Q> x;
 };
 
 template <int FMT, int Q, bool FULL, bool BC>
@@ -148,13 +132,8 @@ __device__ __forceinline__ WTile<FMT, Q> load_wtile(const uint8_t *gbase, int s,
                                                     int nb)
 {
     WTile<FMT, Q> t;
-    if (BC) { // issued first: block 0 needs it together with the first chunk
-#if RFX_XMFMA
+    if (BC) // issued first: block 0 needs it together with the first chunk
         t.x = load_xtile_m<FMT, Q, FULL>(xc, s, nb, lane);
-#else
-        t.x = load_xtile<FMT, Q, FULL>(xc, s, nb, lane);
-#endif
-    }
     t.w = load_tile<FMT>(gbase + (size_t)s * TileFmt<FMT>::bytes, lane);
     return t;
 }
@@ -168,16 +147,10 @@ __device__ __forceinline__ void store_dots_bcast(const WTile<FMT, Q> &t, int b0,
     (
         [&] {
             int d[Q];
-#if RFX_XMFMA
             const i32x4 dm = tile_block_dots_mfma<FMT, Q, BI>(t.w, t.x);
 #pragma unroll
             for (int j = 0; j < Q; j++)
                 d[j] = dm[j];
-#else
-#pragma unroll
-            for (int j = 0; j < Q; j++)
-                d[j] = tile_block_dot_bcast<FMT, Q, BI>(t.w, t.x, j);
-#endif
             if (b0 + BI < a.nb && row < a.N) {
 #pragma unroll
                 for (int j = 0; j < Q; j++)
@@ -193,13 +166,9 @@ __device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int 
 {
     const int b0 = s * 8;
     if (!DOTS) {
-        if (BC) {
-#if RFX_XMFMA
+        if (BC)
             tile_blocks_mfma<FMT, Q, FULL>(t.w, t.x, b0, a.nb, acc);
-#else
-            tile_blocks_bcast<FMT, Q, FULL>(t.w, t.x, b0, a.nb, acc);
-#endif
-        } else
+        else
             tile_blocks<FMT, Q, Q, FULL>(t.w, b0, a.nb, xc, acc);
         return;
     }
@@ -377,13 +346,7 @@ constexpr int kMaxJobs = RFX_MAX_GEMV_JOBS;
 // waves per SIMD: a launch of several large matrices runs one workgroup
 // per row group (no exchange at all, every workgroup resident at once); a
 // lone small matrix still fills the chip.
-#ifndef RFX_GROUP_W
-#define RFX_GROUP_W 4
-#endif
-#ifndef RFX_GROUP_LBC
-#define RFX_GROUP_LBC 1
-#endif
-constexpr int kGroupW = RFX_GROUP_W;
+constexpr int kGroupW = 4;
 
 struct GroupArgs {
     GemvArgs job[kMaxJobs];
@@ -405,7 +368,7 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
     const int local = bid - ga.wg_begin[j];
     const int p = local & (a.P - 1), g = local / a.P;
 #define RFX_JOB(F, QQ)                                                                                        \
-    case 8 * F + QQ: gemv_body<F, QQ, false, FULL, RFX_GROUP_LBC>(a, p, g, red); break;
+    case 8 * F + QQ: gemv_body<F, QQ, false, FULL, true>(a, p, g, red); break;
     switch (ga.kind[j]) {
         RFX_JOB(RFX_FP2, 1) RFX_JOB(RFX_FP2, 2) RFX_JOB(RFX_FP2, 3) RFX_JOB(RFX_FP2, 4)
         RFX_JOB(RFX_FP3, 1) RFX_JOB(RFX_FP3, 2) RFX_JOB(RFX_FP3, 3) RFX_JOB(RFX_FP3, 4)

@@ -1,21 +1,18 @@
-// Activation tiles held in VGPRs and broadcast to the wave with DPP (gfx950).
+// Activation tiles held in VGPRs and the matrix-core block dots (gfx950).
 //
 // Pages cited (title, site):
 //   [HM] "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
 //        (hellomarvisaitoday.com), paragraphs numbered from the top.
 //
 // [HM] para 3: one decoded weight block feeds integer dot products for every
-// activation column. Every lane of a wave (one output row each) needs the
-// same 32 activation bytes per block. Scalar loads give them as SGPR
-// operands, but scalar loads complete out of order, so every use waits for
-// all of them: at q = 4 that is several full memory round trips per block.
-// Here the activation slice of a whole tile (q columns x 256 bytes, plus the
-// eight block scales and sums per column) is read with ordinary vector loads,
-// issued together with the weight tile, and each of the four 16-lane rows of
-// the wave holds a full copy. A v_dot4c_i32_i8 with the DPP control
-// row_newbcast:n reads the activation dword held by lane n of its row, so
-// the broadcast costs no instruction. Vector loads complete in order, so
-// block b waits only for its own data.
+// activation column. With q >= 2 columns those dots run on the matrix core:
+// the activation slice of a whole tile (q columns x 256 bytes, plus the
+// eight block scales and sums per column) is read with ordinary vector loads
+// issued together with the weight tile (vector loads complete in order, so
+// block b waits only for its own data; scalar loads complete out of order
+// and every use waits for all of them), and a v_mfma_i32_4x4x4_16b_i8 per
+// K step takes the decoded weights of each lane's row as one operand and
+// the activations, broadcast from one 4-lane group, as the other.
 #pragma once
 
 #include "rfx_decode.h"
@@ -24,41 +21,6 @@
 
 namespace rfx {
 namespace dev {
-
-// Per-lane part of one tile's activations. Lane n of a row (n = lane & 15)
-// holds bytes [16n, 16n + 16) of column j's 256-byte slice in code[j], the
-// fp32 scale of block n & 7 in sx[j] and, for FP2/FP3, -off * (block sum)
-// in nsum[j] (off = 3 or 7: the codebook offset folded out of the dot).
-template <int Q>
-struct XTile {
-    u32x4 code[Q];
-    float sx[Q];
-    int nsum[Q];
-};
-
-template <int FMT, int Q, bool FULL>
-__device__ __forceinline__ XTile<Q> load_xtile(const XCols<Q> &xc, int s, int nb, int lane)
-{
-    XTile<Q> xt;
-    const int n = lane & 15;
-    // in a tile that ends past K the missing blocks read a valid block (the
-    // last one); their weight scale is forced to zero by the caller
-    const int bc = FULL ? s * 8 + (n >> 1) : min(s * 8 + (n >> 1), nb - 1);
-    const int bs = FULL ? s * 8 + (n & 7) : min(s * 8 + (n & 7), nb - 1);
-#pragma unroll
-    for (int j = 0; j < Q; j++)
-        xt.code[j] = *reinterpret_cast<const u32x4 *>(xc.xq + xc.xoff[j] + (uint32_t)bc * 32u + (uint32_t)(n & 1) * 16u);
-#pragma unroll
-    for (int j = 0; j < Q; j++)
-        xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
-    if (FMT != RFX_FP4) {
-        constexpr int off = FMT == RFX_FP2 ? 3 : 7;
-#pragma unroll
-        for (int j = 0; j < Q; j++)
-            xt.nsum[j] = -off * xc.xsum[xc.moff[j] + (uint32_t)bs];
-    }
-    return xt;
-}
 
 // Selector bytes equal to 2c (twice the code) for FP2 / FP3, so that with
 // v = 2c - off the block dot is sum(2c * x) + (-off * sum(x)): the second
@@ -117,92 +79,12 @@ __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel,
     }
 }
 
-// d += sum over the block's 8 activation dwords of dot4(x, sel[i]); dword i
-// of block BI is component i & 3 of x, held by lane 2 * BI + (i >> 2) of
-// each row. Must run with every lane of the wave active: a DPP read of an
-// inactive lane does not return that lane's register. The compiler sees
-// neither the DPP nor the dot inside the asm, so the asm carries its own
-// wait states: the leading s_nop covers the two a DPP read needs after a
-// VALU write of its source, the trailing one the three that must pass
-// before another instruction reads a v_dot4c result (measured on gfx950:
-// with fewer, the reader gets the accumulator's old value; chained dots on
-// the same accumulator are not affected).
-template <int BI>
-__device__ __forceinline__ int dot_block_bcast(int d, u32x4 x, const Sel8 &s)
-{
-    asm("s_nop 1\n\t"
-        "v_dot4c_i32_i8_dpp %0, %1, %5 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %6 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %3, %7 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %4, %8 row_newbcast:%13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %1, %9 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %2, %10 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %3, %11 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot4c_i32_i8_dpp %0, %4, %12 row_newbcast:%14 row_mask:0xf bank_mask:0xf\n\t"
-        "s_nop 2"
-        : "+v"(d)
-        : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w), "v"(s.v[0]), "v"(s.v[1]), "v"(s.v[2]), "v"(s.v[3]),
-          "v"(s.v[4]), "v"(s.v[5]), "v"(s.v[6]), "v"(s.v[7]), "n"(2 * BI), "n"(2 * BI + 1));
-    return d;
-}
-
 // Broadcast lane N of each 16-lane row (a DPP move the compiler folds into
 // the consuming VALU instruction where it can).
 template <int N>
 __device__ __forceinline__ int bcast_row(int v)
 {
     return __builtin_amdgcn_update_dpp(0, v, 0x150 + N, 0xF, 0xF, true);
-}
-
-// Exact block dot D for column j of block BI.
-template <int FMT, int Q, int BI>
-__device__ __forceinline__ int block_dot_bcast(const Sel8 &sel, const XTile<Q> &xt, int j)
-{
-    const int d0 = FMT == RFX_FP4 ? 0 : bcast_row<BI>(xt.nsum[j]);
-    return dot_block_bcast<BI>(d0, xt.code[j], sel);
-}
-
-template <int FMT, int Q, int BI, bool FULL>
-__device__ __forceinline__ void tile_block_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
-                                                 float (&acc)[Q])
-{
-    Sel8 sel;
-    float sw;
-    decode_block2<FMT, BI>(t, sel, sw);
-    if (!FULL)
-        sw = b0 + BI < nb ? sw : 0.0f;
-#pragma unroll
-    for (int j = 0; j < Q; j++) {
-        const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
-        acc[j] += (sw * sxb) * (float)block_dot_bcast<FMT, Q, BI>(sel, xt, j);
-    }
-    // keep each block's work after its own chunk wait
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int FMT, int Q, bool FULL, int... BI>
-__device__ __forceinline__ void tile_blocks_bcast_seq(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
-                                                      float (&acc)[Q], std::integer_sequence<int, BI...>)
-{
-    (tile_block_bcast<FMT, Q, BI, FULL>(t, xt, b0, nb, acc), ...);
-}
-
-// All 8 blocks of one tile, activations broadcast from the lanes.
-template <int FMT, int Q, bool FULL>
-__device__ __forceinline__ void tile_blocks_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int b0, int nb,
-                                                  float (&acc)[Q])
-{
-    tile_blocks_bcast_seq<FMT, Q, FULL>(t, xt, b0, nb, acc, std::make_integer_sequence<int, 8>{});
-}
-
-// The per-block dots themselves (debug path), block BI, column j.
-template <int FMT, int Q, int BI>
-__device__ __forceinline__ int tile_block_dot_bcast(const TileRegs<FMT> &t, const XTile<Q> &xt, int j)
-{
-    Sel8 sel;
-    float sw;
-    decode_block2<FMT, BI>(t, sel, sw);
-    return block_dot_bcast<FMT, Q, BI>(sel, xt, j);
 }
 
 // ------------------------------------------------------------------
@@ -218,11 +100,17 @@ __device__ __forceinline__ int tile_block_dot_bcast(const TileRegs<FMT> &t, cons
 // ------------------------------------------------------------------
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Per-lane part of one tile's activations: code holds bytes
+// [16 (l / 4), 16 (l / 4) + 16) of column min(l % 4, Q - 1)'s 256-byte
+// slice; lane n of each 16-lane row (n = l & 15) holds column j's fp32
+// scale of block n & 7 in sx[j] and, for FP2/FP3, -off * (block sum) in
+// nsum[j] (off = 3 or 7, the codebook offset folded out of the dot); the
+// block's values reach every lane by DPP row broadcast.
 template <int Q>
 struct XTileM {
-    u32x4 code;  // bytes [16 (l / 4), 16 (l / 4) + 16) of column min(l % 4, Q - 1)
-    float sx[Q]; // as XTile: lane n of a row holds column j's scale of block n & 7
-    int nsum[Q]; // as XTile: -off * (block sum), FP2 / FP3
+    u32x4 code;
+    float sx[Q];
+    int nsum[Q];
 };
 
 template <int FMT, int Q, bool FULL>
