@@ -16,9 +16,13 @@
 // Mapping on gfx950:
 //   - one lane = one output row; a wave covers 64 rows of a 64 x 256 tile
 //     and every 128-bit load of a wave reads 1 KiB of contiguous memory;
-//   - the activation block is the same for all 64 lanes, so it is read with
-//     scalar loads into SGPRs and used directly as the SGPR operand of
-//     v_dot4_i32_i8: no LDS traffic and no cross-lane reduction per row;
+//   - q = 1: the activation block is the same for all 64 lanes, so it is
+//     read with scalar loads into SGPRs and used directly as the SGPR
+//     operand of v_dot4_i32_i8: no LDS traffic, no cross-lane reduction;
+//   - q >= 2: the q column dots of a block run on the matrix core
+//     (v_mfma_i32_4x4x4_16b_i8, weights of the lane's row against the
+//     activations broadcast from one 4-lane group), fed by one vector load
+//     of the tile's activation slice;
 //   - FP2/FP3 codebooks are affine in the code (v = 2c - 3, v = 2c - 7), so
 //     the selector bytes go straight into v_dot4 and the offset is folded in
 //     once per block with the precomputed activation block sum; FP4 (E2M1,
@@ -31,7 +35,9 @@
 //     one two-term fp32 sum, so the result does not depend on arrival order
 //     (deterministic, no float atomics, no counters, no L2 write-back);
 //   - each wave keeps the next tile's loads in flight while it decodes the
-//     current one.
+//     current one;
+//   - several independent GEMVs can share one launch (gemv_grouped_kernel),
+//     so one matrix's last workgroups overlap the next one's weight stream.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
