@@ -33,6 +33,10 @@ import numpy as np
 
 FP2, FP3, FP4 = 2, 3, 4
 FORMATS = (FP2, FP3, FP4)
+# Variant with a scale and a minimum per block (weight = s * c + m, 12 B):
+# the pages let a block carry a second small value; this one is a reading.
+FP2M = 12
+VARIANT_FORMATS = (FP2M,)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "liboracle.so")
@@ -69,6 +73,8 @@ def lib():
     L.orc_pack_codes.restype = None
     L.orc_block_scale.argtypes = [ctypes.c_int, _u8p]
     L.orc_block_scale.restype = ctypes.c_double
+    L.orc_block_min.argtypes = [ctypes.c_int, _u8p]
+    L.orc_block_min.restype = ctypes.c_double
     L.orc_dequantize_block.argtypes = [ctypes.c_int, _u8p, _f64p]
     L.orc_dequantize_block.restype = None
     L.orc_quantize_block.argtypes = [ctypes.c_int, _f32p, _u8p]
@@ -147,6 +153,12 @@ def block_scale(fmt: int, blk) -> float:
     return float(lib().orc_block_scale(fmt, _p(blk, _u8p)))
 
 
+def block_min(fmt: int, blk) -> float:
+    """FP2M's fp16 minimum (0 for the symmetric formats)."""
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    return float(lib().orc_block_min(fmt, _p(blk, _u8p)))
+
+
 def dequantize_block(fmt: int, blk) -> np.ndarray:
     blk = np.ascontiguousarray(blk, dtype=np.uint8)
     out = np.zeros(32, np.float64)
@@ -199,7 +211,8 @@ def act_sums(xq) -> np.ndarray:
 # ----------------------------------------------------------------- gemv
 
 def gemv(fmt: int, blocks, xq, xs, want_dots: bool = False):
-    """y[j][n] = sum_b S[n,b] * s[j,b] * D[j,n,b] in fp64 (exact int dots).
+    """y[j][n] = sum_b S[n,b] * s[j,b] * D[j,n,b] in fp64 (exact int dots);
+    FP2M adds s[j,b] * M[n,b] * X[j,b] (X the activation block sum).
 
     blocks: uint8 [N][K/32][bb]; xq int8 [Q][K]; xs fp32 [Q][K/32].
     Returns fp64 [Q][N] (and int32 dots [Q][N][K/32] when asked)."""

@@ -20,8 +20,8 @@
  *   [KK]  the kaikai365.com post on DeepSeek V4 Flash on Strix Halo, by
  *         section heading.
  *
- * What the pages fix: a block is 32 weights stored as packed low-bit codes
- * plus one or two small scales; FP2 takes 10 bytes per block (2.50 bits per
+ * What the pages fix: a block holds 32 weights as packed codes of a few bits
+ * each, with a single small scale or a pair of them; FP2 takes 10 bytes per block (2.50 bits per
  * weight), FP3 3.50 bits per weight, FP4 4.25 bits per weight ([HM] para 2;
  * [KK] section on the mixed-precision assignment). Decoding expands a small
  * codebook and feeds integer dot products ([HM] para 3).
@@ -36,6 +36,12 @@
  *   FP2: 8 code bytes + fp16 scale (little-endian)       = 10 bytes
  *   FP3: 12 code bytes + fp16 scale                       = 14 bytes
  *   FP4: 16 code bytes + one e8m0 exponent byte           = 17 bytes
+ *
+ * Variant with two small values per block (the page's format overview lets a
+ * block carry a second small value beside its scale; this variant is a
+ * reading, not one of the three named formats):
+ *   FP2M: the FP2 code bytes + fp16 scale s + fp16 minimum m = 12 bytes
+ *         (3.0 bits per weight); weight = s * c + m, c in 0..3.
  */
 #include <math.h>
 #include <stdint.h>
@@ -45,6 +51,7 @@
 #define ORC_FP2 2
 #define ORC_FP3 3
 #define ORC_FP4 4
+#define ORC_FP2M 12
 
 #define ORC_OK 0
 #define ORC_E_INVAL (-1)
@@ -57,6 +64,7 @@ int orc_block_bytes(int fmt)
     case ORC_FP2: return 10;
     case ORC_FP3: return 14;
     case ORC_FP4: return 17;
+    case ORC_FP2M: return 12; /* Reading: 8 code bytes + two fp16 values */
     }
     return ORC_E_INVAL;
 }
@@ -67,6 +75,7 @@ int orc_code_bytes(int fmt)
     case ORC_FP2: return 8;
     case ORC_FP3: return 12;
     case ORC_FP4: return 16;
+    case ORC_FP2M: return 8;
     }
     return ORC_E_INVAL;
 }
@@ -139,7 +148,9 @@ uint16_t orc_f32_to_f16(float f)
  * FP3: codes 0..7 -> -7, -5, ..., +7.
  * FP4: code = sign<<3 | m, m the OCP E2M1 magnitude pattern; value =
  *      2 x E2M1 so it is an integer: m -> 0,1,2,3,4,6,8,12. Code 8 (-0)
- *      decodes to 0 and the encoder never emits it. */
+ *      decodes to 0 and the encoder never emits it.
+ * FP2M: the integer part is the code itself, 0..3; the block's minimum is
+ *      added after the scale (weight = s * c + m). */
 int orc_codebook(int fmt, int code)
 {
     static const int fp4_mag[8] = {0, 1, 2, 3, 4, 6, 8, 12};
@@ -147,13 +158,14 @@ int orc_codebook(int fmt, int code)
     case ORC_FP2: return 2 * code - 3;
     case ORC_FP3: return 2 * code - 7;
     case ORC_FP4: return (code & 8) ? -fp4_mag[code & 7] : fp4_mag[code & 7];
+    case ORC_FP2M: return code;
     }
     return 0;
 }
 
 static int n_codes(int fmt)
 {
-    return fmt == ORC_FP2 ? 4 : fmt == ORC_FP3 ? 8 : 16;
+    return fmt == ORC_FP2 || fmt == ORC_FP2M ? 4 : fmt == ORC_FP3 ? 8 : 16;
 }
 
 /* Nearest codebook value to t, by brute force over every code.
@@ -163,7 +175,8 @@ static int n_codes(int fmt)
  * point would round for tiny t and turn near-ties into false ties.)
  * Reading (ties): FP2/FP3 prefer the larger magnitude, and between equal
  * magnitudes (t = 0) the positive one; FP4 prefers the even E2M1 mantissa
- * (round-half-even on the E2M1 grid), saturating at +-12 by distance. */
+ * (round-half-even on the E2M1 grid), saturating at +-12 by distance;
+ * FP2M (values 0..3, all non-negative) prefers the larger value. */
 int orc_nearest_code(int fmt, double t)
 {
     int best = -1;
@@ -195,8 +208,8 @@ int orc_nearest_code(int fmt, double t)
 /* Bit layout inside a block (Reading: the pages do not give one).    */
 /* ------------------------------------------------------------------ */
 /* Code words are little-endian 32-bit words.
- * FP2: word m (0..1) holds weights 16m..16m+15; weight 16m + 4i + j
- *      (i, j in 0..3) occupies bits [8j + 2i, 8j + 2i + 2).
+ * FP2 (and FP2M): word m (0..1) holds weights 16m..16m+15; weight
+ *      16m + 4i + j (i, j in 0..3) occupies bits [8j + 2i, 8j + 2i + 2).
  * FP3: words 0..1 hold the low two bits of every code exactly as FP2;
  *      word 2 holds the high bit, weight 4i + j (i in 0..7, j in 0..3) at
  *      bit 8j + i.
@@ -219,7 +232,7 @@ static void wr32(uint8_t *p, uint32_t v)
 void orc_unpack_codes(int fmt, const uint8_t *blk, int *codes)
 {
     for (int t = 0; t < 32; t++) {
-        if (fmt == ORC_FP2) {
+        if (fmt == ORC_FP2 || fmt == ORC_FP2M) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             codes[t] = (int)((rd32(blk + 4 * m) >> (8 * j + 2 * i)) & 3u);
         } else if (fmt == ORC_FP3) {
@@ -239,7 +252,7 @@ void orc_pack_codes(int fmt, const int *codes, uint8_t *blk)
 {
     uint32_t w[4] = {0, 0, 0, 0};
     for (int t = 0; t < 32; t++) {
-        if (fmt == ORC_FP2) {
+        if (fmt == ORC_FP2 || fmt == ORC_FP2M) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             w[m] |= (uint32_t)(codes[t] & 3) << (8 * j + 2 * i);
         } else if (fmt == ORC_FP3) {
@@ -268,13 +281,23 @@ double orc_block_scale(int fmt, const uint8_t *blk)
     return orc_f16_to_f64((uint16_t)(blk[cb] | (blk[cb + 1] << 8)));
 }
 
+/* The value added after the scale: FP2M's fp16 minimum (after the fp16
+ * scale), zero for the symmetric formats. */
+double orc_block_min(int fmt, const uint8_t *blk)
+{
+    int cb = orc_code_bytes(fmt);
+    if (fmt != ORC_FP2M)
+        return 0.0;
+    return orc_f16_to_f64((uint16_t)(blk[cb + 2] | (blk[cb + 3] << 8)));
+}
+
 void orc_dequantize_block(int fmt, const uint8_t *blk, double *w)
 {
     int codes[32];
     orc_unpack_codes(fmt, blk, codes);
-    double s = orc_block_scale(fmt, blk);
+    double s = orc_block_scale(fmt, blk), m = orc_block_min(fmt, blk);
     for (int t = 0; t < 32; t++)
-        w[t] = s * (double)orc_codebook(fmt, codes[t]);
+        w[t] = s * (double)orc_codebook(fmt, codes[t]) + m;
 }
 
 /* ------------------------------------------------------------------ */
@@ -296,6 +319,39 @@ int orc_quantize_block(int fmt, const float *w, uint8_t *blk)
             amax = a;
     }
     memset(blk, 0, (size_t)orc_block_bytes(fmt));
+    if (fmt == ORC_FP2M) {
+        /* Reading (asymmetric variant): m = fp16(min w) (round to nearest
+         * even); s = fp16((max w - m) / 3) with the subtraction and the
+         * division in fp32 (a negative span, when m rounded above every
+         * weight, counts as 0); code = the value of 0..3 nearest to
+         * (w - m) / s in fp32, ties to the larger; s = 0 gives code 0. */
+        float lo = w[0], hi = w[0];
+        for (int t = 1; t < 32; t++) {
+            if (w[t] < lo)
+                lo = w[t];
+            if (w[t] > hi)
+                hi = w[t];
+        }
+        uint16_t m16 = orc_f32_to_f16(lo);
+        if ((m16 & 0x7fff) == 0x7c00)
+            return ORC_E_RANGE;
+        float m = (float)orc_f16_to_f64(m16);
+        float span = hi - m;
+        if (span < 0.0f)
+            span = 0.0f;
+        uint16_t s16 = orc_f32_to_f16(span / 3.0f);
+        if ((s16 & 0x7fff) == 0x7c00)
+            return ORC_E_RANGE;
+        float s = (float)orc_f16_to_f64(s16);
+        for (int t = 0; t < 32; t++)
+            codes[t] = s == 0.0f ? 0 : orc_nearest_code(fmt, (double)((w[t] - m) / s));
+        orc_pack_codes(fmt, codes, blk);
+        blk[cb] = (uint8_t)(s16 & 0xff);
+        blk[cb + 1] = (uint8_t)(s16 >> 8);
+        blk[cb + 2] = (uint8_t)(m16 & 0xff);
+        blk[cb + 3] = (uint8_t)(m16 >> 8);
+        return ORC_OK;
+    }
     if (fmt == ORC_FP4) {
         /* OCP MX shared exponent: floor(log2 amax) - emax(E2M1 = 2), biased
          * by 127, clamped to [0, 254]; amax = 0 gives E = 0. */
@@ -396,6 +452,8 @@ int orc_quantize_act(const float *x, int64_t n, int8_t *q, float *s)
 /* ------------------------------------------------------------------ */
 /* Per block: D = sum_t codebook(c_t) * q_t, an exact integer; then
  * y[j][n] = sum_b S[n][b] * s[j][b] * D[j][n][b] in fp64, b ascending.
+ * FP2M adds its minimum: sum_t (S c_t + M) s q_t = s (S D + M X) with X the
+ * block's activation sum, also an exact integer.
  * Each decoded weight serves every one of the Q columns ([AIN] section on
  * the optimization trio: decode once, apply to all verification columns);
  * the result is the same as Q separate one-column products.
@@ -415,15 +473,20 @@ int orc_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *xq, 
             const uint8_t *blk = W + (n * nb + b) * bb;
             int codes[32];
             orc_unpack_codes(fmt, blk, codes);
-            double S = orc_block_scale(fmt, blk);
+            double S = orc_block_scale(fmt, blk), M = orc_block_min(fmt, blk);
             for (int j = 0; j < Q; j++) {
                 const int8_t *xb = xq + (int64_t)j * K + 32 * b;
-                int64_t D = 0;
-                for (int t = 0; t < 32; t++)
+                int64_t D = 0, X = 0;
+                for (int t = 0; t < 32; t++) {
                     D += (int64_t)orc_codebook(fmt, codes[t]) * (int64_t)xb[t];
+                    X += (int64_t)xb[t];
+                }
                 if (dots)
                     dots[((int64_t)j * N + n) * nb + b] = (int32_t)D;
-                y[(int64_t)j * N + n] += S * (double)xs[(int64_t)j * nb + b] * (double)D;
+                if (fmt == ORC_FP2M)
+                    y[(int64_t)j * N + n] += (double)xs[(int64_t)j * nb + b] * (S * (double)D + M * (double)X);
+                else
+                    y[(int64_t)j * N + n] += S * (double)xs[(int64_t)j * nb + b] * (double)D;
             }
         }
     }

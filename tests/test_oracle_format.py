@@ -316,3 +316,109 @@ def test_matrix_is_rowwise_blocks():
         for r in range(5):
             for b in range(3):
                 assert bytes(M[r, b]) == bytes(O.quantize_block(fmt, W[r, 32 * b:32 * b + 32]))
+
+
+# ------------------------------------------------- FP2M (scale + minimum)
+# The variant with two small values per block: weight = s * c + m, c 0..3.
+
+FP2M = O.FP2M
+
+
+def test_fp2m_sizes_and_codebook():
+    assert O.block_bytes(FP2M) == 12 and O.code_bytes(FP2M) == 8
+    assert [O.codebook(FP2M, c) for c in range(4)] == [0, 1, 2, 3]
+
+
+def test_fp2m_nearest_code_argmin_and_ties():
+    rng = np.random.default_rng(7)
+    for t in rng.uniform(-3, 6, 4000):
+        c = O.nearest_code(FP2M, float(t))
+        assert all(abs(t - c) <= abs(t - v) for v in range(4))
+    for t, want in ((0.5, 1), (1.5, 2), (2.5, 3), (-0.7, 0), (9.0, 3), (0.0, 0), (-0.0, 0)):
+        assert O.nearest_code(FP2M, t) == want
+
+
+def test_fp2m_bit_layout_is_fp2s():
+    rng = np.random.default_rng(8)
+    for _ in range(50):
+        codes = rng.integers(0, 4, 32)
+        assert bytes(O.pack_codes(FP2M, codes)) == bytes(O.pack_codes(2, codes))
+        blk = np.zeros(12, np.uint8)
+        blk[:8] = O.pack_codes(FP2M, codes)
+        assert np.array_equal(O.unpack_codes(FP2M, blk), codes)
+
+
+def test_fp2m_scale_and_min_from_the_block_extremes():
+    """m = fp16(min w) and s = fp16(max(max w - m, 0) / 3), recomputed here
+    with numpy's binary16 rounding; every code is the nearest to the fp32
+    t = (w - m) / s (ties up); reconstruction stays within half a step plus
+    the fp16 roundings of m and s."""
+    for w in _random_blocks(70) + [np.full(32, 0.7, np.float32), np.arange(32, dtype=np.float32) - 40]:
+        blk = O.quantize_block(FP2M, w)
+        lo, hi = np.float32(w.min()), np.float32(w.max())
+        m16 = np.float16(lo)
+        m = np.float32(m16)
+        span = np.float32(max(np.float32(hi - m), np.float32(0.0)))
+        s = np.float32(np.float16(span / np.float32(3.0)))
+        assert O.block_min(FP2M, blk) == float(m)
+        assert O.block_scale(FP2M, blk) == float(s)
+        codes = O.unpack_codes(FP2M, blk)
+        if s == 0:
+            assert np.all(codes == 0)
+            continue
+        t = (w - m) / s  # fp32, as the format fixes
+        want = np.clip(np.floor(t.astype(np.float64) + 0.5), 0, 3)
+        assert np.array_equal(codes, want)
+        d = O.dequantize_block(FP2M, blk)
+        err = np.abs(w.astype(np.float64) - d)
+        bound = 0.5 * float(s) + max(float(m) - float(lo), 0.0) + 3 * abs(float(span) / 3 - float(s)) \
+            + 1e-6 * float(np.max(np.abs(w)))
+        assert np.all(err <= bound)
+
+
+def test_fp2m_power_of_two_equivariance():
+    for w in _random_blocks(71, 100):
+        b = O.quantize_block(FP2M, w)
+        s, m = O.block_scale(FP2M, b), O.block_min(FP2M, b)
+        for k in (-2, 3):
+            if not all(v == 0 or 6.2e-5 < abs(v) * 2.0 ** k < 6.0e4 for v in (s, m)):
+                continue
+            if s != 0 and s < 6.2e-5:
+                continue
+            bk = O.quantize_block(FP2M, (w * np.float32(2.0 ** k)).astype(np.float32))
+            assert np.array_equal(O.unpack_codes(FP2M, bk), O.unpack_codes(FP2M, b))
+            assert O.block_scale(FP2M, bk) == s * 2.0 ** k and O.block_min(FP2M, bk) == m * 2.0 ** k
+
+
+def test_fp2m_gemv_is_the_dequantized_product():
+    """The oracle's per-block s * (S D + M X) against the plain fp64 sum of
+    dequantized weights times dequantized activations (a different order of
+    the same exact terms; a dropped or mis-signed minimum term fails)."""
+    rng = np.random.default_rng(72)
+    N, K, Q = 5, 96, 3
+    W = (rng.standard_normal((N, K)) * 0.3 + rng.uniform(-1, 1, (N, 1))).astype(np.float32)
+    blocks = O.quantize_matrix(FP2M, W)
+    x = rng.standard_normal((Q, K)).astype(np.float32)
+    xq, xs = O.quantize_act(x)
+    y, dots = O.gemv(FP2M, blocks, xq, xs, want_dots=True)
+    Wd = O.dequantize_matrix(FP2M, blocks)
+    xd = xq.astype(np.float64) * np.repeat(xs.astype(np.float64), 32, axis=1)
+    assert np.allclose(y, xd @ Wd.T, rtol=1e-12, atol=1e-12)
+    codes = np.array([[O.unpack_codes(FP2M, blocks[n, b]) for b in range(K // 32)] for n in range(N)])
+    for j in range(Q):
+        want = (codes * xq[j].reshape(1, K // 32, 32)).sum(-1)
+        assert np.array_equal(dots[j], want)
+
+
+def test_fp2m_range_errors():
+    w = np.zeros(32, np.float32)
+    w[0] = np.float32(-70000.0)  # the fp16 minimum overflows
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP2M, w)
+    w = np.zeros(32, np.float32)
+    w[0] = np.float32(3.0e5)  # the fp16 scale overflows
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP2M, w)
+    w[0] = np.nan
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP2M, w)
