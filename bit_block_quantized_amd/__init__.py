@@ -18,6 +18,10 @@ import numpy as np
 
 FP2, FP3, FP4 = 2, 3, 4
 FORMATS = (FP2, FP3, FP4)
+# Variant: fp16 scale and fp16 minimum per block (weight = s * c + m),
+# GEMV entry points only.
+FP2M = 12
+VARIANT_FORMATS = (FP2M,)
 
 RFX_OK = 0
 _STATUS = {-1: "RFX_E_INVAL", -2: "RFX_E_ALIGN", -3: "RFX_E_RANGE", -4: "RFX_E_UNSUPPORTED",

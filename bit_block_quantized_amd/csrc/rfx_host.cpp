@@ -85,17 +85,17 @@ const char *rfx_version(void) { return "rfx 0.1 gfx950"; }
 
 int rfx_block_bytes(int fmt)
 {
-    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : RFX_E_INVAL;
+    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M ? 12 : RFX_E_INVAL;
 }
 
 int rfx_code_bytes(int fmt)
 {
-    return fmt == RFX_FP2 ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16 : RFX_E_INVAL;
+    return fmt == RFX_FP2 || fmt == RFX_FP2M ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16 : RFX_E_INVAL;
 }
 
 int rfx_scale_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP3 ? 2 : fmt == RFX_FP4 ? 1 : RFX_E_INVAL;
+    return fmt == RFX_FP2 || fmt == RFX_FP3 ? 2 : fmt == RFX_FP4 ? 1 : fmt == RFX_FP2M ? 4 : RFX_E_INVAL;
 }
 
 } // extern "C"
@@ -135,7 +135,7 @@ inline int code_fp4(float t)
 
 inline void put_code(int fmt, uint8_t *codes, int t, int c)
 {
-    if (fmt == RFX_FP2 || fmt == RFX_FP3) {
+    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         codes[4 * m + j] |= (uint8_t)((c & 3) << (2 * i));
         if (fmt == RFX_FP3)
@@ -148,7 +148,7 @@ inline void put_code(int fmt, uint8_t *codes, int t, int c)
 
 inline int get_code(int fmt, const uint8_t *codes, int t)
 {
-    if (fmt == RFX_FP2 || fmt == RFX_FP3) {
+    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         int c = (codes[4 * m + j] >> (2 * i)) & 3;
         if (fmt == RFX_FP3)
@@ -166,7 +166,62 @@ inline int code_value(int fmt, int c)
         return 2 * c - 3;
     if (fmt == RFX_FP3)
         return 2 * c - 7;
+    if (fmt == RFX_FP2M)
+        return c;
     return (c & 8) ? -mag[c & 7] : mag[c & 7];
+}
+
+inline void put_half(uint8_t *p, _Float16 h)
+{
+    uint16_t bits;
+    std::memcpy(&bits, &h, 2);
+    p[0] = (uint8_t)(bits & 0xff);
+    p[1] = (uint8_t)(bits >> 8);
+}
+
+inline float get_half(const uint8_t *p)
+{
+    const uint16_t bits = (uint16_t)(p[0] | (p[1] << 8));
+    _Float16 h;
+    std::memcpy(&h, &bits, 2);
+    return (float)h;
+}
+
+// FP2M: the minimum and the span over three, both rounded to fp16; codes
+// by threshold on t = (w - m) / s (fp32), ties to the larger code.
+int encode_fp2m(const float *w, uint8_t *blk)
+{
+    // strict comparisons: among equal values (+0 and -0) the first one
+    // stays, so the signs of zero are fixed by the block's order
+    float lo = w[0], hi = w[0];
+    for (int t = 1; t < 32; t++) {
+        if (w[t] < lo)
+            lo = w[t];
+        if (w[t] > hi)
+            hi = w[t];
+    }
+    const _Float16 mh = (_Float16)lo;
+    const float m = (float)mh;
+    if (std::isinf(m))
+        return fail(RFX_E_RANGE, "fp16 minimum overflow (min %g)", (double)lo);
+    float span = hi - m;
+    if (span < 0.0f)
+        span = 0.0f;
+    const _Float16 sh = (_Float16)(span / 3.0f);
+    const float s = (float)sh;
+    if (std::isinf(s))
+        return fail(RFX_E_RANGE, "fp16 scale overflow (span %g)", (double)span);
+    for (int t = 0; t < 32; t++) {
+        int c = 0;
+        if (s != 0.0f) {
+            const float q = (w[t] - m) / s;
+            c = q >= 2.5f ? 3 : q >= 1.5f ? 2 : q >= 0.5f ? 1 : 0;
+        }
+        put_code(RFX_FP2M, blk, t, c);
+    }
+    put_half(blk + 8, sh);
+    put_half(blk + 10, mh);
+    return RFX_OK;
 }
 
 int encode_block(int fmt, const float *w, uint8_t *blk)
@@ -179,6 +234,8 @@ int encode_block(int fmt, const float *w, uint8_t *blk)
         amax = std::fmax(amax, std::fabs(w[t]));
     }
     std::memset(blk, 0, (size_t)rfx_block_bytes(fmt));
+    if (fmt == RFX_FP2M)
+        return encode_fp2m(w, blk);
     if (fmt == RFX_FP4) {
         // OCP MX: E = floor(log2 amax) - 2 + 127, clamped; ilogb is exact,
         // subnormals included.
@@ -214,6 +271,7 @@ struct TilePos {
     size_t code0;  // first 8 or 16 code bytes
     size_t code1;  // FP3: the 4 high-bit bytes
     size_t scale;  // scale byte(s)
+    size_t min;    // FP2M: the fp16 minimum
 };
 
 inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
@@ -233,6 +291,7 @@ inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
             p.scale = tile + 6 * kChunk + lane * 16 + bi * 2;
         } else {
             p.scale = tile + 4 * kChunk + lane * 16 + bi * 2;
+            p.min = tile + 5 * kChunk + lane * 16 + bi * 2;
         }
     }
     return p;
@@ -250,6 +309,8 @@ void place_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *blk
         if (fmt == RFX_FP3)
             std::memcpy(tiled + p.code1, blk + 8, 4);
         std::memcpy(tiled + p.scale, blk + cb, 2);
+        if (fmt == RFX_FP2M)
+            std::memcpy(tiled + p.min, blk + cb + 2, 2);
     }
 }
 
@@ -265,6 +326,8 @@ void fetch_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *til
         if (fmt == RFX_FP3)
             std::memcpy(blk + 8, tiled + p.code1, 4);
         std::memcpy(blk + cb, tiled + p.scale, 2);
+        if (fmt == RFX_FP2M)
+            std::memcpy(blk + cb + 2, tiled + p.min, 2);
     }
 }
 
@@ -336,17 +399,10 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32)
     if (!w32 || !blk)
         return fail(RFX_E_INVAL, "NULL buffer");
     const int cb = rfx_code_bytes(fmt);
-    float s;
-    if (fmt == RFX_FP4) {
-        s = std::ldexp(1.0f, (int)blk[cb] - 128);
-    } else {
-        _Float16 h;
-        uint16_t bits = (uint16_t)(blk[cb] | (blk[cb + 1] << 8));
-        std::memcpy(&h, &bits, 2);
-        s = (float)h;
-    }
+    const float s = fmt == RFX_FP4 ? std::ldexp(1.0f, (int)blk[cb] - 128) : get_half(blk + cb);
+    const float m = fmt == RFX_FP2M ? get_half(blk + cb + 2) : 0.0f;
     for (int t = 0; t < 32; t++)
-        w32[t] = s * (float)code_value(fmt, get_code(fmt, blk, t));
+        w32[t] = s * (float)code_value(fmt, get_code(fmt, blk, t)) + m;
     return RFX_OK;
 }
 

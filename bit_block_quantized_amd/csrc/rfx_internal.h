@@ -18,10 +18,11 @@ constexpr int kChunk = 1024;                                // 64 rows x 16 B
 
 constexpr int tile_bytes(int fmt)
 {
-    return fmt == RFX_FP2 ? 5 * kChunk : fmt == RFX_FP3 ? 7 * kChunk : fmt == RFX_FP4 ? 8 * kChunk + 512 : 0;
+    return fmt == RFX_FP2 ? 5 * kChunk : fmt == RFX_FP3 ? 7 * kChunk : fmt == RFX_FP4 ? 8 * kChunk + 512
+         : fmt == RFX_FP2M ? 6 * kChunk : 0;
 }
 
-inline bool fmt_ok(int fmt) { return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP4; }
+inline bool fmt_ok(int fmt) { return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP4 || fmt == RFX_FP2M; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -50,23 +50,30 @@ enum {
 };
 
 /* Block formats. A block is 32 consecutive weights of one row along the
- * reduction dimension, stored as packed codes plus one scale ([HM] para 2:
- * "packed low-bit codes plus one or two small scales"; this library uses one).
+ * reduction dimension, stored as packed codes plus one scale ([HM] para 2
+ * lets a block carry a single small scale or a pair; the three named formats
+ * here use one, the FP2M variant two).
  *   RFX_FP2: 2-bit codes, codebook {-3,-1,+1,+3}, fp16 scale: 10 B / block
  *   RFX_FP3: 3-bit codes, codebook {-7,-5,...,+7}, fp16 scale: 14 B / block
  *   RFX_FP4: 4-bit OCP E2M1 codes (value = 2 x E2M1, |v| <= 12), one e8m0
  *            exponent byte E, scale 2^(E-128): 17 B / block (MXFP4)
  * 10 / 14 / 17 bytes are the pages' 2.50 / 3.50 / 4.25 bits per weight
- * ([HM] para 2; [KK] mixed-precision section). */
-enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4 };
+ * ([HM] para 2; [KK] mixed-precision section).
+ *   RFX_FP2M: variant with a scale and a minimum per block (a reading of
+ *            the two-value block the same paragraph allows, not one of the
+ *            named formats): 2-bit codes c in 0..3, weight = s * c + m, fp16
+ *            s then fp16 m: 12 B / block (3.0 bits per weight). Supported
+ *            by the encoder, the layout routines and the GEMV entry points;
+ *            the MoE and prefill layers return RFX_E_UNSUPPORTED for it. */
+enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_FP2M = 12 };
 
 const char *rfx_status_str(int status);
 const char *rfx_last_error(void);
 const char *rfx_version(void);
 
-int rfx_block_bytes(int fmt); /* 10 / 14 / 17, or RFX_E_INVAL */
-int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 */
-int rfx_scale_bytes(int fmt); /* 2 / 2 / 1 */
+int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M), or RFX_E_INVAL */
+int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 */
+int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 */
 
 /* ------------------------------------------------------------------ */
 /* Host-side encoder (synchronous, host memory).                       */
@@ -80,12 +87,16 @@ int rfx_scale_bytes(int fmt); /* 2 / 2 / 1 */
  * ties go to the larger magnitude for FP2/FP3 (0 -> +1) and to the even
  * E2M1 mantissa for FP4. A zero (or underflowed) FP2/FP3 scale codes every
  * weight as +1 with s = 0.
+ * FP2M: m = fp16_rne(min w); s = fp16_rne(max(max w - m, 0) / 3) in fp32;
+ * code = nearest of 0..3 to (w - m) / s in fp32, ties to the larger; s = 0
+ * codes every weight as 0. Block: codes, s, m (both fp16 little-endian).
  * Bit layout of the code bytes, as little-endian 32-bit words:
- *   FP2: weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
+ *   FP2 (and FP2M): weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
  *   FP3: low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
  *        at word 2 bit 8j+i
  *   FP4: weight 8m+4i+j (m<4, i<2, j<4) at word m bits [8j+4i, 8j+4i+4)
- * Returns RFX_E_RANGE for a non-finite weight or an fp16 scale overflow. */
+ * Returns RFX_E_RANGE for a non-finite weight or an fp16 scale (or FP2M
+ * minimum) overflow. */
 int rfx_quantize_block(int fmt, const float *w32, uint8_t *blk);
 int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
 
@@ -105,6 +116,7 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
  *       chunk 6 = the eight fp16 scales.
  *   FP4 (tile 8704 B): chunks 0-7 = codes of block c; then 64 rows x 8 B of
  *       e8m0 scales at byte 8192 + r * 8.
+ *   FP2M (tile 6144 B): chunks 0-4 as FP2; chunk 5 = the eight fp16 minima.
  * Rows beyond `rows` and blocks beyond cols/32 are zero (scale 0). Block
  * bits are exactly those of the canonical block. A stack of `count`
  * matrices (MoE experts) places matrix e at e * rfx_qmat_bytes(...). */
@@ -202,8 +214,8 @@ int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsu
 /* ------------------------------------------------------------------ */
 /* Routed experts: gate and up (rows = inter, cols = hidden) and down
  * (rows = hidden, cols = inter), `n_experts` stacked each ([HM] para 2 and
- * [KK] ROCmFPX section: gate/up in FP2, down in FP3; any format is
- * accepted). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
+ * [KK] ROCmFPX section: gate/up in FP2, down in FP3; any of RFX_FP2, RFX_FP3
+ * and RFX_FP4 is accepted, RFX_FP2M is not). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
  * or sh_gate.data == NULL for none. Router: fp32 [n_experts][hidden]
  * weights and an optional fp32 [n_experts] bias. */
 typedef struct rfx_moe_layer {

@@ -16,6 +16,7 @@ import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FMTS = (2, 3, 4)
+ALL_FMTS = (2, 3, 4, 12)  # the three named formats and the FP2M variant
 
 
 def _header_functions():
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_sizes():
     for fmt, (bb, cb, sb, tile) in {2: (10, 8, 2, 5120), 3: (14, 12, 2, 7168),
-                                     4: (17, 16, 1, 8704)}.items():
+                                     4: (17, 16, 1, 8704), 12: (12, 8, 4, 6144)}.items():
         assert R.block_bytes(fmt) == bb == O.block_bytes(fmt)
         assert R.code_bytes(fmt) == cb and R.scale_bytes(fmt) == sb
         assert R.qmat_bytes(fmt, 64, 256) == tile == 64 * 8 * bb
@@ -65,10 +66,23 @@ def _adversarial_blocks():
     w = np.zeros(32, np.float32)
     w[7] = 2.0 ** -130
     blocks.append(w)
+    # FP2M: exact ties (m = 0, s = 1), a minimum that rounds above every
+    # weight (negative span), signed zeros in either order, an offset block
+    w = np.zeros(32, np.float32)
+    w[1:6] = [3.0, 0.5, 1.5, 2.5, 1.0]
+    blocks.append(w)
+    blocks.append(np.full(32, 0.99995, np.float32))
+    for first in (-0.0, 0.0):
+        w = np.zeros(32, np.float32)
+        w[0] = first
+        w[5] = -first
+        blocks.append(w)
+    blocks.append((rng.standard_normal(32) * 0.01 + 40.0).astype(np.float32))
+    blocks.append(np.linspace(-65000.0, 60000.0, 32).astype(np.float32))
     return blocks
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_host_encoder_matches_oracle(fmt):
     for w in _adversarial_blocks():
         a = R.quantize_block(fmt, w)
@@ -78,7 +92,7 @@ def test_host_encoder_matches_oracle(fmt):
                               O.dequantize_block(fmt, b))
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 @pytest.mark.parametrize("shape", [(1, 32), (64, 256), (65, 288), (200, 544), (130, 1024)])
 def test_tiled_packer_roundtrip(fmt, shape):
     rows, cols = shape
@@ -94,7 +108,7 @@ def test_tiled_layout_positions():
     """A block's bytes land where the header says: tile (g, s), chunk c,
     row r at c*1024 + r*16."""
     rows, cols = 130, 600
-    for fmt in FMTS:
+    for fmt in ALL_FMTS:
         nb = cols // 32
         bb = R.block_bytes(fmt)
         blocks = np.zeros((rows, nb, bb), np.uint8)
@@ -118,6 +132,9 @@ def test_tiled_layout_positions():
             else:
                 sc = tile + 4 * 1024 + lane * 16 + bi * 2
                 assert list(t[sc:sc + 2]) == [9, 10]
+                if fmt == 12:
+                    mn = tile + 5 * 1024 + lane * 16 + bi * 2
+                    assert list(t[mn:mn + 2]) == [11, 12]
         assert int(t.astype(np.int64).sum()) == int(np.arange(1, bb + 1).sum())
 
 
@@ -198,6 +215,23 @@ def test_device_entry_validation_without_gpu():
     assert L.rfx_quantize_act(None, 1, 64, _fake(good), _fake(good), _fake(good), null) == -1
     assert L.rfx_debug_block_dots(ctypes.byref(W), _fake(good), _fake(good), 0, _fake(good), null) == -1
     assert b"q" in L.rfx_last_error()
+
+
+def test_moe_rejects_the_gemv_only_variant():
+    """The MoE and prefill layers refuse FP2M before any HIP call."""
+    L = R.lib()
+    good = 0x7f0000000000
+    f = _fake(good)
+    H, I, E = 256, 512, 4
+    lay = R.MoeLayerC(H, I, E, 0, R.QMat(12, I, H, E, good), R.QMat(12, I, H, E, good),
+                      R.QMat(3, H, I, E, good), R.QMat(0, 0, 0, 0, None), R.QMat(0, 0, 0, 0, None),
+                      R.QMat(0, 0, 0, 0, None), good, None)
+    st = L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, 1 << 20, None)
+    assert st == -4 and b"FP2M" in L.rfx_last_error()
+    lay.gate.fmt = lay.up.fmt = 2
+    lay.down.fmt = 12
+    st = L.rfx_moe_route_topk(ctypes.byref(lay), f, 1, 2, f, f, f, f, f, f, f, f, 1 << 20, None)
+    assert st == -4
 
 
 def test_status_strings():
