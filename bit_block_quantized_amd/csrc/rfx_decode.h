@@ -32,8 +32,8 @@ __device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p) { return (sptr_
 
 template <int FMT>
 struct TileFmt {
-    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : 8704;
-    static constexpr int code_chunks = FMT == RFX_FP2 ? 4 : FMT == RFX_FP3 ? 6 : 8;
+    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : FMT == RFX_FP2M ? 6144 : 8704;
+    static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M ? 4 : FMT == RFX_FP3 ? 6 : 8;
 };
 
 // ------------------------------------------------------------------
@@ -127,13 +127,11 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
 template <int FMT>
 struct TileRegs {
     u32x4 c[TileFmt<FMT>::code_chunks];
-    u32x4 sc16; // FP2/FP3: eight fp16 scales
+    u32x4 sc16; // FP2/FP3/FP2M: eight fp16 scales
+    u32x4 mn16; // FP2M: eight fp16 minima
     u32x2 sc8;  // FP4: eight e8m0 bytes
 };
 
-// Issue order = use order: the scales first, then the code chunks in the
-// order blocks 0..7 need them, so that with straight-line code the compiler's
-// partial vmcnt waits let block 0 start while later chunks are in flight.
 // Issue order = use order: the scales first, then the code chunks in the
 // order blocks 0..7 need them, so that with straight-line code the compiler's
 // partial vmcnt waits let block 0 start while later chunks are in flight.
@@ -163,6 +161,8 @@ __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ t
         RFX_LD(t.c[3], tp + 64 * 3);
     } else {
         RFX_LD(t.sc16, tp + 64 * 4);
+        if (FMT == RFX_FP2M)
+            RFX_LD(t.mn16, tp + 64 * 5);
 #pragma unroll
         for (int k = 0; k < 4; k++)
             RFX_LD(t.c[k], tp + 64 * k);
@@ -171,7 +171,22 @@ __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ t
     return t;
 }
 
+// fp16 value bi (0..7) of eight packed in a 16-byte chunk.
+__device__ __forceinline__ float half_of(const u32x4 &v, int bi)
+{
+    const uint32_t w2 = (bi >> 1) == 0 ? v.x : (bi >> 1) == 1 ? v.y : (bi >> 1) == 2 ? v.z : v.w;
+    return half_bits_to_float((bi & 1) ? (w2 >> 16) : (w2 & 0xffffu));
+}
+
+// The value added after the scale: FP2M's block minimum, 0 otherwise.
+template <int FMT>
+__device__ __forceinline__ float block_min(const TileRegs<FMT> &t, int bi)
+{
+    return FMT == RFX_FP2M ? half_of(t.mn16, bi) : 0.0f;
+}
+
 // Selector bytes and dequantization scale of block bi (0..7) of a tile.
+// FP2M shares FP2's code layout; its selector byte is the code c itself.
 template <int FMT>
 __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel8 &sel, float &sw)
 {
@@ -234,7 +249,8 @@ __device__ __forceinline__ XBlock<Q> load_xblock(const XCols<Q> &c, int b)
     return xb;
 }
 
-// Exact per-block integer dot D for column j (codebook offset folded in).
+// Exact per-block integer dot D for column j (codebook offset folded in;
+// FP2M: D = sum(c x), the minimum enters through the block sum).
 template <int FMT, int Q>
 __device__ __forceinline__ int block_dot(const Sel8 &sel, const XBlock<Q> &xb, int j)
 {
@@ -249,13 +265,19 @@ __device__ __forceinline__ int block_dot(const Sel8 &sel, const XBlock<Q> &xb, i
     return d;
 }
 
+// FP2M: the block is s * c + m, so its dot is sx * (s D + m X), X the
+// activation block's code sum.
 template <int FMT, int Q, int NQ>
 __device__ __forceinline__ void accumulate_block(const Sel8 &sel, float sw, const XBlock<Q> &xb,
-                                                 float (&acc)[Q])
+                                                 float (&acc)[Q], float mn = 0.0f)
 {
 #pragma unroll
-    for (int j = 0; j < NQ; j++)
-        acc[j] += (sw * xb.sx[j]) * (float)block_dot<FMT, Q>(sel, xb, j);
+    for (int j = 0; j < NQ; j++) {
+        if (FMT == RFX_FP2M)
+            acc[j] += xb.sx[j] * (sw * (float)block_dot<FMT, Q>(sel, xb, j) + mn * (float)xb.sum[j]);
+        else
+            acc[j] += (sw * xb.sx[j]) * (float)block_dot<FMT, Q>(sel, xb, j);
+    }
 }
 
 // All blocks of one tile (blocks b0 .. b0 + 7 of the row) against one set of
@@ -276,9 +298,12 @@ __device__ __forceinline__ void tile_blocks(const TileRegs<FMT> &t, int b0, int 
         Sel8 sel;
         float sw;
         decode_block<FMT>(t, bi, sel, sw);
-        if (!FULL)
+        float mn = block_min<FMT>(t, bi);
+        if (!FULL) {
             sw = b0 + bi < nb ? sw : 0.0f;
-        accumulate_block<FMT, Q, NQ>(sel, sw, xb, acc);
+            mn = b0 + bi < nb ? mn : 0.0f;
+        }
+        accumulate_block<FMT, Q, NQ>(sel, sw, xb, acc, mn);
         // keep each block's work after its own chunk wait (the scheduler
         // would otherwise hoist the decodes and wait for the whole tile)
         __builtin_amdgcn_sched_barrier(0);

@@ -55,8 +55,8 @@ __device__ __forceinline__ Sel8 sel2_fp3(uint32_t w0, uint32_t w1, uint32_t h)
     return s;
 }
 
-// Selector bytes (2c for FP2/FP3, signed values for FP4) and the weight
-// scale of block BI of a tile.
+// Selector bytes (2c for FP2/FP3, c for FP2M, signed values for FP4) and
+// the weight scale of block BI of a tile.
 template <int FMT, int BI>
 __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel, float &sw)
 {
@@ -71,6 +71,8 @@ __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel,
             const u32x4 h4 = t.c[4 + (BI >> 2)];
             const uint32_t h = (BI & 3) == 0 ? h4.x : (BI & 3) == 1 ? h4.y : (BI & 3) == 2 ? h4.z : h4.w;
             sel = sel2_fp3(w0, w1, h);
+        } else if (FMT == RFX_FP2M) {
+            sel = sel_fp2(w0, w1);
         } else {
             sel = sel2_fp2(w0, w1);
         }
@@ -104,8 +106,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // [16 (l / 4), 16 (l / 4) + 16) of column min(l % 4, Q - 1)'s 256-byte
 // slice; lane n of each 16-lane row (n = l & 15) holds column j's fp32
 // scale of block n & 7 in sx[j] and, for FP2/FP3, -off * (block sum) in
-// nsum[j] (off = 3 or 7, the codebook offset folded out of the dot); the
-// block's values reach every lane by DPP row broadcast.
+// nsum[j] (off = 3 or 7, the codebook offset folded out of the dot; FP2M:
+// the block sum itself, which multiplies the block minimum); the block's
+// values reach every lane by DPP row broadcast.
 template <int Q>
 struct XTileM {
     u32x4 code;
@@ -131,7 +134,7 @@ __device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int
     for (int j = 0; j < Q; j++)
         xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
     if (FMT != RFX_FP4) {
-        constexpr int off = FMT == RFX_FP2 ? 3 : 7;
+        constexpr int off = FMT == RFX_FP2 ? 3 : FMT == RFX_FP3 ? 7 : -1; // FP2M: +sum
 #pragma unroll
         for (int j = 0; j < Q; j++)
             xt.nsum[j] = -off * xc.xsum[xc.moff[j] + (uint32_t)bs];
@@ -155,7 +158,7 @@ template <int FMT, int Q, int BI>
 __device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt)
 {
     i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
-    if (FMT != RFX_FP4) {
+    if (FMT == RFX_FP2 || FMT == RFX_FP3) {
 #pragma unroll
         for (int j = 0; j < Q; j++)
             d0[j] = bcast_row<BI>(xt.nsum[j]);
@@ -178,13 +181,19 @@ __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XT
     Sel8 sel;
     float sw;
     decode_block2<FMT, BI>(t, sel, sw);
-    if (!FULL)
+    float mn = block_min<FMT>(t, BI);
+    if (!FULL) {
         sw = b0 + BI < nb ? sw : 0.0f;
+        mn = b0 + BI < nb ? mn : 0.0f;
+    }
     const i32x4 d = block_dots_mfma<FMT, Q, BI>(sel, xt);
 #pragma unroll
     for (int j = 0; j < Q; j++) {
         const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
-        acc[j] += (sw * sxb) * (float)d[j];
+        if (FMT == RFX_FP2M) // sx * (s D + m X)
+            acc[j] += sxb * (sw * (float)d[j] + mn * (float)bcast_row<BI>(xt.nsum[j]));
+        else
+            acc[j] += (sw * sxb) * (float)d[j];
     }
     __builtin_amdgcn_sched_barrier(0);
 }

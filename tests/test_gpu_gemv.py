@@ -14,6 +14,8 @@ from gpu_common import TOL, need_gpu, quantize_on_gpu, rel_err, say, upload_matr
 
 pytestmark = pytest.mark.gpu
 FMTS = (2, 3, 4)
+FP2M = R.FP2M
+GEMV_FMTS = FMTS + (FP2M,)  # the GEMV entry points also take the FP2M variant
 
 
 def _sync(torch):
@@ -59,7 +61,7 @@ def _run(torch, fmt, W, x, q, split, blocks=None):
     return y.cpu().numpy(), dots.cpu().numpy(), yo, do
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
 @pytest.mark.parametrize("q", [1, 2, 3, 4])
 @pytest.mark.parametrize("shape", [(200, 544), (64, 256), (1, 32), (65, 288), (130, 2080)])
 def test_gemv_small_shapes(fmt, q, shape):
@@ -90,12 +92,12 @@ _BIG = {}
 
 def _big(fmt):
     if fmt not in _BIG:
-        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20}[fmt], outliers=True)
+        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30}[fmt], outliers=True)
         _BIG[fmt] = (W, O.quantize_matrix(fmt, W))
     return _BIG[fmt]
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
 @pytest.mark.parametrize("q", [1, 4])
 def test_gemv_7168_full(fmt, q):
     """7168 x 7168 with 1% outliers, q columns seeds 1..q, split-K launch."""
@@ -110,7 +112,7 @@ def test_gemv_7168_full(fmt, q):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("fmt", GEMV_FMTS)
 def test_gemv_deterministic_and_columns_independent(fmt):
     torch = need_gpu()
     say(f"gemv determinism fmt={fmt}")
@@ -131,6 +133,24 @@ def test_gemv_deterministic_and_columns_independent(fmt):
         y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
         R.gemv(dW, xq[j:j + 1], xs[j:j + 1], xsum[j:j + 1], 1, y1, ws1)
         assert rel_err(y1.cpu().numpy()[0], outs[0][j]) <= 1e-6
+
+
+@pytest.mark.parametrize("q", [1, 4])
+def test_gemv_fp2m_offset_rows(q):
+    """FP2M on rows whose weights sit far from zero (each row its own
+    offset, the case the block minimum is for), with ragged K so the
+    minimum of blocks past K must be dropped too."""
+    torch = need_gpu()
+    say(f"gemv fp2m offset rows q={q}")
+    N, K = 300, 1312
+    rng = np.random.default_rng(90 + q)
+    W = (inputgen.dense_weight(N, K, seed=91) * np.float32(0.2)
+         + rng.uniform(-3, 3, (N, 1)).astype(np.float32))
+    x = inputgen.activations(q, K, seed=92)
+    for split in (False, True):
+        y, d, yo, do = _run(torch, FP2M, W, x, q, split)
+        assert np.array_equal(d, do)
+        assert rel_err(y, yo) <= TOL, (split, rel_err(y, yo))
 
 
 # ---------------------------------------------------------- grouped gemv
@@ -172,6 +192,8 @@ def _grouped(torch, specs, seed, big=False):
     [(4, 1, 1024, 1024), (2, 4, 300, 4096), (3, 2, 77, 2048), (4, 3, 512, 768)],
     # a single job
     [(3, 4, 640, 1536)],
+    # the FP2M variant beside the named formats, ragged and full tiles
+    [(12, 1, 200, 544), (2, 4, 130, 2080), (12, 4, 65, 1024), (12, 2, 1, 32), (4, 1, 256, 512)],
 ])
 def test_gemv_grouped_small(specs):
     torch = need_gpu()
