@@ -8,8 +8,9 @@ each with q = 1 and q = 4 activation columns (six GEMVs), run as one
 grouped launch (rfx_gemv_grouped). Weights are N(0, 0.02) with 1% outliers
 x10 (seeds 0 / 10 / 20); columns N(0, 1), seeds 1..q. Each format keeps R
 copies of its matrix at distinct addresses (R x size >= 512 MB, twice the
-256 MB last-level cache); step i uses copy i mod R, so weights stream from
-HBM. Inputs are resident in HBM before the timed region; steps are replayed
+256 MB last-level cache); in step i the q = 1 GEMV uses copy 2i mod R and
+the q = 4 GEMV copy 2i + 1 mod R, so no two GEMVs of a step share weights
+and every byte counted streams from HBM. Inputs are resident in HBM before the timed region; steps are replayed
 from a HIP graph. The same step as six separate launches is reported too.
 
 value = algorithmic bytes of the step (packed weights + quantized
@@ -18,7 +19,9 @@ activations read) / step time, in GB/s.
 Extra fields: per-kernel timings, the MoE decode layer (256 experts, hidden
 4096, intermediate 2048, FP2 gate/up, FP3 down, FP4 shared, q = 4, top-6)
 and the 8-layer stack (top-4, Zipf(1.1) router bias, q = 1 and q = 4), the
-HBM copy reference and the CPU oracle on a bounded sample.
+HBM copy reference and the CPU oracle on a bounded sample. The FP2M
+variant (fp16 scale + fp16 minimum, 12 B / 32 weights, seed 30) is timed
+per kernel beside the named formats; it is not part of the step.
 
 Prints one JSON line. Only one GPU is supported.
 """
@@ -37,7 +40,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 N = K = 7168
 FORMATS = (2, 3, 4)
-SEEDS = {2: 0, 3: 10, 4: 20}
+VARIANTS = (12,)  # FP2M: timed per kernel, not part of the step
+SEEDS = {2: 0, 3: 10, 4: 20, 12: 30}
+FMT_NAME = {2: "FP2", 3: "FP3", 4: "FP4", 12: "FP2M"}
 LLC_BYTES = 256 << 20
 MOE_H, MOE_I, MOE_E = 4096, 2048, 256
 
@@ -56,7 +61,7 @@ def algorithmic_bytes(R, fmt, q, n=N, k=K):
 
 def build_gemv(torch, R, inputgen):
     work = {}
-    for fmt in FORMATS:
+    for fmt in FORMATS + VARIANTS:
         W = inputgen.dense_weight(N, K, seed=SEEDS[fmt], outliers=True)
         tiled = R.quantize_matrix(fmt, W)
         nbytes = tiled.nbytes
@@ -78,12 +83,17 @@ def build_gemv(torch, R, inputgen):
         acts[q] = {"xq": xq, "xs": xs, "xsum": xsum,
                    "y": torch.empty((q, N), dtype=torch.float32, device="cuda")}
     ws = {}
-    for fmt in FORMATS:
+    for fmt in FORMATS + VARIANTS:
         for q in (1, 4):
             n = R.gemv_workspace_bytes(work[fmt]["mats"][0], q)
             ws[(fmt, q)] = torch.zeros(n, dtype=torch.uint8, device="cuda") if n else None
     torch.cuda.synchronize()
     return work, acts, ws
+
+
+def copy_index(q, i):
+    """Weight copy of the q-column GEMV in step i (distinct for q = 1, 4)."""
+    return 2 * i + (q > 1)
 
 
 def gemv_launch(R, work, acts, ws, fmt, q, i):
@@ -94,7 +104,8 @@ def gemv_launch(R, work, acts, ws, fmt, q, i):
 
 def grouped_step_jobs(torch, R, work, acts):
     """Job arrays of the grouped step, one per rotation index, and their
-    (shared, zero-filled) workspace. Each job writes its own output."""
+    (shared, zero-filled) workspace. Each job writes its own output and
+    reads its own weight copy."""
     rot = max(len(work[f]["mats"]) for f in FORMATS)
     ys = {(f, q): torch.empty((q, N), dtype=torch.float32, device="cuda") for f in FORMATS for q in (1, 4)}
     arrs = []
@@ -104,7 +115,7 @@ def grouped_step_jobs(torch, R, work, acts):
             mats = work[fmt]["mats"]
             for q in (1, 4):
                 a = acts[q]
-                jobs.append((mats[i % len(mats)], q, a["xq"], a["xs"], a["xsum"], ys[(fmt, q)]))
+                jobs.append((mats[copy_index(q, i) % len(mats)], q, a["xq"], a["xs"], a["xsum"], ys[(fmt, q)]))
         arrs.append(R.gemv_jobs(jobs))
     n = R.gemv_grouped_workspace_bytes(arrs[0])
     gws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
@@ -397,30 +408,30 @@ def main():
         return
 
     per = []
-    for fmt in FORMATS:
+    for fmt in FORMATS + VARIANTS:
         for q in (1, 4):
             copies = len(work[fmt]["mats"])
             g = graph_of(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), copies)
             us = time_graph(torch, g, args.kernel_reps) * 1e3 / copies
             us_eager = time_eager(torch, lambda i: gemv_launch(R, work, acts, ws, fmt, q, i), 4 * copies) * 1e3
             w, a, wr = algorithmic_bytes(R, fmt, q)
-            per.append({"fmt": f"FP{fmt}", "q": q, "us": round(us, 3), "eager_us": round(us_eager, 3),
+            per.append({"fmt": FMT_NAME[fmt], "q": q, "us": round(us, 3), "eager_us": round(us_eager, 3),
                         "weight_bytes": w, "act_bytes": a, "write_bytes": wr,
                         "GBps": round((w + a) / us / 1e3, 1),
                         "frac_hbm": round((w + a) / us / 1e3 / HBM_PEAK_GBPS, 4)})
-            log(f"FP{fmt} q={q}: {us:.2f} us (eager {us_eager:.2f})  {(w + a) / us / 1e3:.0f} GB/s")
+            log(f"{FMT_NAME[fmt]} q={q}: {us:.2f} us (eager {us_eager:.2f})  {(w + a) / us / 1e3:.0f} GB/s")
             del g
 
     # whole step: the six GEMVs as one grouped launch (the headline) and,
     # for comparison, as six launches back to back; one graph holds `rot`
     # steps
-    assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per)
+    assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per if p["fmt"] != "FP2M")
     rot = len(garrs)
 
     def step_six(i):
         for fmt in FORMATS:
             for q in (1, 4):
-                gemv_launch(R, work, acts, ws, fmt, q, i)
+                gemv_launch(R, work, acts, ws, fmt, q, copy_index(q, i))
 
     g = graph_of(torch, step_six, rot)
     ms_six = time_graph(torch, g, max(1, -(-args.steps // rot))) / rot
@@ -450,17 +461,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dense GEMV 7168x7168, FP2/FP3/FP4 x q=1,4 per step, rotated copies",
                    "rows": N, "cols": K, "formats": ["FP2", "FP3", "FP4"], "q": [1, 4],
-                   "copies": {f"FP{f}": len(work[f]["mats"]) for f in FORMATS},
+                   "copies": {FMT_NAME[f]: len(work[f]["mats"]) for f in FORMATS},
                    "timing": "HIP graph replay, one grouped launch per step"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gemv_grouped_kernel (FP2/FP3/FP4 x q=1,4, 7168x7168)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("grouped"),
-                     "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy; for "
-                                     "this kernel the read counter gives 0.70 x the unique weight bytes "
-                                     "(L2 hits on long streams without counted DRAM reads; lone GEMV "
-                                     "launches read 1.01 x): profiles/gemv_grouped_7168_pmc.txt",
+                     "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy "
+                                     "(read 1.010 x the algorithmic bytes): "
+                                     "profiles/gemv_grouped_7168_pmc.txt",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(ms * 1e3, 3)},
         "step_six_launches": {"us": round(ms_six * 1e3, 3),
