@@ -276,7 +276,7 @@ def bench_prefill(torch, R, inputgen, layer, reps, tokens=2048, k=6):
             "timing": "HIP graph replay of route + FFN"}
 
 
-GEMV_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_xtile.h")
+GEMV_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_mx4.h", "rfx_xtile.h")
 
 
 def kernel_sources_sha256():
@@ -469,7 +469,7 @@ def main():
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("grouped"),
                      "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy "
-                                     "(read 1.010 x the algorithmic bytes): "
+                                     "(read 1.009 x the algorithmic bytes): "
                                      "profiles/gemv_grouped_7168_pmc.txt",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(ms * 1e3, 3)},

@@ -46,6 +46,7 @@
 #include <cstdio>
 
 #include "rfx_decode.h"
+#include "rfx_mx4.h"
 #include "rfx_xtile.h"
 #include "rfx_internal.h"
 
@@ -333,12 +334,84 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float
         gemv_finish<Q>(a, p, g, W, red);
 }
 
+// FP4 blocks go to the block-scaled matrix core (rfx_mx4.h) for one or two
+// activation columns (one column pair of the B operand). From three columns
+// on, the two pairs cost more registers (166 per lane: three waves per
+// SIMD) and a longer dependency chain per tile than the vector decode with
+// the 4x4x4 int8 matrix op saves; measured on the 7168 x 7168 step, the
+// FP4 q = 4 job ran faster on that path.
+template <int FMT, int Q>
+constexpr bool use_mx()
+{
+    return FMT == RFX_FP4 && Q <= 2;
+}
+
+// FP4 on the block-scaled matrix core (rfx_mx4.h): the same tile split,
+// K split and epilogue as gemv_body, with each wave's partials moved into
+// the row layout of the LDS reduction before it. LBC: the multi-tile loop
+// keeps the next tile in flight (two tile buffers; within the register
+// budget of a workgroup of at most 256 threads), else it loads and
+// computes one tile at a time.
+template <int Q, bool FULL, bool LBC>
+__device__ __forceinline__ void gemv_body_mx(const GemvArgs &a, int p, int g, float *red)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    XCols<Q> xc;
+    xc.xq = a.xq;
+    xc.xs = a.xs;
+    xc.xsum = a.xsum;
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        xc.xoff[j] = (uint32_t)j * (uint32_t)a.K;
+        xc.moff[j] = (uint32_t)j * (uint32_t)a.nb;
+    }
+    const MxLane<Q> ml = mx_lane<Q>(lane, xc);
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            acc[i][v] = 0.0f;
+
+    const int nw = a.P * W, vv = p * W + wave;
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * vv) / (unsigned)nw));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * (vv + 1)) / (unsigned)nw));
+    const uint8_t *gbase = a.W + (size_t)g * a.S * TileFmt<RFX_FP4>::bytes;
+    constexpr int TB = TileFmt<RFX_FP4>::bytes;
+    if (LBC && s_end - s_begin > 1) {
+        MxTile<Q> ta = load_mx_tile<Q, FULL>(gbase + (size_t)s_begin * TB, s_begin, a.nb, lane, xc, ml), tb;
+        for (int s = s_begin; s < s_end; s += 2) {
+            if (s + 1 < s_end)
+                tb = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 1) * TB, s + 1, a.nb, lane, xc, ml);
+            compute_mx_tile<Q>(ta, ml, acc);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end)
+                ta = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 2) * TB, s + 2, a.nb, lane, xc, ml);
+            compute_mx_tile<Q>(tb, ml, acc);
+        }
+    } else {
+        for (int s = s_begin; s < s_end; s++) {
+            const MxTile<Q> t = load_mx_tile<Q, FULL>(gbase + (size_t)s * TB, s, a.nb, lane, xc, ml);
+            compute_mx_tile<Q>(t, ml, acc);
+        }
+    }
+    mx_to_red<Q>(acc, red, wave, lane);
+    __syncthreads();
+    if (wave == 0)
+        gemv_finish<Q>(a, p, g, W, red);
+}
+
 // One GEMV; grid = (P, G).
 template <int FMT, int Q, bool DOTS, bool FULL>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 {
     __shared__ float red[16 * Q * 64];
-    gemv_body<FMT, Q, DOTS, FULL>(a, blockIdx.x, blockIdx.y, red);
+    if constexpr (use_mx<FMT, Q>() && !DOTS)
+        gemv_body_mx<Q, FULL, false>(a, blockIdx.x, blockIdx.y, red);
+    else
+        gemv_body<FMT, Q, DOTS, FULL>(a, blockIdx.x, blockIdx.y, red);
 }
 
 // Several independent GEMVs in one launch. The workgroups are the jobs'
@@ -376,7 +449,12 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
     const int local = bid - ga.wg_begin[j];
     const int p = local & (a.P - 1), g = local / a.P;
 #define RFX_JOB(F, QQ)                                                                                        \
-    case 8 * F + QQ: gemv_body<F, QQ, false, FULL, true>(a, p, g, red); break;
+    case 8 * F + QQ:                                                                                          \
+        if constexpr (use_mx<F, QQ>())                                                                        \
+            gemv_body_mx<QQ, FULL, true>(a, p, g, red);                                                       \
+        else                                                                                                  \
+            gemv_body<F, QQ, false, FULL, true>(a, p, g, red);                                                \
+        break;
     switch (ga.kind[j]) {
         RFX_JOB(RFX_FP2, 1) RFX_JOB(RFX_FP2, 2) RFX_JOB(RFX_FP2, 3) RFX_JOB(RFX_FP2, 4)
         RFX_JOB(RFX_FP3, 1) RFX_JOB(RFX_FP3, 2) RFX_JOB(RFX_FP3, 3) RFX_JOB(RFX_FP3, 4)
