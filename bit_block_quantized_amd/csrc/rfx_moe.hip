@@ -28,6 +28,7 @@
 #include "rfx_decode.h"
 #include "rfx_internal.h"
 #include "rfx_moe_ws.h"
+#include "rfx_mx4.h"
 #include "rfx_xtile.h"
 
 using namespace rfx;
@@ -435,6 +436,41 @@ __device__ __forceinline__ void gateup_tile(const GUTile<FG, NE> &t, int s, int 
         tile_blocks2<FG, FG, NE, false>(t.g, t.u, s * 8, nbH, xc, ag, au);
 }
 
+// Wave 0: sum the W waves' gate and up partials of row g * 64 + lane (fixed
+// order), SwiGLU, and the per-32 requantization of h.
+template <int NE>
+__device__ __forceinline__ void gateup_finish(const FfnArgs &a, const SlotCols<NE> &cols, int g, int lane, int W,
+                                              const float *red)
+{
+#define RED_GU(w, m, j) red[(((w) * 2 + (m)) * kMaxDecodeQ + (j)) * 64 + lane]
+    const int row = g * 64 + lane; // row of the intermediate dimension
+    const int nbI = a.I / 32;
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        float gv = RED_GU(0, 0, j), uv = RED_GU(0, 1, j);
+        for (int w = 1; w < W; w++) {
+            gv += RED_GU(w, 0, j);
+            uv += RED_GU(w, 1, j);
+        }
+#undef RED_GU
+        // SwiGLU: silu(g) * u
+        const float hv = row < a.I ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
+        const size_t idx = (size_t)cols.out_idx[j];
+        int8_t qv;
+        float sv;
+        int32_t sm;
+        quant32(hv, &qv, &sv, &sm, true);
+        if (row < a.I) {
+            a.ws.h[idx * a.I + row] = hv;
+            a.ws.hq[idx * a.I + row] = qv;
+            if ((lane & 31) == 0) {
+                a.ws.hs[idx * nbI + (row >> 5)] = sv;
+                a.ws.hsum[idx * nbI + (row >> 5)] = sm;
+            }
+        }
+    }
+}
+
 template <int FG, int NE>
 __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W,
                             float *red)
@@ -492,41 +528,89 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
             gateup_tile<FG, NE>(tb, s + 1, nbH, xc, ag, au);
         }
     }
-    // fixed-order reduction over waves; red[w][m][j][lane], m = gate/up
-#define RED_GU(w, m, j) red[(((w) * 2 + (m)) * kMaxDecodeQ + (j)) * 64 + lane]
+    // fixed-order reduction over waves; red[w][m][j][row], m = gate/up
 #pragma unroll
     for (int j = 0; j < NE; j++) {
-        RED_GU(wave, 0, j) = ag[j];
-        RED_GU(wave, 1, j) = au[j];
+        red[((wave * 2 + 0) * kMaxDecodeQ + j) * 64 + lane] = ag[j];
+        red[((wave * 2 + 1) * kMaxDecodeQ + j) * 64 + lane] = au[j];
     }
     __syncthreads();
-    if (wave != 0)
-        return;
-    const int row = g * 64 + lane; // row of the intermediate dimension
-    const int nbI = a.I / 32;
+    if (wave == 0)
+        gateup_finish<NE>(a, cols, g, lane, W, red);
+}
+
+// FP4 gate and up with one or two tokens on the block-scaled matrix core
+// (rfx_mx4.h): both matrices' products take the same activation operand,
+// built once per (half, column pair). Same tile split, reduction and
+// epilogue as gateup_body.
+template <int NE>
+__device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
+{
+    constexpr int TB = TileFmt<RFX_FP4>::bytes;
+    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const int nbH = a.H / 32;
+    XCols<NE> xc;
+    xc.xq = a.xq;
+    xc.xs = a.xs;
+    xc.xsum = a.xsum;
 #pragma unroll
     for (int j = 0; j < NE; j++) {
-        float gv = RED_GU(0, 0, j), uv = RED_GU(0, 1, j);
-        for (int w = 1; w < W; w++) {
-            gv += RED_GU(w, 0, j);
-            uv += RED_GU(w, 1, j);
-        }
-        // SwiGLU: silu(g) * u
-        const float hv = row < a.I ? gv / (1.0f + expf(-gv)) * uv : 0.0f;
-        const size_t idx = (size_t)cols.out_idx[j];
-        int8_t qv;
-        float sv;
-        int32_t sm;
-        quant32(hv, &qv, &sv, &sm, true);
-        if (row < a.I) {
-            a.ws.h[idx * a.I + row] = hv;
-            a.ws.hq[idx * a.I + row] = qv;
-            if ((lane & 31) == 0) {
-                a.ws.hs[idx * nbI + (row >> 5)] = sv;
-                a.ws.hsum[idx * nbI + (row >> 5)] = sm;
+        xc.xoff[j] = (uint32_t)cols.token[j] * (uint32_t)a.H;
+        xc.moff[j] = (uint32_t)cols.token[j] * (uint32_t)nbH;
+    }
+    const int S = (a.H + 255) / 256;
+    const uint8_t *gm, *um;
+    if (si.kind == 2) {
+        gm = a.sh_gate;
+        um = a.sh_up;
+    } else {
+        gm = a.gate + a.gate_stride * (size_t)si.expert;
+        um = a.up + a.up_stride * (size_t)si.expert;
+    }
+    gm += (size_t)g * S * TB;
+    um += (size_t)g * S * TB;
+    const MxLane<NE> ml = mx_lane<NE>(lane, xc);
+    float acc[2][4][4];
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                acc[m][i][v] = 0.0f;
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
+    if (s_begin < s_end) {
+        // two buffers used in turn: tile s + 1 in flight while s is computed
+        MxW wa[2], wb[2];
+        MxX<NE> xa = load_mx_x<NE, false>(s_begin, nbH, xc, ml), xb;
+        wa[0] = load_mx_w(gm + (size_t)s_begin * TB, lane);
+        wa[1] = load_mx_w(um + (size_t)s_begin * TB, lane);
+        for (int s = s_begin; s < s_end; s += 2) {
+            if (s + 1 < s_end) {
+                xb = load_mx_x<NE, false>(s + 1, nbH, xc, ml);
+                wb[0] = load_mx_w(gm + (size_t)(s + 1) * TB, lane);
+                wb[1] = load_mx_w(um + (size_t)(s + 1) * TB, lane);
             }
+            compute_mx<NE, 2>(wa, xa, ml, acc);
+            if (s + 1 >= s_end)
+                break;
+            if (s + 2 < s_end) {
+                xa = load_mx_x<NE, false>(s + 2, nbH, xc, ml);
+                wa[0] = load_mx_w(gm + (size_t)(s + 2) * TB, lane);
+                wa[1] = load_mx_w(um + (size_t)(s + 2) * TB, lane);
+            }
+            compute_mx<NE, 2>(wb, xb, ml, acc);
         }
     }
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+        mx_rows<NE>(acc[m], lane, [&](int col, int row, float v) {
+            red[((wave * 2 + m) * kMaxDecodeQ + col) * 64 + row] = v;
+        });
+    __syncthreads();
+    if (wave == 0)
+        gateup_finish<NE>(a, cols, g, lane, W, red);
 }
 
 template <int FG, int FS>
@@ -539,18 +623,39 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
+    // FP4 with one or two tokens: the block-scaled matrix core
     if (si.kind == 2) {
         switch (ne) {
-        case 1: gateup_body<FS, 1>(a, si, blockIdx.y, lane, wave, W, red); break;
-        case 2: gateup_body<FS, 2>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 1:
+            if constexpr (FS == RFX_FP4)
+                gateup_body_mx<1>(a, si, blockIdx.y, lane, wave, W, red);
+            else
+                gateup_body<FS, 1>(a, si, blockIdx.y, lane, wave, W, red);
+            break;
+        case 2:
+            if constexpr (FS == RFX_FP4)
+                gateup_body_mx<2>(a, si, blockIdx.y, lane, wave, W, red);
+            else
+                gateup_body<FS, 2>(a, si, blockIdx.y, lane, wave, W, red);
+            break;
         case 3: gateup_body<FS, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
         case 4: gateup_body<FS, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
         default: break;
         }
     } else {
         switch (ne) {
-        case 1: gateup_body<FG, 1>(a, si, blockIdx.y, lane, wave, W, red); break;
-        case 2: gateup_body<FG, 2>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 1:
+            if constexpr (FG == RFX_FP4)
+                gateup_body_mx<1>(a, si, blockIdx.y, lane, wave, W, red);
+            else
+                gateup_body<FG, 1>(a, si, blockIdx.y, lane, wave, W, red);
+            break;
+        case 2:
+            if constexpr (FG == RFX_FP4)
+                gateup_body_mx<2>(a, si, blockIdx.y, lane, wave, W, red);
+            else
+                gateup_body<FG, 2>(a, si, blockIdx.y, lane, wave, W, red);
+            break;
         case 3: gateup_body<FG, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
         case 4: gateup_body<FG, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
         default: break;

@@ -98,47 +98,77 @@ __device__ __forceinline__ MxLane<Q> mx_lane(int lane, const XCols<Q> &xc)
     return m;
 }
 
-// One tile (64 rows x 8 blocks) of FP4 codes with its activation operands.
-template <int Q>
-struct MxTile {
-    static constexpr int NP = (Q + 1) / 2;
-    u32x4 a[8];       // A of (g, h), index 2g + h
-    uint32_t sa[4];   // e8m0 bytes of row 16g + l % 16, blocks 2 (l / 16) + {0, 1}
-    u32x4 xr[2][NP];  // raw int8 activations for the B operand of (h, pair)
-    float sx[2][NP];  // fp32 scale of this lane's (column, block); 0 off-lane
+// One tile (64 rows x 8 blocks) of FP4 codes ...
+struct MxW {
+    u32x4 a[8];     // A of (g, h), index 2g + h
+    uint32_t sa[4]; // e8m0 bytes of row 16g + l % 16, blocks 2 (l / 16) + {0, 1}
 };
 
-template <int Q, bool FULL>
-__device__ __forceinline__ MxTile<Q> load_mx_tile(const uint8_t *__restrict__ tile, int s, int nb, int lane,
-                                                  const XCols<Q> &xc, const MxLane<Q> &ml)
+// ... and the activation operands of its K range (shared by every weight
+// matrix over that range, e.g. an expert's gate and up).
+template <int Q>
+struct MxX {
+    static constexpr int NP = (Q + 1) / 2;
+    u32x4 xr[2][NP]; // raw int8 activations for the B operand of (h, pair)
+    float sx[2][NP]; // fp32 scale of this lane's (column, block); 0 off-lane
+};
+
+// Every address is a uniform base plus a 32-bit lane offset (the
+// SGPR-base form of the global loads): A in 16-byte units at chunk
+// 2 (l / 16) + h, row 16g + l % 16; the two scale bytes of that row.
+__device__ __forceinline__ MxW load_mx_w(const uint8_t *__restrict__ tile, int lane)
 {
-    // Every address is a uniform base plus a 32-bit lane offset (the
-    // SGPR-base form of the global loads): A in 16-byte units at chunk
-    // 2 (l / 16) + h, row 16g + l % 16; the two scale bytes of that row.
-    MxTile<Q> t;
+    MxW w;
     const uint32_t gb = (uint32_t)lane >> 4, n = (uint32_t)lane & 15u;
     const uint32_t ai = 128u * gb + n, si = 4096u + 4u * n + gb; // si in 16-bit units
     const u32x4 *tv = reinterpret_cast<const u32x4 *>(tile);
     const uint16_t *th = reinterpret_cast<const uint16_t *>(tile);
 #pragma unroll
     for (int g = 0; g < 4; g++)
-        t.sa[g] = th[si + 64u * g];
+        w.sa[g] = th[si + 64u * g];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-        // activation block of (h, lane), clamped into K (weights past K are zero)
-        const int blk = FULL ? s * 8 + 2 * ml.bn + h : min(s * 8 + 2 * ml.bn + h, nb - 1);
-#pragma unroll
-        for (int p = 0; p < MxTile<Q>::NP; p++) {
-            t.xr[h][p] = *reinterpret_cast<const u32x4 *>(xc.xq + (ml.xo[p] + 32u * (uint32_t)blk));
-            const float sxv = xc.xs[ml.mo[p] + (uint32_t)blk];
-            t.sx[h][p] = ml.lo[p] ? sxv : 0.0f;
-        }
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-            t.a[2 * g + h] = __builtin_nontemporal_load(tv + (ai + 64u * h + 16u * g));
+            w.a[2 * g + h] = __builtin_nontemporal_load(tv + (ai + 64u * h + 16u * g));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    return w;
+}
+
+// Activation block of (h, lane): s * 8 + 2 bn + h, clamped into K (the
+// weights past K are zero).
+template <int Q, bool FULL>
+__device__ __forceinline__ MxX<Q> load_mx_x(int s, int nb, const XCols<Q> &xc, const MxLane<Q> &ml)
+{
+    MxX<Q> x;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int blk = FULL ? s * 8 + 2 * ml.bn + h : min(s * 8 + 2 * ml.bn + h, nb - 1);
+#pragma unroll
+        for (int p = 0; p < MxX<Q>::NP; p++) {
+            x.xr[h][p] = *reinterpret_cast<const u32x4 *>(xc.xq + (ml.xo[p] + 32u * (uint32_t)blk));
+            const float sxv = xc.xs[ml.mo[p] + (uint32_t)blk];
+            x.sx[h][p] = ml.lo[p] ? sxv : 0.0f;
+        }
+    }
+    return x;
+}
+
+template <int Q>
+struct MxTile {
+    MxW w;
+    MxX<Q> x;
+};
+
+template <int Q, bool FULL>
+__device__ __forceinline__ MxTile<Q> load_mx_tile(const uint8_t *__restrict__ tile, int s, int nb, int lane,
+                                                  const XCols<Q> &xc, const MxLane<Q> &ml)
+{
+    MxTile<Q> t;
+    t.x = load_mx_x<Q, FULL>(s, nb, xc, ml);
+    t.w = load_mx_w(tile, lane);
     return t;
 }
 
@@ -187,26 +217,32 @@ __device__ __forceinline__ f32x4 mx_product(const u32x4 &a4, const i32x8 &b, uin
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 4, 0, H, (int)sa, 0, (int)sb);
 }
 
-// All eight (g, h) products of a tile, then per output the high part folded
-// into the low one and the fp32 block scale applied: acc[g][v] collects
-// row 16g + 4 (l / 16) + v of the lane's column (see MxLane).
-template <int Q>
-__device__ __forceinline__ void compute_mx_tile(const MxTile<Q> &t, const MxLane<Q> &ml, float (&acc)[4][4])
+// All eight (g, h) products of a tile for each of M weight matrices over
+// the same K range (one B operand per (half, pair) serves them all), then
+// per output the high part folded into the low one and the fp32 block scale
+// applied: acc[m][g][v] collects row 16g + 4 (l / 16) + v of the lane's
+// column (see MxLane).
+template <int Q, int M>
+__device__ __forceinline__ void compute_mx(const MxW (&w)[M], const MxX<Q> &x, const MxLane<Q> &ml,
+                                           float (&acc)[M][4][4])
 {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
 #pragma unroll
-        for (int p = 0; p < MxTile<Q>::NP; p++) {
-            const i32x8 b = build_b<Q>(t.xr[h][p], ml, p);
+        for (int p = 0; p < MxX<Q>::NP; p++) {
+            const i32x8 b = build_b<Q>(x.xr[h][p], ml, p);
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const f32x4 d = h == 0 ? mx_product<0>(t.a[2 * g], b, t.sa[g], ml.sb[p])
-                                       : mx_product<1>(t.a[2 * g + 1], b, t.sa[g], ml.sb[p]);
+            for (int m = 0; m < M; m++) {
 #pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const float hi = p == 0 ? high_part<0>(d[v]) : high_part<1>(d[v]);
-                    const float blk = d[v] + hi;
-                    acc[g][v] = fmaf(t.sx[h][p], blk, acc[g][v]);
+                for (int g = 0; g < 4; g++) {
+                    const f32x4 d = h == 0 ? mx_product<0>(w[m].a[2 * g], b, w[m].sa[g], ml.sb[p])
+                                           : mx_product<1>(w[m].a[2 * g + 1], b, w[m].sa[g], ml.sb[p]);
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        const float hi = p == 0 ? high_part<0>(d[v]) : high_part<1>(d[v]);
+                        const float blk = d[v] + hi;
+                        acc[m][g][v] = fmaf(x.sx[h][p], blk, acc[m][g][v]);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -214,11 +250,19 @@ __device__ __forceinline__ void compute_mx_tile(const MxTile<Q> &t, const MxLane
     }
 }
 
-// Quad sums (the four blocks of a half) and the per-row partials of every
-// column into red[(wave * Q + col) * 64 + row], the layout the GEMV
-// epilogue reads.
 template <int Q>
-__device__ __forceinline__ void mx_to_red(float (&acc)[4][4], float *red, int wave, int lane)
+__device__ __forceinline__ void compute_mx_tile(const MxTile<Q> &t, const MxLane<Q> &ml, float (&acc)[4][4])
+{
+    const MxW w[1] = {t.w};
+    float (&a1)[1][4][4] = reinterpret_cast<float (&)[1][4][4]>(acc);
+    compute_mx<Q, 1>(w, t.x, ml, a1);
+}
+
+// Quad sums (the four blocks of a half), then store(col, row, value) for
+// the lane's column and its rows 16g + 4 (l / 16) + v of the tile (one lane
+// per quad stores).
+template <int Q, typename Store>
+__device__ __forceinline__ void mx_rows(float (&acc)[4][4], int lane, Store store)
 {
     const int n = lane & 15, rq = lane >> 4, k = n >> 2;
     const int col = (k & 1) ? 2 + (k >> 1) : (k >> 1);
@@ -230,9 +274,17 @@ __device__ __forceinline__ void mx_to_red(float (&acc)[4][4], float *red, int wa
             s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
             s += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
             if ((n & 3) == 0 && col < Q)
-                red[(wave * Q + col) * 64 + 16 * g + 4 * rq + v] = s;
+                store(col, 16 * g + 4 * rq + v, s);
         }
     }
+}
+
+// The per-row partials of every column into red[(wave * Q + col) * 64 + row],
+// the layout the GEMV epilogue reads.
+template <int Q>
+__device__ __forceinline__ void mx_to_red(float (&acc)[4][4], float *red, int wave, int lane)
+{
+    mx_rows<Q>(acc, lane, [&](int col, int row, float v) { red[(wave * Q + col) * 64 + row] = v; });
 }
 
 } // namespace dev
