@@ -692,6 +692,24 @@ __device__ __forceinline__ void down_tile(const DTile<FD, NE> &t, int s, int nbI
         tile_blocks<FD, NE, NE, false>(t.w, s * 8, nbI, xc, ao);
 }
 
+// Wave 0: sum the W waves' partials of output row g * 64 + lane (fixed
+// order) and leave them in o for the combine.
+template <int NE>
+__device__ __forceinline__ void down_finish(const FfnArgs &a, const SlotCols<NE> &cols, int g, int lane, int W,
+                                            const float *red)
+{
+    const int row = g * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < NE; j++) {
+        float v = red[j * 64 + lane];
+        for (int w = 1; w < W; w++)
+            v += red[(w * kMaxDecodeQ + j) * 64 + lane];
+        if (row < a.H)
+            __hip_atomic_store(a.ws.o + (size_t)cols.out_idx[j] * a.H + row, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int FD, int NE>
 __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
 {
@@ -734,23 +752,52 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
             down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
         }
     }
-#define RED_D(w, j) red[((w) * kMaxDecodeQ + (j)) * 64 + lane]
 #pragma unroll
     for (int j = 0; j < NE; j++)
-        RED_D(wave, j) = ao[j];
+        red[(wave * kMaxDecodeQ + j) * 64 + lane] = ao[j];
     __syncthreads();
-    if (wave == 0) {
-        const int row = g * 64 + lane;
+    if (wave == 0)
+        down_finish<NE>(a, cols, g, lane, W, red);
+}
+
+// FP4 down with one or two tokens on the block-scaled matrix core
+// (rfx_mx4.h), one tile at a time (a workgroup of up to 1024 threads has
+// 128 registers per lane, and the waves mostly get one tile each).
+template <int NE>
+__device__ void down_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
+{
+    constexpr int TB = TileFmt<RFX_FP4>::bytes;
+    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const int nbI = a.I / 32;
+    XCols<NE> xc;
+    xc.xq = a.ws.hq;
+    xc.xs = a.ws.hs;
+    xc.xsum = a.ws.hsum;
 #pragma unroll
-        for (int j = 0; j < NE; j++) {
-            float v = RED_D(0, j);
-            for (int w = 1; w < W; w++)
-                v += RED_D(w, j);
-            if (row < a.H)
-                __hip_atomic_store(a.ws.o + (size_t)cols.out_idx[j] * a.H + row, v, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+    for (int j = 0; j < NE; j++) {
+        xc.xoff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)a.I;
+        xc.moff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)nbI;
     }
+    const int S = (a.I + 255) / 256;
+    const uint8_t *dm = si.kind == 2 ? a.sh_down : a.down + a.down_stride * (size_t)si.expert;
+    dm += (size_t)g * S * TB;
+    const MxLane<NE> ml = mx_lane<NE>(lane, xc);
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+            acc[i][v] = 0.0f;
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
+    for (int s = s_begin; s < s_end; s++) {
+        const MxTile<NE> t = load_mx_tile<NE, false>(dm + (size_t)s * TB, s, nbI, lane, xc, ml);
+        compute_mx_tile<NE>(t, ml, acc);
+    }
+    mx_rows<NE>(acc, lane, [&](int col, int row, float v) { red[(wave * kMaxDecodeQ + col) * 64 + row] = v; });
+    __syncthreads();
+    if (wave == 0)
+        down_finish<NE>(a, cols, g, lane, W, red);
 }
 
 template <int FD, int FSD>
@@ -764,18 +811,39 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
+    // FP4 with one or two tokens: the block-scaled matrix core
     if (si.kind == 2) {
         switch (ne) {
-        case 1: down_body<FSD, 1>(a, si, g, lane, wave, W, red); break;
-        case 2: down_body<FSD, 2>(a, si, g, lane, wave, W, red); break;
+        case 1:
+            if constexpr (FSD == RFX_FP4)
+                down_body_mx<1>(a, si, g, lane, wave, W, red);
+            else
+                down_body<FSD, 1>(a, si, g, lane, wave, W, red);
+            break;
+        case 2:
+            if constexpr (FSD == RFX_FP4)
+                down_body_mx<2>(a, si, g, lane, wave, W, red);
+            else
+                down_body<FSD, 2>(a, si, g, lane, wave, W, red);
+            break;
         case 3: down_body<FSD, 3>(a, si, g, lane, wave, W, red); break;
         case 4: down_body<FSD, 4>(a, si, g, lane, wave, W, red); break;
         default: break;
         }
     } else {
         switch (ne) {
-        case 1: down_body<FD, 1>(a, si, g, lane, wave, W, red); break;
-        case 2: down_body<FD, 2>(a, si, g, lane, wave, W, red); break;
+        case 1:
+            if constexpr (FD == RFX_FP4)
+                down_body_mx<1>(a, si, g, lane, wave, W, red);
+            else
+                down_body<FD, 1>(a, si, g, lane, wave, W, red);
+            break;
+        case 2:
+            if constexpr (FD == RFX_FP4)
+                down_body_mx<2>(a, si, g, lane, wave, W, red);
+            else
+                down_body<FD, 2>(a, si, g, lane, wave, W, red);
+            break;
         case 3: down_body<FD, 3>(a, si, g, lane, wave, W, red); break;
         case 4: down_body<FD, 4>(a, si, g, lane, wave, W, red); break;
         default: break;
