@@ -862,18 +862,37 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
         return;
     const int row = g * 64 + lane;
     if (wave == 0 && row < a.H) {
-        for (int t = 0; t < a.q; t++) {
-            float acc = a.has_shared ? __hip_atomic_load(a.ws.o + (size_t)(a.q * a.k + t) * a.H + row,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                     : 0.0f;
-            if (a.resid)
-                acc = a.resid[(size_t)t * a.H + row] + acc;
-            for (int j = 0; j < a.k; j++) {
-                const float w = a.topk_w[t * a.k + j];
-                const float ov = __hip_atomic_load(a.ws.o + (size_t)(t * a.k + j) * a.H + row,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                acc += w * ov;
+        // every load issued before the first sum (one round trip, not one
+        // per pair), then the sums in the fixed order
+        float os[kMaxDecodeQ], rs[kMaxDecodeQ], ov[kMaxDecodeQ][kMaxK];
+#pragma unroll
+        for (int t = 0; t < kMaxDecodeQ; t++) {
+            os[t] = 0.0f;
+            rs[t] = 0.0f;
+            if (t < a.q) {
+                if (a.has_shared)
+                    os[t] = __hip_atomic_load(a.ws.o + (size_t)(a.q * a.k + t) * a.H + row, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                if (a.resid)
+                    rs[t] = a.resid[(size_t)t * a.H + row];
             }
+#pragma unroll
+            for (int j = 0; j < kMaxK; j++)
+                ov[t][j] = t < a.q && j < a.k ? __hip_atomic_load(a.ws.o + (size_t)(t * a.k + j) * a.H + row,
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                              : 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < kMaxDecodeQ; t++) {
+            if (t >= a.q)
+                break;
+            float acc = os[t];
+            if (a.resid)
+                acc = rs[t] + acc;
+#pragma unroll
+            for (int j = 0; j < kMaxK; j++)
+                if (j < a.k)
+                    acc += a.topk_w[t * a.k + j] * ov[t][j];
             a.y[(size_t)t * a.H + row] = acc;
         }
     }
