@@ -301,8 +301,11 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 }
 
 // ------------------------------------------------------------------
-// Slot plan: slot i < n_active is the i-th expert (in id order) that has
-// pairs; slot n_active is the shared expert (when present).
+// Slot plan: slot 0 is the shared expert (when present), then the routed
+// experts that have pairs, in id order. The FFN grids are (row group,
+// slot) with the row group fastest, so the shared expert (the slot with
+// the most tokens and, for sensitive layers, the heaviest format) is
+// dispatched first.
 // ------------------------------------------------------------------
 struct SlotInfo {
     int kind;   // 0 = none, 1 = routed expert, 2 = shared expert
@@ -327,19 +330,20 @@ __device__ __forceinline__ SlotInfo find_slot(int slot, const int32_t *__restric
             lo[r] = expert_off[e];
             hi[r] = expert_off[min(e + 1, E)];
         }
+        const int rslot = has_shared ? slot - 1 : slot; // routed rank (-1: the shared slot)
         int total = 0, found_r = -1;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const bool act = (lane + 64 * r) < E && hi[r] > lo[r];
             const unsigned long long bal = __ballot(act);
             const int rank = total + __popcll(bal & ((1ull << lane) - 1ull));
-            if (act && rank == slot)
+            if (act && rank == rslot)
                 found_r = r;
             total += __popcll(bal);
         }
         if (lane == 0) {
             s_info.n_slots = total + (has_shared ? 1 : 0);
-            s_info.kind = (has_shared && slot == total) ? 2 : 0;
+            s_info.kind = (has_shared && slot == 0) ? 2 : 0;
             s_info.expert = -1;
             s_info.pb = s_info.pe = 0;
         }
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
     __shared__ float red[8 * 2 * kMaxDecodeQ * 64];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const SlotInfo si = find_slot(blockIdx.x, a.expert_off, a.E, a.has_shared);
+    const SlotInfo si = find_slot(blockIdx.y, a.expert_off, a.E, a.has_shared);
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
@@ -628,36 +632,36 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
         switch (ne) {
         case 1:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<1>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red);
             else
-                gateup_body<FS, 1>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body<FS, 1>(a, si, blockIdx.x, lane, wave, W, red);
             break;
         case 2:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<2>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red);
             else
-                gateup_body<FS, 2>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body<FS, 2>(a, si, blockIdx.x, lane, wave, W, red);
             break;
-        case 3: gateup_body<FS, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
-        case 4: gateup_body<FS, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 3: gateup_body<FS, 3>(a, si, blockIdx.x, lane, wave, W, red); break;
+        case 4: gateup_body<FS, 4>(a, si, blockIdx.x, lane, wave, W, red); break;
         default: break;
         }
     } else {
         switch (ne) {
         case 1:
             if constexpr (FG == RFX_FP4)
-                gateup_body_mx<1>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red);
             else
-                gateup_body<FG, 1>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body<FG, 1>(a, si, blockIdx.x, lane, wave, W, red);
             break;
         case 2:
             if constexpr (FG == RFX_FP4)
-                gateup_body_mx<2>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red);
             else
-                gateup_body<FG, 2>(a, si, blockIdx.y, lane, wave, W, red);
+                gateup_body<FG, 2>(a, si, blockIdx.x, lane, wave, W, red);
             break;
-        case 3: gateup_body<FG, 3>(a, si, blockIdx.y, lane, wave, W, red); break;
-        case 4: gateup_body<FG, 4>(a, si, blockIdx.y, lane, wave, W, red); break;
+        case 3: gateup_body<FG, 3>(a, si, blockIdx.x, lane, wave, W, red); break;
+        case 4: gateup_body<FG, 4>(a, si, blockIdx.x, lane, wave, W, red); break;
         default: break;
         }
     }
@@ -806,8 +810,8 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
     __shared__ float red[16 * kMaxDecodeQ * 64];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const int g = blockIdx.y;
-    const SlotInfo si = find_slot(blockIdx.x, a.expert_off, a.E, a.has_shared);
+    const int g = blockIdx.x;
+    const SlotInfo si = find_slot(blockIdx.y, a.expert_off, a.E, a.has_shared);
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
@@ -1093,7 +1097,7 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     const int SH = (int)ceil_div(L->hidden, 256), SI = (int)ceil_div(L->inter, 256);
     {
         const int W = waves_for(max_slots * GI, SH, 8);
-        dim3 grid(max_slots, GI), block(64 * W);
+        dim3 grid(GI, max_slots), block(64 * W);
         switch (a.fmt_g) {
         case RFX_FP2: st = launch_gateup<RFX_FP2>(a.fmt_sg, a, grid, block, s); break;
         case RFX_FP3: st = launch_gateup<RFX_FP3>(a.fmt_sg, a, grid, block, s); break;
@@ -1104,7 +1108,7 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     }
     {
         const int W = waves_for(max_slots * GH, SI, 16);
-        dim3 grid(max_slots, GH), block(64 * W);
+        dim3 grid(GH, max_slots), block(64 * W);
         switch (a.fmt_d) {
         case RFX_FP2: st = launch_down<RFX_FP2>(a.fmt_sd, a, grid, block, s); break;
         case RFX_FP3: st = launch_down<RFX_FP3>(a.fmt_sd, a, grid, block, s); break;
