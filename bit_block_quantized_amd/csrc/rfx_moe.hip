@@ -518,8 +518,15 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
     const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
     const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
     // two buffers per stream used in turn: tile s + 1 in flight while s is
-    // computed, with no register copies (which would wait for the loads)
-    if (s_begin < s_end) {
+    // computed, with no register copies (which would wait for the loads).
+    // FP4 tiles take one buffer: their registers set the kernel's budget,
+    // and two would halve the workgroups resident per CU.
+    if (FG == RFX_FP4) {
+        for (int s = s_begin; s < s_end; s++) {
+            const GUTile<FG, NE> t = load_gu<FG, NE>(gm, um, s, nbH, xc, lane);
+            gateup_tile<FG, NE>(t, s, nbH, xc, ag, au);
+        }
+    } else if (s_begin < s_end) {
         GUTile<FG, NE> ta = load_gu<FG, NE>(gm, um, s_begin, nbH, xc, lane), tb;
         for (int s = s_begin; s < s_end; s += 2) {
             if (s + 1 < s_end)
@@ -546,8 +553,8 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
 // FP4 gate and up with one or two tokens on the block-scaled matrix core
 // (rfx_mx4.h): both matrices' products take the same activation operand,
 // built once per (half, column pair). Same tile split, reduction and
-// epilogue as gateup_body.
-template <int NE>
+// epilogue as gateup_body. SINGLE: one tile buffer (see gateup_body).
+template <int NE, bool SINGLE = true>
 __device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
 {
     constexpr int TB = TileFmt<RFX_FP4>::bytes;
@@ -584,7 +591,15 @@ __device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int 
                 acc[m][i][v] = 0.0f;
     const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
     const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
-    if (s_begin < s_end) {
+    if (SINGLE) {
+        for (int s = s_begin; s < s_end; s++) {
+            const MxX<NE> x = load_mx_x<NE, false>(s, nbH, xc, ml);
+            MxW w[2];
+            w[0] = load_mx_w(gm + (size_t)s * TB, lane);
+            w[1] = load_mx_w(um + (size_t)s * TB, lane);
+            compute_mx<NE, 2>(w, x, ml, acc);
+        }
+    } else if (s_begin < s_end) {
         // two buffers used in turn: tile s + 1 in flight while s is computed
         MxW wa[2], wb[2];
         MxX<NE> xa = load_mx_x<NE, false>(s_begin, nbH, xc, ml), xb;
