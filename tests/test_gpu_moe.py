@@ -90,6 +90,26 @@ def test_moe_small(q, shared, bias):
     _check_layer(spec, gpu, x, 4, orc)
 
 
+@pytest.mark.parametrize("fmts", [(4, 4, 2), (3, 2, 3), (4, 3, 4)])
+@pytest.mark.parametrize("q", [1, 2, 4])
+def test_moe_other_formats(fmts, q):
+    """Other format assignments (gate/up, down, shared): FP4 routed experts
+    (their one- and two-token slots take the block-scaled matrix core for
+    gate/up and down), FP2 / FP3 shared experts (the vector paths for the
+    shared slot), with experts picked by several tokens."""
+    torch = need_gpu()
+    fg, fd, fs = fmts
+    say(f"moe formats gate/up FP{fg} down FP{fd} shared FP{fs} q={q}")
+    spec = LayerSpec(layer=7, hidden=512, inter=320, n_experts=8, shared=True,
+                     fmt_gate=fg, fmt_down=fd, fmt_shared=fs)
+    spec.router_b = np.array([6, 0, 5, 0, 0, 0, 0, 0], np.float32)  # experts 0, 2 for most tokens
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    x = inputgen.tokens(7, 20 + q, q, spec.hidden)
+    gpu = _run_layer(torch, spec, dev, x, k=3)
+    _check_layer(spec, gpu, x, 3, orc)
+
+
 def test_moe_shared_token_experts_and_k_edges():
     """Tokens that pick the same experts (one expert decoded for several
     tokens), k = 1 and k = 8, and more pairs than experts."""

@@ -131,6 +131,22 @@ def test_prefill_small(q, k, shared, bias):
     _check_all(spec, gpu, x, k, orc)
 
 
+@pytest.mark.parametrize("fmts", [(4, 4, 2), (3, 2, 3)])
+def test_prefill_other_formats(fmts):
+    """Other format assignments (gate/up, down, shared) through the prefill
+    kernels' codebook expansion: FP4 routed experts, FP2 / FP3 shared."""
+    torch = need_gpu()
+    fg, fd, fs = fmts
+    say(f"prefill formats gate/up FP{fg} down FP{fd} shared FP{fs}")
+    spec = LayerSpec(layer=11, hidden=512, inter=320, n_experts=8, shared=True,
+                     fmt_gate=fg, fmt_down=fd, fmt_shared=fs)
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    x = inputgen.tokens(11, 0, 40, spec.hidden)
+    gpu = _run(torch, spec, dev, x, 3)
+    _check_all(spec, gpu, x, 3, orc)
+
+
 def test_prefill_partial_tiles_and_residual():
     """hidden = 288 (gate/up K ends in a partial tile; the down output's last
     row group is half full), inter = 320, residual fused into the combine."""
