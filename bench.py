@@ -323,6 +323,54 @@ def hbm_reference(torch):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def hbm_read_reference(torch, R):
+    """A 4 GiB streaming read with the GEMV kernels' load form
+    (rfx_read_reference, 32768 workgroups of 256 threads, the best of a
+    1024..32768 sweep): bytes read / time."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    out = torch.empty(32768, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        R.read_reference(a, out)
+    ms = time_eager(torch, lambda i: R.read_reference(a, out), 10)
+    del a, out
+    return 4 * n / (ms * 1e-3) / 1e9
+
+
+def bench_config1(torch, R, inputgen, reps):
+    """FP4 1024 x 1024, q = 1 (W seed 0, x seed 1): microseconds per call
+    (0.56 MB stays in L2, so the time is launch and latency), and the same
+    call over 1024 distinct copies (570 MB) back to back for a rate."""
+    n = 1024
+    W = inputgen.dense_weight(n, n, seed=0)
+    tiled = R.quantize_matrix(4, W)
+    nbytes = tiled.nbytes
+    copies = 1024
+    base = torch.empty(copies * nbytes, dtype=torch.uint8, device="cuda")
+    one = torch.from_numpy(tiled).cuda()
+    for c in range(copies):
+        base[c * nbytes:(c + 1) * nbytes].copy_(one)
+    mats = [R.DeviceQMat(4, n, n, base[c * nbytes:(c + 1) * nbytes]) for c in range(copies)]
+    x = torch.from_numpy(inputgen.activations(1, n, seed=1)).cuda()
+    xq = torch.empty((1, n), dtype=torch.int8, device="cuda")
+    xs = torch.empty((1, n // 32), dtype=torch.float32, device="cuda")
+    xsum = torch.empty((1, n // 32), dtype=torch.int32, device="cuda")
+    R.quantize_act(x, xq, xs, xsum)
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(R.gemv_workspace_bytes(mats[0], 1), 256), dtype=torch.uint8, device="cuda")
+    g = graph_of(torch, lambda i: R.gemv(mats[0], xq, xs, xsum, 1, y, ws), 32)
+    us_one = time_graph(torch, g, reps) * 1e3 / 32
+    del g
+    g = graph_of(torch, lambda i: R.gemv(mats[i], xq, xs, xsum, 1, y, ws), copies)
+    us_rot = time_graph(torch, g, 3) * 1e3 / copies
+    del g, base, mats
+    w, a, _ = algorithmic_bytes(R, 4, 1, n=n, k=n)
+    return {"workload": "FP4 1024x1024 q=1, W seed 0, x seed 1", "us_per_call": round(us_one, 3),
+            "rotated_1024_copies": {"us_per_call": round(us_rot, 3),
+                                    "GBps": round((w + a) / (us_rot * 1e-6) / 1e9, 1)},
+            "bytes_per_call": w + a}
+
+
 def cpu_baseline(R, work, rows=N, repeats=8):
     """The CPU oracle on a bounded sample: the first `rows` rows of every
     matrix, all six (format, q) products, `repeats` times, one thread."""
@@ -480,6 +528,12 @@ def main():
     }
     del work
     torch.cuda.empty_cache()
+    out["config1"] = bench_config1(torch, R, inputgen, args.kernel_reps)
+    log(f"config 1: {out['config1']}")
+    torch.cuda.empty_cache()
+    props = torch.cuda.get_device_properties(0)
+    out["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "cus": props.multi_processor_count, "hip": torch.version.hip}
     if args.moe_layers > 0:
         layers = build_moe_layers(torch, R, inputgen, args.moe_layers)
         out["moe"] = bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))
@@ -488,6 +542,7 @@ def main():
         torch.cuda.empty_cache()
     try:
         out["hbm_copy_GBps"] = round(hbm_reference(torch), 1)
+        out["hbm_read_GBps"] = round(hbm_read_reference(torch, R), 1)
     except Exception as e:  # pragma: no cover
         out["hbm_copy_GBps"] = f"failed: {e}"
     if not args.no_cpu_baseline:

@@ -85,6 +85,7 @@ _SIGS = {
     "rfx_gemv_grouped_workspace_bytes": ([_P, _I], _SZ),
     "rfx_gemv_grouped": ([_P, _I, _P, _SZ, _P], _I),
     "rfx_debug_block_dots": ([_P, _P, _P, _I, _P, _P], _I),
+    "rfx_read_reference": ([_P, _SZ, _P, _I, _P], _I),
     "rfx_moe_workspace_bytes": ([_P, _I, _I], _SZ),
     "rfx_moe_route_topk": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_moe_ffn": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
@@ -281,6 +282,13 @@ def gemv_grouped(jobs, ws=None, stream=None):
 def debug_block_dots(W: DeviceQMat, xq, xsum, q, dots, stream=None):
     _check(lib().rfx_debug_block_dots(W.ref(), _dptr(xq), _dptr(xsum), q, _dptr(dots),
                                       _stream(stream)))
+
+
+def read_reference(buf, out, stream=None):
+    """Measurement aid: stream `buf` (a device tensor) once; out (int32 or
+    uint32 device tensor) gets one XOR fold per workgroup."""
+    _check(lib().rfx_read_reference(_dptr(buf), buf.numel() * buf.element_size(), _dptr(out), out.numel(),
+                                    _stream(stream)))
 
 
 # ------------------------------------------------------------------ MoE

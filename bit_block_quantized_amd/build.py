@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "librfx.so")
 
-SOURCES = ["rfx_host.cpp", "rfx_gemv.hip", "rfx_moe.hip", "rfx_prefill.hip"]
+SOURCES = ["rfx_host.cpp", "rfx_gemv.hip", "rfx_moe.hip", "rfx_prefill.hip", "rfx_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

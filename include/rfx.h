@@ -209,6 +209,15 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
 int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,
                          int32_t *dots, void *stream);
 
+/* Measurement aid (not part of the method): reads `bytes` (a positive
+ * multiple of 16; buf 16-B aligned, device) once with the nontemporal
+ * 16-byte loads the GEMV kernels use, XOR-folding every 32-bit word, over
+ * n_out workgroups (1..2^20) of 256 threads; workgroup i writes its fold to
+ * out[i] (device, n_out words), so the XOR of out[0..n_out) is the XOR of
+ * all the buffer's words. Its time gives the HBM read rate for that load
+ * form. Errors: RFX_E_INVAL / RFX_E_ALIGN before any HIP call. */
+int rfx_read_reference(const void *buf, size_t bytes, uint32_t *out, int n_out, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* MoE layer: decode (q <= 4 tokens) and prefill (q > 4).               */
 /* ------------------------------------------------------------------ */

@@ -167,6 +167,23 @@ def test_gemv_fp2m_offset_rows(q):
         assert rel_err(y, yo) <= TOL, (split, rel_err(y, yo))
 
 
+def test_read_reference_folds_every_word():
+    """The streaming-read reference (a measurement aid) reads every word:
+    the XOR of its per-workgroup folds equals numpy's XOR of the buffer,
+    including a size that leaves a remainder after the 4-load loop."""
+    torch = need_gpu()
+    say("read reference")
+    rng = np.random.default_rng(3)
+    for n_words, n_out in ((4 * 1000, 7), (4 * 65537, 64), (1 << 22, 512)):
+        host = rng.integers(0, 2 ** 32, n_words, dtype=np.uint64).astype(np.uint32)
+        buf = torch.from_numpy(host.view(np.int32)).cuda()
+        out = torch.zeros(n_out, dtype=torch.int32, device="cuda")
+        R.read_reference(buf, out)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), (n_words, n_out)
+
+
 # ---------------------------------------------------------- grouped gemv
 
 def _grouped(torch, specs, seed, big=False):

@@ -234,6 +234,17 @@ def test_moe_rejects_the_gemv_only_variant():
     assert st == -4
 
 
+def test_read_reference_validation_without_gpu():
+    L = R.lib()
+    good = 0x7f0000000000
+    f = _fake(good)
+    assert L.rfx_read_reference(None, 64, f, 1, None) == -1
+    assert L.rfx_read_reference(_fake(good + 8), 64, f, 1, None) == -2
+    assert L.rfx_read_reference(f, 40, f, 1, None) == -1
+    assert L.rfx_read_reference(f, 0, f, 1, None) == -1
+    assert L.rfx_read_reference(f, 64, f, 0, None) == -1
+
+
 def test_status_strings():
     L = R.lib()
     for st in (0, -1, -2, -3, -4, -5, -6):
