@@ -36,7 +36,10 @@ FORMATS = (FP2, FP3, FP4)
 # Variant with a scale and a minimum per block (weight = s * c + m, 12 B):
 # the pages let a block carry a second small value; this one is a reading.
 FP2M = 12
-VARIANT_FORMATS = (FP2M,)
+# A tier above FP4 (the same paragraph keeps dense and sensitive
+# projections at FP4 or higher): 32 int8 codes + an fp16 scale, 34 B.
+Q8 = 8
+VARIANT_FORMATS = (FP2M, Q8)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "liboracle.so")

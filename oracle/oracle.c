@@ -42,6 +42,12 @@
  * reading, not one of the three named formats):
  *   FP2M: the FP2 code bytes + fp16 scale s + fp16 minimum m = 12 bytes
  *         (3.0 bits per weight); weight = s * c + m, c in 0..3.
+ *
+ * A tier above FP4 for the dense and sensitive projections (the same
+ * paragraph keeps those at FP4 "or higher" without naming a format; this
+ * tier is a reading):
+ *   Q8:   32 int8 codes in weight order + fp16 scale = 34 bytes
+ *         (8.5 bits per weight); weight = s * c, c in -127..127.
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,6 +58,7 @@
 #define ORC_FP3 3
 #define ORC_FP4 4
 #define ORC_FP2M 12
+#define ORC_Q8 8
 
 #define ORC_OK 0
 #define ORC_E_INVAL (-1)
@@ -65,6 +72,7 @@ int orc_block_bytes(int fmt)
     case ORC_FP3: return 14;
     case ORC_FP4: return 17;
     case ORC_FP2M: return 12; /* Reading: 8 code bytes + two fp16 values */
+    case ORC_Q8: return 34;   /* Reading: 32 int8 codes + an fp16 scale */
     }
     return ORC_E_INVAL;
 }
@@ -76,6 +84,7 @@ int orc_code_bytes(int fmt)
     case ORC_FP3: return 12;
     case ORC_FP4: return 16;
     case ORC_FP2M: return 8;
+    case ORC_Q8: return 32;
     }
     return ORC_E_INVAL;
 }
@@ -159,13 +168,14 @@ int orc_codebook(int fmt, int code)
     case ORC_FP3: return 2 * code - 7;
     case ORC_FP4: return (code & 8) ? -fp4_mag[code & 7] : fp4_mag[code & 7];
     case ORC_FP2M: return code;
+    case ORC_Q8: return (int)(int8_t)(uint8_t)code; /* the byte as two's complement */
     }
     return 0;
 }
 
 static int n_codes(int fmt)
 {
-    return fmt == ORC_FP2 || fmt == ORC_FP2M ? 4 : fmt == ORC_FP3 ? 8 : 16;
+    return fmt == ORC_FP2 || fmt == ORC_FP2M ? 4 : fmt == ORC_FP3 ? 8 : fmt == ORC_Q8 ? 256 : 16;
 }
 
 /* Nearest codebook value to t, by brute force over every code.
@@ -183,6 +193,8 @@ int orc_nearest_code(int fmt, double t)
     for (int c = 0; c < n_codes(fmt); c++) {
         if (fmt == ORC_FP4 && c == 8)
             continue; /* -0 is never emitted */
+        if (fmt == ORC_Q8 && c == 0x80)
+            continue; /* -128 is never emitted: the codes are symmetric */
         if (best < 0) {
             best = c;
             continue;
@@ -195,6 +207,9 @@ int orc_nearest_code(int fmt, double t)
         } else if (t == mid) { /* exact tie between c and best */
             if (fmt == ORC_FP4) {
                 if (((c & 7) % 2) == 0)
+                    best = c;
+            } else if (fmt == ORC_Q8) {
+                if ((v & 1) == 0) /* half to even, as the activations */
                     best = c;
             } else if (abs(v) > abs(vb) || (abs(v) == abs(vb) && v > vb)) {
                 best = c;
@@ -241,6 +256,8 @@ void orc_unpack_codes(int fmt, const uint8_t *blk, int *codes)
             int ih = t / 4, jh = t % 4;
             int hi = (int)((rd32(blk + 8) >> (8 * jh + ih)) & 1u);
             codes[t] = lo | (hi << 2);
+        } else if (fmt == ORC_Q8) {
+            codes[t] = blk[t]; /* byte t is weight t */
         } else {
             int m = t / 8, r = t % 8, i = r / 4, j = r % 4;
             codes[t] = (int)((rd32(blk + 4 * m) >> (8 * j + 4 * i)) & 15u);
@@ -250,6 +267,11 @@ void orc_unpack_codes(int fmt, const uint8_t *blk, int *codes)
 
 void orc_pack_codes(int fmt, const int *codes, uint8_t *blk)
 {
+    if (fmt == ORC_Q8) {
+        for (int t = 0; t < 32; t++)
+            blk[t] = (uint8_t)codes[t];
+        return;
+    }
     uint32_t w[4] = {0, 0, 0, 0};
     for (int t = 0; t < 32; t++) {
         if (fmt == ORC_FP2 || fmt == ORC_FP2M) {
@@ -372,6 +394,24 @@ int orc_quantize_block(int fmt, const float *w, uint8_t *blk)
         }
         orc_pack_codes(fmt, codes, blk);
         blk[cb] = (uint8_t)E;
+        return ORC_OK;
+    }
+    if (fmt == ORC_Q8) {
+        /* Reading: s = fp16(amax / 127), the division in fp32; code = the
+         * int8 value nearest to w / s in fp32, ties to even, within
+         * -127..127; s = 0 gives code 0. */
+        uint16_t q16 = orc_f32_to_f16(amax / 127.0f);
+        if ((q16 & 0x7fff) == 0x7c00)
+            return ORC_E_RANGE;
+        float qs = (float)orc_f16_to_f64(q16);
+        for (int t = 0; t < 32; t++) {
+            double r = qs == 0.0f ? 0.0 : rint((double)(w[t] / qs)); /* half to even */
+            r = r > 127.0 ? 127.0 : r < -127.0 ? -127.0 : r;
+            codes[t] = (int)(uint8_t)(int8_t)(int)r; /* stored as the byte */
+        }
+        orc_pack_codes(fmt, codes, blk);
+        blk[cb] = (uint8_t)(q16 & 0xff);
+        blk[cb + 1] = (uint8_t)(q16 >> 8);
         return ORC_OK;
     }
     float cmax = (fmt == ORC_FP2) ? 3.0f : 7.0f;

@@ -422,3 +422,83 @@ def test_fp2m_range_errors():
     w[0] = np.nan
     with pytest.raises(O.OracleError):
         O.quantize_block(FP2M, w)
+
+
+# ------------------------------------------------------ Q8 (the int8 tier)
+# 32 int8 codes + an fp16 scale; weight = s * c.
+
+Q8 = O.Q8
+
+
+def test_q8_sizes_and_codebook():
+    assert O.block_bytes(Q8) == 34 and O.code_bytes(Q8) == 32
+    assert [O.codebook(Q8, c) for c in (0, 1, 127, 0x81, 0xFF, 0x80)] == [0, 1, 127, -127, -1, -128]
+
+
+def test_q8_nearest_code_is_clamped_round_half_even():
+    """The brute-force argmin over the 255 codes (never -128) equals the
+    plain definition the encoder writes out: clamp(rint(t), -127, 127)."""
+    rng = np.random.default_rng(9)
+    ts = list(rng.uniform(-140, 140, 3000)) + [k + 0.5 for k in range(-130, 130)] + [127.6, -127.6, 300.0, -0.0]
+    for t in ts:
+        c = O.nearest_code(Q8, float(t))
+        assert c != 0x80
+        want = int(np.clip(np.rint(t), -127, 127))
+        assert O.codebook(Q8, c) == want, t
+
+
+def test_q8_scale_codes_and_error_bound():
+    for w in _random_blocks(80) + [np.zeros(32, np.float32), np.full(32, -3e-7, np.float32)]:
+        blk = O.quantize_block(Q8, w)
+        amax = np.float32(np.max(np.abs(w)))
+        s = np.float32(np.float16(amax / np.float32(127.0)))
+        assert O.block_scale(Q8, blk) == float(s)
+        codes = np.array([O.codebook(Q8, c) for c in O.unpack_codes(Q8, blk)])
+        if s == 0:
+            assert np.all(codes == 0)
+            continue
+        want = np.clip(np.rint((w / s).astype(np.float64)), -127, 127)  # w / s in fp32
+        assert np.array_equal(codes, want)
+        d = O.dequantize_block(Q8, blk)
+        err = np.abs(w.astype(np.float64) - d)
+        assert np.all(err <= 0.5 * float(s) + abs(float(amax) - 127 * float(s)) + 1e-7 * float(amax))
+
+
+def test_q8_power_of_two_equivariance():
+    for w in _random_blocks(81, 100):
+        b = O.quantize_block(Q8, w)
+        s = O.block_scale(Q8, b)
+        for k in (-3, 2):
+            # both scales normal fp16 (a subnormal one has fewer bits)
+            if not (s == 0 or (6.2e-5 < s < 6.0e4 and 6.2e-5 < s * 2.0 ** k < 6.0e4)):
+                continue
+            bk = O.quantize_block(Q8, (w * np.float32(2.0 ** k)).astype(np.float32))
+            assert np.array_equal(O.unpack_codes(Q8, bk), O.unpack_codes(Q8, b))
+            assert O.block_scale(Q8, bk) == s * 2.0 ** k
+
+
+def test_q8_gemv_is_the_dequantized_product():
+    rng = np.random.default_rng(82)
+    N, K, Q = 6, 128, 3
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    blocks = O.quantize_matrix(Q8, W)
+    x = rng.standard_normal((Q, K)).astype(np.float32)
+    xq, xs = O.quantize_act(x)
+    y, dots = O.gemv(Q8, blocks, xq, xs, want_dots=True)
+    Wd = O.dequantize_matrix(Q8, blocks)
+    xd = xq.astype(np.float64) * np.repeat(xs.astype(np.float64), 32, axis=1)
+    assert np.allclose(y, xd @ Wd.T, rtol=1e-12, atol=1e-12)
+    vals = np.array([[[O.codebook(Q8, c) for c in O.unpack_codes(Q8, blocks[n, b])] for b in range(K // 32)]
+                     for n in range(N)])
+    for j in range(Q):
+        assert np.array_equal(dots[j], (vals * xq[j].reshape(1, K // 32, 32)).sum(-1))
+
+
+def test_q8_range_errors():
+    w = np.zeros(32, np.float32)
+    w[3] = np.float32(1e7)  # fp16 scale overflow
+    with pytest.raises(O.OracleError):
+        O.quantize_block(Q8, w)
+    w[3] = np.inf
+    with pytest.raises(O.OracleError):
+        O.quantize_block(Q8, w)
