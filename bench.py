@@ -20,8 +20,9 @@ Extra fields: per-kernel timings, the MoE decode layer (256 experts, hidden
 4096, intermediate 2048, FP2 gate/up, FP3 down, FP4 shared, q = 4, top-6)
 and the 8-layer stack (top-4, Zipf(1.1) router bias, q = 1 and q = 4), the
 HBM copy reference and the CPU oracle on a bounded sample. The FP2M
-variant (fp16 scale + fp16 minimum, 12 B / 32 weights, seed 30) is timed
-per kernel beside the named formats; it is not part of the step.
+variant (fp16 scale + fp16 minimum, 12 B / 32 weights, seed 30) and the Q8
+tier (int8 codes + fp16 scale, 34 B, seed 40) are timed per kernel beside
+the named formats; they are not part of the step.
 
 Prints one JSON line. Only one GPU is supported.
 """
@@ -40,9 +41,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 N = K = 7168
 FORMATS = (2, 3, 4)
-VARIANTS = (12,)  # FP2M: timed per kernel, not part of the step
-SEEDS = {2: 0, 3: 10, 4: 20, 12: 30}
-FMT_NAME = {2: "FP2", 3: "FP3", 4: "FP4", 12: "FP2M"}
+VARIANTS = (12, 8)  # FP2M and Q8: timed per kernel, not part of the step
+SEEDS = {2: 0, 3: 10, 4: 20, 12: 30, 8: 40}
+FMT_NAME = {2: "FP2", 3: "FP3", 4: "FP4", 12: "FP2M", 8: "Q8"}
 LLC_BYTES = 256 << 20
 MOE_H, MOE_I, MOE_E = 4096, 2048, 256
 
@@ -473,7 +474,7 @@ def main():
     # whole step: the six GEMVs as one grouped launch (the headline) and,
     # for comparison, as six launches back to back; one graph holds `rot`
     # steps
-    assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per if p["fmt"] != "FP2M")
+    assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per if p["fmt"] in ("FP2", "FP3", "FP4"))
     rot = len(garrs)
 
     def step_six(i):

@@ -21,7 +21,9 @@ FORMATS = (FP2, FP3, FP4)
 # Variant: fp16 scale and fp16 minimum per block (weight = s * c + m),
 # GEMV entry points only.
 FP2M = 12
-VARIANT_FORMATS = (FP2M,)
+# A tier above FP4: 32 int8 codes + an fp16 scale (34 B), GEMV entry points only.
+Q8 = 8
+VARIANT_FORMATS = (FP2M, Q8)
 
 RFX_OK = 0
 _STATUS = {-1: "RFX_E_INVAL", -2: "RFX_E_ALIGN", -3: "RFX_E_RANGE", -4: "RFX_E_UNSUPPORTED",

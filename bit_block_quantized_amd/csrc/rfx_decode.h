@@ -32,8 +32,12 @@ __device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p) { return (sptr_
 
 template <int FMT>
 struct TileFmt {
-    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : FMT == RFX_FP2M ? 6144 : 8704;
-    static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M ? 4 : FMT == RFX_FP3 ? 6 : 8;
+    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : FMT == RFX_FP2M ? 6144
+                               : FMT == RFX_Q8 ? 17408 : 8704;
+    static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M ? 4 : FMT == RFX_FP3 ? 6
+                                     : FMT == RFX_Q8 ? 16 : 8;
+    // the activation block sums enter the result (codebook offset or minimum)
+    static constexpr bool needs_sum = FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP2M;
 };
 
 // ------------------------------------------------------------------
@@ -127,7 +131,7 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
 template <int FMT>
 struct TileRegs {
     u32x4 c[TileFmt<FMT>::code_chunks];
-    u32x4 sc16; // FP2/FP3/FP2M: eight fp16 scales
+    u32x4 sc16; // FP2/FP3/FP2M/Q8: eight fp16 scales
     u32x4 mn16; // FP2M: eight fp16 minima
     u32x2 sc8;  // FP4: eight e8m0 bytes
 };
@@ -150,6 +154,11 @@ __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ t
         RFX_LD(t.sc8, reinterpret_cast<const u32x2 *>(tile + 8 * 1024) + lane);
 #pragma unroll
         for (int k = 0; k < 8; k++)
+            RFX_LD(t.c[k], tp + 64 * k);
+    } else if (FMT == RFX_Q8) {
+        RFX_LD(t.sc16, tp + 64 * 16);
+#pragma unroll
+        for (int k = 0; k < 16; k++)
             RFX_LD(t.c[k], tp + 64 * k);
     } else if (FMT == RFX_FP3) {
         RFX_LD(t.sc16, tp + 64 * 6);
@@ -190,7 +199,12 @@ __device__ __forceinline__ float block_min(const TileRegs<FMT> &t, int bi)
 template <int FMT>
 __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel8 &sel, float &sw)
 {
-    if (FMT == RFX_FP4) {
+    if (FMT == RFX_Q8) { // the codes are the int8 values: no expansion
+        const u32x4 a = t.c[2 * bi], b = t.c[2 * bi + 1];
+        sel.v[0] = (int)a.x, sel.v[1] = (int)a.y, sel.v[2] = (int)a.z, sel.v[3] = (int)a.w;
+        sel.v[4] = (int)b.x, sel.v[5] = (int)b.y, sel.v[6] = (int)b.z, sel.v[7] = (int)b.w;
+        sw = half_of(t.sc16, bi);
+    } else if (FMT == RFX_FP4) {
         sel = sel_fp4(t.c[bi]);
         const uint32_t e = ((bi < 4 ? t.sc8.x : t.sc8.y) >> (8 * (bi & 3))) & 0xffu;
         sw = ldexpf(1.0f, (int)e - 128); // 2 x E2M1 codebook: scale 2^(E-128)
@@ -294,7 +308,7 @@ __device__ __forceinline__ void tile_blocks(const TileRegs<FMT> &t, int b0, int 
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
         const int b = FULL ? b0 + bi : min(b0 + bi, nb - 1);
-        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b);
+        const XBlock<Q> xb = load_xblock<TileFmt<FMT>::needs_sum, Q>(xc, b);
         Sel8 sel;
         float sw;
         decode_block<FMT>(t, bi, sel, sw);

@@ -189,7 +189,7 @@ __device__ __forceinline__ void compute_tile(const WTile<FMT, Q> &t, int s, int 
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
         const int b = min(b0 + bi, a.nb - 1);
-        const XBlock<Q> xb = load_xblock<FMT != RFX_FP4, Q>(xc, b);
+        const XBlock<Q> xb = load_xblock<TileFmt<FMT>::needs_sum, Q>(xc, b);
         Sel8 sel;
         float sw;
         decode_block<FMT>(t.w, bi, sel, sw);
@@ -304,6 +304,15 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float
         constexpr bool BC = use_bcast<Q>();
         const WTile<FMT, Q> t = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb);
         compute_tile<FMT, Q, DOTS, FULL, BC>(t, s_begin, row, a, xc, acc);
+    } else if (TileFmt<FMT>::code_chunks > 8) {
+        // Q8 tiles (64 registers of codes) take one buffer, so that the
+        // format does not raise the register budget of the kernels it
+        // shares with the smaller formats
+        constexpr bool BC = LBC && use_bcast<Q>();
+        for (int s = s_begin; s < s_end; s++) {
+            const WTile<FMT, Q> t = load_wtile<FMT, Q, FULL, BC>(gbase, s, lane, xc, a.nb);
+            compute_tile<FMT, Q, DOTS, FULL, BC>(t, s, row, a, xc, acc);
+        }
     } else if (s_begin < s_end) {
         // two tile buffers used in turn (no register copies, which would
         // wait for the loads they copy): tile s + 1 in flight while s is
@@ -460,6 +469,7 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
         RFX_JOB(RFX_FP3, 1) RFX_JOB(RFX_FP3, 2) RFX_JOB(RFX_FP3, 3) RFX_JOB(RFX_FP3, 4)
         RFX_JOB(RFX_FP4, 1) RFX_JOB(RFX_FP4, 2) RFX_JOB(RFX_FP4, 3) RFX_JOB(RFX_FP4, 4)
         RFX_JOB(RFX_FP2M, 1) RFX_JOB(RFX_FP2M, 2) RFX_JOB(RFX_FP2M, 3) RFX_JOB(RFX_FP2M, 4)
+        RFX_JOB(RFX_Q8, 1) RFX_JOB(RFX_Q8, 2) RFX_JOB(RFX_Q8, 3) RFX_JOB(RFX_Q8, 4)
     default: break;
     }
 #undef RFX_JOB
@@ -518,6 +528,7 @@ int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
     case RFX_FP3: return full ? launch_q<RFX_FP3, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP3, DOTS, false>(a, q, G, W, st);
     case RFX_FP4: return full ? launch_q<RFX_FP4, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP4, DOTS, false>(a, q, G, W, st);
     case RFX_FP2M: return full ? launch_q<RFX_FP2M, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2M, DOTS, false>(a, q, G, W, st);
+    case RFX_Q8: return full ? launch_q<RFX_Q8, DOTS, true>(a, q, G, W, st) : launch_q<RFX_Q8, DOTS, false>(a, q, G, W, st);
     }
     return fail(RFX_E_INVAL, "unknown format");
 }
@@ -669,7 +680,7 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         order[j] = j;
     auto cost = [&](int j) {
         const int f = jobs[j].W.fmt, q = jobs[j].q;
-        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : f == RFX_FP2M ? 38 : 75;
+        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : f == RFX_FP2M ? 38 : f == RFX_Q8 ? 20 : 75;
         return base + 12 * q;
     };
     for (int i = 1; i < n_jobs; i++) // stable insertion sort, n <= 16

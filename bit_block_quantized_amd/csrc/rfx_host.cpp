@@ -85,17 +85,20 @@ const char *rfx_version(void) { return "rfx 0.1 gfx950"; }
 
 int rfx_block_bytes(int fmt)
 {
-    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M ? 12 : RFX_E_INVAL;
+    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M ? 12
+         : fmt == RFX_Q8 ? 34 : RFX_E_INVAL;
 }
 
 int rfx_code_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP2M ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16 : RFX_E_INVAL;
+    return fmt == RFX_FP2 || fmt == RFX_FP2M ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16
+         : fmt == RFX_Q8 ? 32 : RFX_E_INVAL;
 }
 
 int rfx_scale_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP3 ? 2 : fmt == RFX_FP4 ? 1 : fmt == RFX_FP2M ? 4 : RFX_E_INVAL;
+    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_Q8 ? 2 : fmt == RFX_FP4 ? 1 : fmt == RFX_FP2M ? 4
+         : RFX_E_INVAL;
 }
 
 } // extern "C"
@@ -135,7 +138,9 @@ inline int code_fp4(float t)
 
 inline void put_code(int fmt, uint8_t *codes, int t, int c)
 {
-    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
+    if (fmt == RFX_Q8) {
+        codes[t] = (uint8_t)c;
+    } else if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         codes[4 * m + j] |= (uint8_t)((c & 3) << (2 * i));
         if (fmt == RFX_FP3)
@@ -148,6 +153,8 @@ inline void put_code(int fmt, uint8_t *codes, int t, int c)
 
 inline int get_code(int fmt, const uint8_t *codes, int t)
 {
+    if (fmt == RFX_Q8)
+        return codes[t];
     if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         int c = (codes[4 * m + j] >> (2 * i)) & 3;
@@ -168,6 +175,8 @@ inline int code_value(int fmt, int c)
         return 2 * c - 7;
     if (fmt == RFX_FP2M)
         return c;
+    if (fmt == RFX_Q8)
+        return (int)(int8_t)(uint8_t)c;
     return (c & 8) ? -mag[c & 7] : mag[c & 7];
 }
 
@@ -236,6 +245,19 @@ int encode_block(int fmt, const float *w, uint8_t *blk)
     std::memset(blk, 0, (size_t)rfx_block_bytes(fmt));
     if (fmt == RFX_FP2M)
         return encode_fp2m(w, blk);
+    if (fmt == RFX_Q8) {
+        const _Float16 h = (_Float16)(amax / 127.0f); // fp32 division, then RNE to binary16
+        const float s = (float)h;
+        if (std::isinf(s))
+            return fail(RFX_E_RANGE, "fp16 scale overflow (amax %g)", (double)amax);
+        for (int t = 0; t < 32; t++) {
+            float r = s == 0.0f ? 0.0f : std::nearbyint(w[t] / s); // half to even
+            r = std::fmin(std::fmax(r, -127.0f), 127.0f);
+            put_code(fmt, blk, t, (int)r);
+        }
+        put_half(blk + cb, h);
+        return RFX_OK;
+    }
     if (fmt == RFX_FP4) {
         // OCP MX: E = floor(log2 amax) - 2 + 127, clamped; ilogb is exact,
         // subnormals included.
@@ -284,6 +306,10 @@ inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
     if (fmt == RFX_FP4) {
         p.code0 = tile + bi * kChunk + lane * 16;
         p.scale = tile + 8 * kChunk + lane * 8 + bi;
+    } else if (fmt == RFX_Q8) {
+        p.code0 = tile + (2 * bi) * kChunk + lane * 16;
+        p.code1 = tile + (2 * bi + 1) * kChunk + lane * 16;
+        p.scale = tile + 16 * kChunk + lane * 16 + bi * 2;
     } else {
         p.code0 = tile + (bi / 2) * kChunk + lane * 16 + (bi % 2) * 8;
         if (fmt == RFX_FP3) {
@@ -304,6 +330,10 @@ void place_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *blk
     if (fmt == RFX_FP4) {
         std::memcpy(tiled + p.code0, blk, 16);
         tiled[p.scale] = blk[16];
+    } else if (fmt == RFX_Q8) {
+        std::memcpy(tiled + p.code0, blk, 16);
+        std::memcpy(tiled + p.code1, blk + 16, 16);
+        std::memcpy(tiled + p.scale, blk + cb, 2);
     } else {
         std::memcpy(tiled + p.code0, blk, 8);
         if (fmt == RFX_FP3)
@@ -321,6 +351,10 @@ void fetch_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *til
     if (fmt == RFX_FP4) {
         std::memcpy(blk, tiled + p.code0, 16);
         blk[16] = tiled[p.scale];
+    } else if (fmt == RFX_Q8) {
+        std::memcpy(blk, tiled + p.code0, 16);
+        std::memcpy(blk + 16, tiled + p.code1, 16);
+        std::memcpy(blk + cb, tiled + p.scale, 2);
     } else {
         std::memcpy(blk, tiled + p.code0, 8);
         if (fmt == RFX_FP3)
@@ -424,7 +458,7 @@ int rfx_quantize_matrix(int fmt, const float *W, int64_t rows, int64_t cols, voi
     const size_t group_bytes = (size_t)S * tile_bytes(fmt);
     return for_row_groups(rows, threads, [&](int64_t g) -> int {
         std::memset(out + g * group_bytes, 0, group_bytes);
-        uint8_t blk[17];
+        uint8_t blk[kMaxBlockBytes];
         for (int64_t r = g * kTileRows; r < std::min<int64_t>(rows, (g + 1) * kTileRows); r++)
             for (int64_t b = 0; b < nb; b++) {
                 int s2 = encode_block(fmt, W + r * cols + b * 32, blk);

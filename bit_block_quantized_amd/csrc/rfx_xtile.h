@@ -60,7 +60,9 @@ __device__ __forceinline__ Sel8 sel2_fp3(uint32_t w0, uint32_t w1, uint32_t h)
 template <int FMT, int BI>
 __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel, float &sw)
 {
-    if (FMT == RFX_FP4) {
+    if (FMT == RFX_Q8) {
+        decode_block<FMT>(t, BI, sel, sw);
+    } else if (FMT == RFX_FP4) {
         sel = sel_fp4(t.c[BI]);
         const uint32_t e = ((BI < 4 ? t.sc8.x : t.sc8.y) >> (8 * (BI & 3))) & 0xffu;
         sw = ldexpf(1.0f, (int)e - 128);
@@ -133,7 +135,7 @@ __device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int
 #pragma unroll
     for (int j = 0; j < Q; j++)
         xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
-    if (FMT != RFX_FP4) {
+    if (TileFmt<FMT>::needs_sum) {
         constexpr int off = FMT == RFX_FP2 ? 3 : FMT == RFX_FP3 ? 7 : -1; // FP2M: +sum
 #pragma unroll
         for (int j = 0; j < Q; j++)

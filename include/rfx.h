@@ -64,16 +64,20 @@ enum {
  *            named formats): 2-bit codes c in 0..3, weight = s * c + m, fp16
  *            s then fp16 m: 12 B / block (3.0 bits per weight). Supported
  *            by the encoder, the layout routines and the GEMV entry points;
- *            the MoE and prefill layers return RFX_E_UNSUPPORTED for it. */
-enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_FP2M = 12 };
+ *            the MoE and prefill layers return RFX_E_UNSUPPORTED for it.
+ *   RFX_Q8:  a tier above FP4 (the same paragraph keeps dense and sensitive
+ *            projections at FP4 or higher; this tier is a reading): 32 int8
+ *            codes in weight order, then an fp16 scale s; weight = s * c:
+ *            34 B / block (8.5 bits per weight). Same support as RFX_FP2M. */
+enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_Q8 = 8, RFX_FP2M = 12 };
 
 const char *rfx_status_str(int status);
 const char *rfx_last_error(void);
 const char *rfx_version(void);
 
-int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M), or RFX_E_INVAL */
-int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 */
-int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 */
+int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M) / 34 (Q8), or RFX_E_INVAL */
+int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 / 32 */
+int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 */
 
 /* ------------------------------------------------------------------ */
 /* Host-side encoder (synchronous, host memory).                       */
@@ -90,6 +94,9 @@ int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 */
  * FP2M: m = fp16_rne(min w); s = fp16_rne(max(max w - m, 0) / 3) in fp32;
  * code = nearest of 0..3 to (w - m) / s in fp32, ties to the larger; s = 0
  * codes every weight as 0. Block: codes, s, m (both fp16 little-endian).
+ * Q8: s = fp16_rne(amax / 127) in fp32; code = clamp(round half to even of
+ * w / s in fp32, -127, 127) stored as the two's-complement byte; s = 0
+ * codes every weight as 0. Code byte t is weight t.
  * Bit layout of the code bytes, as little-endian 32-bit words:
  *   FP2 (and FP2M): weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
  *   FP3: low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
@@ -117,6 +124,8 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
  *   FP4 (tile 8704 B): chunks 0-7 = codes of block c; then 64 rows x 8 B of
  *       e8m0 scales at byte 8192 + r * 8.
  *   FP2M (tile 6144 B): chunks 0-4 as FP2; chunk 5 = the eight fp16 minima.
+ *   Q8 (tile 17408 B): chunk 2b + h = code bytes 16h..16h+15 of block b;
+ *       chunk 16 = the eight fp16 scales.
  * Rows beyond `rows` and blocks beyond cols/32 are zero (scale 0). Block
  * bits are exactly those of the canonical block. A stack of `count`
  * matrices (MoE experts) places matrix e at e * rfx_qmat_bytes(...). */

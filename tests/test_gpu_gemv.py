@@ -15,7 +15,8 @@ from gpu_common import TOL, need_gpu, quantize_on_gpu, rel_err, say, upload_matr
 pytestmark = pytest.mark.gpu
 FMTS = (2, 3, 4)
 FP2M = R.FP2M
-GEMV_FMTS = FMTS + (FP2M,)  # the GEMV entry points also take the FP2M variant
+Q8 = R.Q8
+GEMV_FMTS = FMTS + (FP2M, Q8)  # the GEMV entry points also take the FP2M variant and the Q8 tier
 
 
 def _sync(torch):
@@ -92,7 +93,7 @@ _BIG = {}
 
 def _big(fmt):
     if fmt not in _BIG:
-        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30}[fmt], outliers=True)
+        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30, Q8: 40}[fmt], outliers=True)
         _BIG[fmt] = (W, O.quantize_matrix(fmt, W))
     return _BIG[fmt]
 
@@ -134,7 +135,7 @@ def test_gemv_deterministic_and_columns_independent(fmt):
     # more columns: vector decode and int8 dots), so they agree to fp32
     # rounding of the row sums rather than to the last bits; a column
     # leaking into another would be off by far more.
-    same_path = fmt != 4
+    same_path = fmt != 4  # FP4: matrix core at q = 1, vector path at q = 4
     oq, os_ = O.quantize_act(x)
     blocks = O.quantize_matrix(fmt, W)
     for j in range(4):
@@ -225,6 +226,8 @@ def _grouped(torch, specs, seed, big=False):
     [(3, 4, 640, 1536)],
     # the FP2M variant beside the named formats, ragged and full tiles
     [(12, 1, 200, 544), (2, 4, 130, 2080), (12, 4, 65, 1024), (12, 2, 1, 32), (4, 1, 256, 512)],
+    # the Q8 tier (one tile buffer) beside the others, a multi-tile K split
+    [(8, 1, 300, 4096), (8, 4, 65, 1312), (3, 2, 130, 2048), (8, 3, 1, 32)],
 ])
 def test_gemv_grouped_small(specs):
     torch = need_gpu()

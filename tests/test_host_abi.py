@@ -16,7 +16,7 @@ import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FMTS = (2, 3, 4)
-ALL_FMTS = (2, 3, 4, 12)  # the three named formats and the FP2M variant
+ALL_FMTS = (2, 3, 4, 12, 8)  # the three named formats, the FP2M variant, the Q8 tier
 
 
 def _header_functions():
@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_sizes():
     for fmt, (bb, cb, sb, tile) in {2: (10, 8, 2, 5120), 3: (14, 12, 2, 7168),
-                                     4: (17, 16, 1, 8704), 12: (12, 8, 4, 6144)}.items():
+                                     4: (17, 16, 1, 8704), 12: (12, 8, 4, 6144),
+                                     8: (34, 32, 2, 17408)}.items():
         assert R.block_bytes(fmt) == bb == O.block_bytes(fmt)
         assert R.code_bytes(fmt) == cb and R.scale_bytes(fmt) == sb
         assert R.qmat_bytes(fmt, 64, 256) == tile == 64 * 8 * bb
@@ -121,6 +122,12 @@ def test_tiled_layout_positions():
         if fmt == 4:
             assert list(t[tile + bi * 1024 + lane * 16: tile + bi * 1024 + lane * 16 + 16]) == list(range(1, 17))
             assert t[tile + 8192 + lane * 8 + bi] == 17
+        elif fmt == 8:
+            for h in range(2):
+                c = tile + (2 * bi + h) * 1024 + lane * 16
+                assert list(t[c:c + 16]) == list(range(1 + 16 * h, 17 + 16 * h))
+            sc = tile + 16 * 1024 + lane * 16 + bi * 2
+            assert list(t[sc:sc + 2]) == [33, 34]
         else:
             c0 = tile + (bi // 2) * 1024 + lane * 16 + (bi % 2) * 8
             assert list(t[c0:c0 + 8]) == list(range(1, 9))
