@@ -44,7 +44,7 @@
  *         (3.0 bits per weight); weight = s * c + m, c in 0..3.
  *
  * A tier above FP4 for the dense and sensitive projections (the same
- * paragraph keeps those at FP4 "or higher" without naming a format; this
+ * paragraph keeps those at FP4 or a wider format without naming one; this
  * tier is a reading):
  *   Q8:   32 int8 codes in weight order + fp16 scale = 34 bytes
  *         (8.5 bits per weight); weight = s * c, c in -127..127.
