@@ -130,68 +130,93 @@ __device__ __forceinline__ uint32_t logit_key(float l)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave: softmax over the E logits of token t held 4 per lane (expert
-// lane + 64 r) and the top k by logit, equal logits to the lower id: k
-// rounds of (largest key, then lowest id holding it). Writes topk_idx /
-// topk_w and s_idx[t*k + j].
+// Inverse of logit_key.
+__device__ __forceinline__ float key_logit(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Candidate order of the top-k: larger key first, equal keys by lower id.
+__device__ __forceinline__ void order_pair(uint32_t &ka, int &ia, uint32_t &kb, int &ib)
+{
+    const bool sw = kb > ka || (kb == ka && ib < ia);
+    const uint32_t k0 = sw ? kb : ka, k1 = sw ? ka : kb;
+    const int i0 = sw ? ib : ia, i1 = sw ? ia : ib;
+    ka = k0;
+    kb = k1;
+    ia = i0;
+    ib = i1;
+}
+
+// One wave: softmax over the E <= 256 logits of token t, held 4 per lane
+// (expert lane + 64 r), and the top k by logit, equal logits to the lower
+// id. Each lane sorts its four candidates once; a round then takes the
+// wave maximum of the lane heads and the lowest id among the heads equal
+// to it (one ballot; a second reduction only when several lanes tie), and
+// that lane drops its head. Lane j keeps pick j. Writes topk_idx / topk_w
+// and s_idx[t*k + j]. The last workgroup runs this once per call, with a
+// cold instruction cache, so the loops stay rolled and the code short.
 __device__ void wave_topk(const float (&l)[4], int E, int k, int t, int lane, int32_t *topk_idx, float *topk_w,
                           int *s_idx)
 {
     uint32_t key[4];
-    bool live[4];
+    int id[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-        live[r] = lane + 64 * r < E;
-        key[r] = live[r] ? logit_key(l[r]) : 0u; // 0 is below every finite logit
+        id[r] = lane + 64 * r;
+        key[r] = id[r] < E ? logit_key(l[r]) : 0u; // 0 is below every finite logit
     }
-    float m = 0.0f, z = 0.0f;
+    order_pair(key[0], id[0], key[1], id[1]);
+    order_pair(key[2], id[2], key[3], id[3]);
+    order_pair(key[0], id[0], key[2], id[2]);
+    order_pair(key[1], id[1], key[3], id[3]);
+    order_pair(key[1], id[1], key[2], id[2]);
+
+    uint32_t my_key = 0u, top_key = 0u;
+    int my_id = 0;
+#pragma unroll 1
     for (int j = 0; j < k; j++) {
-        uint32_t loc = 0u;
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            loc = (live[r] && key[r] > loc) ? key[r] : loc;
-        const uint32_t best = wave_umax(loc);
-        uint32_t id = 0xFFFFFFFFu;
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            if (live[r] && key[r] == best)
-                id = min(id, (uint32_t)(lane + 64 * r));
-        const int e = (int)wave_umin(id);
-        float le = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            if (lane + 64 * r == e) {
-                live[r] = false;
-                le = l[r];
-            }
-        le = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(le), e & 63));
-        if (j == 0) {
-            m = le; // the largest logit
-            float zz = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                zz += lane + 64 * r < E ? expf(l[r] - m) : 0.0f;
-            z = wave_fsum(zz);
+        const uint32_t best = wave_umax(key[0]);
+        const unsigned long long tied = __ballot(key[0] == best);
+        int e;
+        if (__popcll(tied) == 1)
+            e = __builtin_amdgcn_readlane(id[0], __ffsll((long long)tied) - 1);
+        else
+            e = (int)wave_umin(key[0] == best ? (uint32_t)id[0] : 0xFFFFFFFFu);
+        if (lane == (e & 63)) { // the winner's lane drops its head
+            key[0] = key[1];
+            key[1] = key[2];
+            key[2] = key[3];
+            key[3] = 0u;
+            id[0] = id[1];
+            id[1] = id[2];
+            id[2] = id[3];
+            id[3] = 0x7FFFFFFF;
         }
-        if (lane == 0) {
-            topk_idx[t * k + j] = e;
-            topk_w[t * k + j] = expf(le - m) / z;
-            s_idx[t * k + j] = e;
+        if (lane == j) {
+            my_key = best;
+            my_id = e;
         }
+        top_key = j == 0 ? best : top_key;
+    }
+    // softmax denominator against the largest logit
+    const float m = key_logit(top_key);
+    float zz = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+        zz += lane + 64 * r < E ? expf(l[r] - m) : 0.0f;
+    const float z = wave_fsum(zz);
+    if (lane < k) {
+        topk_idx[t * k + lane] = my_id;
+        topk_w[t * k + lane] = expf(key_logit(my_key) - m) / z;
+        s_idx[t * k + lane] = my_id;
     }
 }
 
-// Router for q <= 4 tokens: one workgroup per expert row of Wr; the last
-// workgroup to finish picks the top k per token and buckets the pairs.
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
+// Quantization of the router's tokens for the experts: 32 lanes per
+// 32-element block, blocks spread over all workgroups of the router.
+__device__ __forceinline__ void route_quant(const RouteArgs &a, int wave, int lane)
 {
-    __shared__ int s_last;
-    __shared__ int s_idx[kMaxDecodeQ * kMaxK];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // (1) quantize the tokens for the experts: 32 lanes per 32-element
-    // block, blocks spread over all workgroups
     const int nblk = a.q * (a.H / 32);
     for (int base = (blockIdx.x * 4 + wave) * 2; base < nblk; base += gridDim.x * 8) {
         const int blk = base + (lane >> 5);
@@ -210,60 +235,92 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
             }
         }
     }
+}
 
-    // (2) one workgroup per expert row: each thread takes up to 8 float4
-    //     columns (h = 4 tid + 1024 i), every load issued before the sums;
-    //     fixed-order reduction (lane butterfly, then waves in order)
+// Router for q <= 4 tokens: one workgroup per expert row of Wr. Arrival
+// is counted in two levels (kRouteGroup workgroups per sub-counter, then
+// one counter over the groups), since atomics on one address serialize;
+// the last workgroup to arrive picks the top k per token and buckets the
+// pairs.
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
+{
+    __shared__ int s_last;
+    __shared__ __align__(16) int s_idx[kMaxDecodeQ * kMaxK];
     __shared__ float s_part[4][kMaxDecodeQ];
-    for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
-        const float *wrow = a.wr + (size_t)e * a.H;
-        float4 w4[8];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int e = blockIdx.x;
+
+    // (0) the workgroup's row of Wr: each thread takes up to 8 float4
+    //     columns (h = 4 tid + 1024 i), issued before anything waits
+    const float *wrow = a.wr + (size_t)e * a.H;
+    float4 w4[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int h = tid * 4 + 1024 * i;
+        w4[i] = h < a.H ? *reinterpret_cast<const float4 *>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // (1) logits of row e: every token's x loaded at once, then a
+    //     fixed-order reduction (per thread, the lane butterfly, then the
+    //     waves in order)
+    float4 x4[kMaxDecodeQ][8];
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeQ; t++)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int h = tid * 4 + 1024 * i;
-            w4[i] = h < a.H ? *reinterpret_cast<const float4 *>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+            x4[t][i] = (t < a.q && h < a.H) ? *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        float part[kMaxDecodeQ];
+    float part[kMaxDecodeQ];
 #pragma unroll
-        for (int t = 0; t < kMaxDecodeQ; t++) {
-            part[t] = 0.0f;
-            if (t < a.q) {
-                float4 x4[8];
+    for (int t = 0; t < kMaxDecodeQ; t++) {
+        part[t] = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const int h = tid * 4 + 1024 * i;
-                    x4[i] = h < a.H ? *reinterpret_cast<const float4 *>(a.x + (size_t)t * a.H + h)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int i = 0; i < 8; i++)
-                    part[t] += w4[i].x * x4[i].x + w4[i].y * x4[i].y + w4[i].z * x4[i].z + w4[i].w * x4[i].w;
-            }
-            for (int o = 32; o > 0; o >>= 1)
-                part[t] += __shfl_xor(part[t], o, 64);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int t = 0; t < kMaxDecodeQ; t++)
-                s_part[wave][t] = part[t];
-        }
-        __syncthreads();
-        if (tid < a.q) {
-            const float l = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
-            __hip_atomic_store(a.logits + (size_t)tid * a.E + e, a.wb ? l + a.wb[e] : l, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
+        for (int i = 0; i < 8; i++)
+            part[t] += w4[i].x * x4[t][i].x + w4[i].y * x4[t][i].y + w4[i].z * x4[t][i].z + w4[i].w * x4[t][i].w;
+        for (int o = 32; o > 0; o >>= 1)
+            part[t] += __shfl_xor(part[t], o, 64);
     }
+    if (lane == 0) {
+#pragma unroll
+        for (int t = 0; t < kMaxDecodeQ; t++)
+            s_part[wave][t] = part[t];
+    }
+    __syncthreads();
+    if (tid < a.q) {
+        const float l = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+        __hip_atomic_store(a.logits + (size_t)tid * a.E + e, a.wb ? l + a.wb[e] : l, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // (2) arrival. Every workgroup but the last then quantizes its share
+    //     of the tokens (late, so that no logit waits for it) and leaves;
+    //     the last does its share after the top-k and the bucketing.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(a.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    const int ngroups = (gridDim.x + kRouteGroup - 1) / kRouteGroup;
+    if (tid == 0) {
+        const int g = blockIdx.x / kRouteGroup;
+        const unsigned gsize = (unsigned)min(kRouteGroup, (int)gridDim.x - g * kRouteGroup);
+        bool last = false;
+        if (__hip_atomic_fetch_add(a.cnt + kRouteCntStride * g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            gsize - 1)
+            last = __hip_atomic_fetch_add(a.cnt + kRouteCntStride * kRouteMaxGroups, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)ngroups - 1;
+        s_last = last;
+    }
     __syncthreads();
-    if (!s_last)
+    if (!s_last) {
+        route_quant(a, wave, lane);
         return;
+    }
 
-    // (3) last workgroup: softmax and top-k, one wave per token
+    // (3) last workgroup: softmax and top-k, one wave per token (the
+    //     pair list's unused tail holds a key above every expert)
+    const int np = a.q * a.k;
+    if (tid >= np && tid < kMaxDecodeQ * kMaxK)
+        s_idx[tid] = 0x7FFFFFFF;
     if (wave < a.q) {
         const int t = wave;
         float l[4];
@@ -278,26 +335,38 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
     }
     __syncthreads();
 
-    // (4) stable bucketing of the q*k <= 32 pairs by expert (pair p = t*k+j):
-    //     position = pairs of lower experts + earlier pairs of the same one
-    const int np = a.q * a.k;
-    if (tid < np) {
-        const int ep = s_idx[tid];
-        int pos = 0;
-        for (int p = 0; p < np; p++) {
-            const int eo = s_idx[p];
-            pos += (eo < ep || (eo == ep && p < tid)) ? 1 : 0;
+    // (4) stable bucketing of the np = q*k <= 32 pairs by expert (pair
+    //     p = t*k + j): position = pairs of lower experts + earlier pairs
+    //     of the same one; expert_off[ee] = pairs of experts below ee.
+    //     Every thread reads the list as int4 words and compares eight
+    //     entries per step, skipping steps past np.
+    const int mine = tid < np ? s_idx[tid] : 0;
+    int pos = 0, before = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxDecodeQ * kMaxK; c += 8) {
+        if (c < np) {
+            const int4 u = reinterpret_cast<const int4 *>(s_idx)[c / 4];
+            const int4 v = reinterpret_cast<const int4 *>(s_idx)[c / 4 + 1];
+            const int pe[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                pos += (pe[i] < mine || (pe[i] == mine && c + i < tid)) ? 1 : 0;
+                before += pe[i] < tid ? 1 : 0;
+            }
         }
+    }
+    if (tid < np)
         a.pairs_sorted[pos] = tid;
-    }
-    for (int ee = tid; ee <= a.E; ee += 256) {
-        int before = 0;
-        for (int p = 0; p < np; p++)
-            before += s_idx[p] < ee ? 1 : 0;
-        a.expert_off[ee] = before;
-    }
+    if (tid < a.E)
+        a.expert_off[tid] = before;
     if (tid == 0)
-        __hip_atomic_store(a.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.expert_off[a.E] = np;
+    if (tid < ngroups)
+        __hip_atomic_store(a.cnt + kRouteCntStride * tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+        __hip_atomic_store(a.cnt + kRouteCntStride * kRouteMaxGroups, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    route_quant(a, wave, lane);
 }
 
 // ------------------------------------------------------------------

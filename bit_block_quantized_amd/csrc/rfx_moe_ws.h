@@ -16,6 +16,11 @@ constexpr int kMaxE = 256;        // routed experts per layer
 constexpr int kMaxDecodeQ = 4;    // tokens handled by the decode kernels
 constexpr int kPrefillChunk = 64; // tokens per work item of the prefill kernels
 constexpr int kMaxPrefillQ = 1 << 16;
+// Arrival counters of the decode router: one per kRouteGroup workgroups,
+// then one over the groups, each on its own 128-byte line.
+constexpr int kRouteGroup = 16;
+constexpr int kRouteMaxGroups = kMaxE / kRouteGroup;
+constexpr int kRouteCntStride = 32; // 32-bit words between counters
 
 // Work items of the prefill FFN: (expert, first token) per chunk of up to
 // kPrefillChunk tokens of one expert, then the shared expert's chunks.
@@ -30,7 +35,7 @@ inline int prefill_max_items(int q, int k, int E)
 // expert.
 struct MoeWs {
     float *logits;      // [q][E] (decode)
-    unsigned *route_cnt;
+    unsigned *route_cnt; // [kRouteMaxGroups + 1] counters, kRouteCntStride words apart
     float *h;           // [NP][I]   NP = q*k + q (decode keeps it for inspection)
     int8_t *hq;         // [NP][I]
     float *hs;          // [NP][I/32]
@@ -54,7 +59,7 @@ inline MoeWs carve(void *base, int q, int k, int E, int H, int I)
         return o;
     };
     const size_t o_logits = take((size_t)q * E * 4);
-    const size_t o_rc = take(4);
+    const size_t o_rc = take((size_t)(kRouteMaxGroups + 1) * kRouteCntStride * 4);
     const size_t o_h = take(NP * I * 4);
     const size_t o_hq = take(NP * I);
     const size_t o_hs = take(NP * (I / 32) * 4);

@@ -172,3 +172,36 @@ def test_moe_stack_two_layers_zipf_top4(q):
         x = (x + gpu["y"]).astype(np.float32)
         del dev
         torch.cuda.empty_cache()
+
+
+def test_moe_router_exact_ties_go_to_lower_id():
+    """Experts with identical router rows and biases have bit-identical
+    logits on both sides, so the tie rule (equal logits to the lower id)
+    decides their order. The tied groups sit in one lane of the router's
+    wave (experts 5, 69, 133, 197 share a lane), across lanes (10, 11,
+    12, 74) and at the ends of the id range (0, 255); k = 6 splits a
+    group."""
+    torch = need_gpu()
+    spec = LayerSpec(layer=9, hidden=256, inter=64, n_experts=256, shared=False)
+    groups = ([5, 69, 133, 197], [74, 12, 10, 11], [255, 0])
+    w = spec.router_w.copy()
+    b = np.zeros(spec.n_experts, np.float32)
+    for gi, g in enumerate(groups):
+        for e in g:
+            w[e] = w[g[0]]
+            b[e] = 8.0 - gi
+    spec.router_w, spec.router_b = w, b
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    for q, k in ((4, 8), (4, 6), (1, 3), (3, 2)):
+        say(f"router ties q={q} k={k}")
+        x = inputgen.tokens(9, 40 + q + k, q, spec.hidden)
+        ref = orc.route(x, k)
+        # the groups' logits are far apart for these tokens, so only the
+        # exact ties inside a group decide the order
+        for t in range(q):
+            lg = sorted(ref["logits"][t][g[0]] for g in groups)
+            assert min(np.diff(lg)) > 1e-3
+        gpu = _run_layer(torch, spec, dev, x, k)
+        assert np.array_equal(gpu["topk_idx"], ref["idx"]), (gpu["topk_idx"], ref["idx"])
+        _check_layer(spec, gpu, x, k, orc)
