@@ -39,7 +39,11 @@ FP2M = 12
 # A tier above FP4 (the same paragraph keeps dense and sensitive
 # projections at FP4 or higher): 32 int8 codes + an fp16 scale, 34 B.
 Q8 = 8
-VARIANT_FORMATS = (FP2M, Q8)
+# Variant with two 16-weight sub-scales (each half an FP2 block of its own,
+# 12 B): the second of the two small values a block may carry is a second
+# scale; a reading.
+FP2S = 16
+VARIANT_FORMATS = (FP2M, Q8, FP2S)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "liboracle.so")
@@ -78,6 +82,8 @@ def lib():
     L.orc_block_scale.restype = ctypes.c_double
     L.orc_block_min.argtypes = [ctypes.c_int, _u8p]
     L.orc_block_min.restype = ctypes.c_double
+    L.orc_weight_scale.argtypes = [ctypes.c_int, _u8p, ctypes.c_int]
+    L.orc_weight_scale.restype = ctypes.c_double
     L.orc_dequantize_block.argtypes = [ctypes.c_int, _u8p, _f64p]
     L.orc_dequantize_block.restype = None
     L.orc_quantize_block.argtypes = [ctypes.c_int, _f32p, _u8p]
@@ -156,6 +162,13 @@ def block_scale(fmt: int, blk) -> float:
     return float(lib().orc_block_scale(fmt, _p(blk, _u8p)))
 
 
+def weight_scale(fmt: int, blk, t: int) -> float:
+    """Scale of weight t of a block: FP2S's scale of the half holding t,
+    the block scale otherwise."""
+    blk = np.ascontiguousarray(blk, dtype=np.uint8)
+    return float(lib().orc_weight_scale(fmt, _p(blk, _u8p), t))
+
+
 def block_min(fmt: int, blk) -> float:
     """FP2M's fp16 minimum (0 for the symmetric formats)."""
     blk = np.ascontiguousarray(blk, dtype=np.uint8)
@@ -215,7 +228,9 @@ def act_sums(xq) -> np.ndarray:
 
 def gemv(fmt: int, blocks, xq, xs, want_dots: bool = False):
     """y[j][n] = sum_b S[n,b] * s[j,b] * D[j,n,b] in fp64 (exact int dots);
-    FP2M adds s[j,b] * M[n,b] * X[j,b] (X the activation block sum).
+    FP2M adds s[j,b] * M[n,b] * X[j,b] (X the activation block sum); FP2S
+    takes s[j,b] * (S0 D0 + S1 D1) over the two halves (the dots returned
+    are D = D0 + D1).
 
     blocks: uint8 [N][K/32][bb]; xq int8 [Q][K]; xs fp32 [Q][K/32].
     Returns fp64 [Q][N] (and int32 dots [Q][N][K/32] when asked)."""

@@ -43,6 +43,11 @@
  *   FP2M: the FP2 code bytes + fp16 scale s + fp16 minimum m = 12 bytes
  *         (3.0 bits per weight); weight = s * c + m, c in 0..3.
  *
+ * Variant with two small scales per block (the same overview; a reading):
+ *   FP2S: the FP2 code bytes + fp16 scale s0 of weights 0..15 + fp16 scale
+ *         s1 of weights 16..31 = 12 bytes (3.0 bits per weight);
+ *         weight t = s_(t/16) * (2c - 3), each half encoded as FP2 is.
+ *
  * A tier above FP4 for the dense and sensitive projections (the same
  * paragraph keeps those at FP4 or a wider format without naming one; this
  * tier is a reading):
@@ -59,6 +64,7 @@
 #define ORC_FP4 4
 #define ORC_FP2M 12
 #define ORC_Q8 8
+#define ORC_FP2S 16
 
 #define ORC_OK 0
 #define ORC_E_INVAL (-1)
@@ -73,6 +79,7 @@ int orc_block_bytes(int fmt)
     case ORC_FP4: return 17;
     case ORC_FP2M: return 12; /* Reading: 8 code bytes + two fp16 values */
     case ORC_Q8: return 34;   /* Reading: 32 int8 codes + an fp16 scale */
+    case ORC_FP2S: return 12; /* Reading: 8 code bytes + two fp16 scales */
     }
     return ORC_E_INVAL;
 }
@@ -85,6 +92,7 @@ int orc_code_bytes(int fmt)
     case ORC_FP4: return 16;
     case ORC_FP2M: return 8;
     case ORC_Q8: return 32;
+    case ORC_FP2S: return 8;
     }
     return ORC_E_INVAL;
 }
@@ -159,12 +167,14 @@ uint16_t orc_f32_to_f16(float f)
  *      2 x E2M1 so it is an integer: m -> 0,1,2,3,4,6,8,12. Code 8 (-0)
  *      decodes to 0 and the encoder never emits it.
  * FP2M: the integer part is the code itself, 0..3; the block's minimum is
- *      added after the scale (weight = s * c + m). */
+ *      added after the scale (weight = s * c + m).
+ * FP2S: FP2's codebook; the scale depends on the half of the block. */
 int orc_codebook(int fmt, int code)
 {
     static const int fp4_mag[8] = {0, 1, 2, 3, 4, 6, 8, 12};
     switch (fmt) {
-    case ORC_FP2: return 2 * code - 3;
+    case ORC_FP2:
+    case ORC_FP2S: return 2 * code - 3;
     case ORC_FP3: return 2 * code - 7;
     case ORC_FP4: return (code & 8) ? -fp4_mag[code & 7] : fp4_mag[code & 7];
     case ORC_FP2M: return code;
@@ -175,7 +185,7 @@ int orc_codebook(int fmt, int code)
 
 static int n_codes(int fmt)
 {
-    return fmt == ORC_FP2 || fmt == ORC_FP2M ? 4 : fmt == ORC_FP3 ? 8 : fmt == ORC_Q8 ? 256 : 16;
+    return fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S ? 4 : fmt == ORC_FP3 ? 8 : fmt == ORC_Q8 ? 256 : 16;
 }
 
 /* Nearest codebook value to t, by brute force over every code.
@@ -223,7 +233,7 @@ int orc_nearest_code(int fmt, double t)
 /* Bit layout inside a block (Reading: the pages do not give one).    */
 /* ------------------------------------------------------------------ */
 /* Code words are little-endian 32-bit words.
- * FP2 (and FP2M): word m (0..1) holds weights 16m..16m+15; weight
+ * FP2 (and FP2M, FP2S): word m (0..1) holds weights 16m..16m+15; weight
  *      16m + 4i + j (i, j in 0..3) occupies bits [8j + 2i, 8j + 2i + 2).
  * FP3: words 0..1 hold the low two bits of every code exactly as FP2;
  *      word 2 holds the high bit, weight 4i + j (i in 0..7, j in 0..3) at
@@ -247,7 +257,7 @@ static void wr32(uint8_t *p, uint32_t v)
 void orc_unpack_codes(int fmt, const uint8_t *blk, int *codes)
 {
     for (int t = 0; t < 32; t++) {
-        if (fmt == ORC_FP2 || fmt == ORC_FP2M) {
+        if (fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             codes[t] = (int)((rd32(blk + 4 * m) >> (8 * j + 2 * i)) & 3u);
         } else if (fmt == ORC_FP3) {
@@ -274,7 +284,7 @@ void orc_pack_codes(int fmt, const int *codes, uint8_t *blk)
     }
     uint32_t w[4] = {0, 0, 0, 0};
     for (int t = 0; t < 32; t++) {
-        if (fmt == ORC_FP2 || fmt == ORC_FP2M) {
+        if (fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             w[m] |= (uint32_t)(codes[t] & 3) << (8 * j + 2 * i);
         } else if (fmt == ORC_FP3) {
@@ -303,6 +313,18 @@ double orc_block_scale(int fmt, const uint8_t *blk)
     return orc_f16_to_f64((uint16_t)(blk[cb] | (blk[cb + 1] << 8)));
 }
 
+/* Scale of weight t of a block: FP2S's fp16 scale of the half holding t
+ * (bytes cb..cb+1 for weights 0..15, cb+2..cb+3 for 16..31); the block
+ * scale for every other format. */
+double orc_weight_scale(int fmt, const uint8_t *blk, int t)
+{
+    int cb = orc_code_bytes(fmt);
+    if (fmt != ORC_FP2S)
+        return orc_block_scale(fmt, blk);
+    int o = cb + 2 * (t / 16);
+    return orc_f16_to_f64((uint16_t)(blk[o] | (blk[o + 1] << 8)));
+}
+
 /* The value added after the scale: FP2M's fp16 minimum (after the fp16
  * scale), zero for the symmetric formats. */
 double orc_block_min(int fmt, const uint8_t *blk)
@@ -317,9 +339,9 @@ void orc_dequantize_block(int fmt, const uint8_t *blk, double *w)
 {
     int codes[32];
     orc_unpack_codes(fmt, blk, codes);
-    double s = orc_block_scale(fmt, blk), m = orc_block_min(fmt, blk);
+    double m = orc_block_min(fmt, blk);
     for (int t = 0; t < 32; t++)
-        w[t] = s * (double)orc_codebook(fmt, codes[t]) + m;
+        w[t] = orc_weight_scale(fmt, blk, t) * (double)orc_codebook(fmt, codes[t]) + m;
 }
 
 /* ------------------------------------------------------------------ */
@@ -414,6 +436,28 @@ int orc_quantize_block(int fmt, const float *w, uint8_t *blk)
         blk[cb + 1] = (uint8_t)(q16 >> 8);
         return ORC_OK;
     }
+    if (fmt == ORC_FP2S) {
+        /* Reading: each 16-weight half h is encoded exactly as an FP2
+         * block would be with its own amax: s_h = fp16(amax_h / 3), the
+         * division in fp32; code = the FP2 value nearest to w / s_h in
+         * fp32; s_h = 0 gives every weight of the half the code of +1. */
+        for (int h = 0; h < 2; h++) {
+            float ah = 0.0f;
+            for (int t = 16 * h; t < 16 * h + 16; t++)
+                if (fabsf(w[t]) > ah)
+                    ah = fabsf(w[t]);
+            uint16_t h16 = orc_f32_to_f16(ah / 3.0f);
+            if ((h16 & 0x7fff) == 0x7c00)
+                return ORC_E_RANGE;
+            float hs = (float)orc_f16_to_f64(h16);
+            for (int t = 16 * h; t < 16 * h + 16; t++)
+                codes[t] = hs == 0.0f ? 2 : orc_nearest_code(fmt, (double)(w[t] / hs));
+            blk[cb + 2 * h] = (uint8_t)(h16 & 0xff);
+            blk[cb + 2 * h + 1] = (uint8_t)(h16 >> 8);
+        }
+        orc_pack_codes(fmt, codes, blk);
+        return ORC_OK;
+    }
     float cmax = (fmt == ORC_FP2) ? 3.0f : 7.0f;
     float s32 = amax / cmax; /* IEEE fp32 division */
     uint16_t s16 = orc_f32_to_f16(s32);
@@ -494,6 +538,8 @@ int orc_quantize_act(const float *x, int64_t n, int8_t *q, float *s)
  * y[j][n] = sum_b S[n][b] * s[j][b] * D[j][n][b] in fp64, b ascending.
  * FP2M adds its minimum: sum_t (S c_t + M) s q_t = s (S D + M X) with X the
  * block's activation sum, also an exact integer.
+ * FP2S scales its halves apart: s (S0 D0 + S1 D1), D0 and D1 the exact
+ * dots over weights 0..15 and 16..31 (D = D0 + D1 is the block dot).
  * Each decoded weight serves every one of the Q columns ([AIN] section on
  * the optimization trio: decode once, apply to all verification columns);
  * the result is the same as Q separate one-column products.
@@ -514,16 +560,20 @@ int orc_gemv(int fmt, const uint8_t *W, int64_t N, int64_t K, const int8_t *xq, 
             int codes[32];
             orc_unpack_codes(fmt, blk, codes);
             double S = orc_block_scale(fmt, blk), M = orc_block_min(fmt, blk);
+            double S0 = orc_weight_scale(fmt, blk, 0), S1 = orc_weight_scale(fmt, blk, 16);
             for (int j = 0; j < Q; j++) {
                 const int8_t *xb = xq + (int64_t)j * K + 32 * b;
-                int64_t D = 0, X = 0;
+                int64_t D = 0, X = 0, Dh[2] = {0, 0};
                 for (int t = 0; t < 32; t++) {
                     D += (int64_t)orc_codebook(fmt, codes[t]) * (int64_t)xb[t];
+                    Dh[t / 16] += (int64_t)orc_codebook(fmt, codes[t]) * (int64_t)xb[t];
                     X += (int64_t)xb[t];
                 }
                 if (dots)
                     dots[((int64_t)j * N + n) * nb + b] = (int32_t)D;
-                if (fmt == ORC_FP2M)
+                if (fmt == ORC_FP2S)
+                    y[(int64_t)j * N + n] += (double)xs[(int64_t)j * nb + b] * (S0 * (double)Dh[0] + S1 * (double)Dh[1]);
+                else if (fmt == ORC_FP2M)
                     y[(int64_t)j * N + n] += (double)xs[(int64_t)j * nb + b] * (S * (double)D + M * (double)X);
                 else
                     y[(int64_t)j * N + n] += S * (double)xs[(int64_t)j * nb + b] * (double)D;

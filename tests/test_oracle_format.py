@@ -502,3 +502,99 @@ def test_q8_range_errors():
     w[3] = np.inf
     with pytest.raises(O.OracleError):
         O.quantize_block(Q8, w)
+
+
+# ---------------------------------------------- FP2S (two 16-weight scales)
+# The FP2 codes and codebook; weights 0..15 take the fp16 scale s0, weights
+# 16..31 the fp16 scale s1, each half encoded as an FP2 block of its own.
+
+FP2S = O.FP2S
+
+
+def test_fp2s_sizes_codebook_and_layout():
+    assert O.block_bytes(FP2S) == 12 and O.code_bytes(FP2S) == 8
+    assert [O.codebook(FP2S, c) for c in range(4)] == [O.codebook(2, c) for c in range(4)]
+    rng = np.random.default_rng(90)
+    for _ in range(20):
+        codes = rng.integers(0, 4, 32)
+        assert bytes(O.pack_codes(FP2S, codes)) == bytes(O.pack_codes(2, codes))
+
+
+def test_fp2s_each_half_is_an_fp2_block():
+    """Half h of an FP2S block equals the first half of the FP2 encoding of
+    the block [w_h, w_h] (same amax, so the same scale and codes): the FP2
+    encoder, pinned on its own, pins the per-half scale and codes."""
+    for w in _random_blocks(91) + [np.r_[np.zeros(16), np.full(16, 0.7)].astype(np.float32)]:
+        blk = O.quantize_block(FP2S, w)
+        codes = O.unpack_codes(FP2S, blk)
+        for h in range(2):
+            half = w[16 * h:16 * h + 16]
+            ref = O.quantize_block(2, np.r_[half, half].astype(np.float32))
+            assert O.weight_scale(FP2S, blk, 16 * h) == O.block_scale(2, ref)
+            assert all(O.weight_scale(FP2S, blk, t) == O.weight_scale(FP2S, blk, 16 * h)
+                       for t in range(16 * h, 16 * h + 16))
+            assert np.array_equal(codes[16 * h:16 * h + 16], O.unpack_codes(2, ref)[:16])
+            d = O.dequantize_block(FP2S, blk)[16 * h:16 * h + 16]
+            assert np.array_equal(d, O.dequantize_block(2, ref)[:16])
+
+
+def test_fp2s_equal_halves_reduce_to_fp2():
+    """With the same amax in both halves the two scales equal FP2's one
+    scale and the block decodes to the FP2 block exactly."""
+    rng = np.random.default_rng(92)
+    for _ in range(40):
+        w = (rng.standard_normal(32) * 0.02).astype(np.float32)
+        w[rng.integers(0, 16)] = np.float32(0.09)
+        w[16 + rng.integers(0, 16)] = np.float32(-0.09)
+        b2, bs = O.quantize_block(2, w), O.quantize_block(FP2S, w)
+        assert O.weight_scale(FP2S, bs, 0) == O.weight_scale(FP2S, bs, 31) == O.block_scale(2, b2)
+        assert np.array_equal(O.dequantize_block(FP2S, bs), O.dequantize_block(2, b2))
+
+
+def test_fp2s_power_of_two_equivariance():
+    for w in _random_blocks(93, 100):
+        b = O.quantize_block(FP2S, w)
+        s0, s1 = O.weight_scale(FP2S, b, 0), O.weight_scale(FP2S, b, 16)
+        for k in (-3, 2):
+            # every scale normal fp16 before and after (a subnormal one has
+            # fewer bits)
+            ok = all(s == 0 or (6.2e-5 < s < 6.0e4 and 6.2e-5 < s * 2.0 ** k < 6.0e4) for s in (s0, s1))
+            if not ok:
+                continue
+            bk = O.quantize_block(FP2S, (w * np.float32(2.0 ** k)).astype(np.float32))
+            assert np.array_equal(O.unpack_codes(FP2S, bk), O.unpack_codes(FP2S, b))
+            assert O.weight_scale(FP2S, bk, 0) == s0 * 2.0 ** k
+            assert O.weight_scale(FP2S, bk, 16) == s1 * 2.0 ** k
+
+
+def test_fp2s_gemv_is_the_dequantized_product():
+    """The oracle's per-block s * (S0 D0 + S1 D1) against the plain fp64 sum
+    of dequantized weights times dequantized activations (swapped or shared
+    half scales, or a half dot over the wrong weights, fail); the dots are
+    the unit-scale block dots D0 + D1."""
+    rng = np.random.default_rng(94)
+    N, K, Q = 5, 128, 3
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    W[:, 16:32] *= 8.0  # the second half of block 0 on a different scale
+    blocks = O.quantize_matrix(FP2S, W)
+    x = rng.standard_normal((Q, K)).astype(np.float32)
+    xq, xs = O.quantize_act(x)
+    y, dots = O.gemv(FP2S, blocks, xq, xs, want_dots=True)
+    Wd = O.dequantize_matrix(FP2S, blocks)
+    xd = xq.astype(np.float64) * np.repeat(xs.astype(np.float64), 32, axis=1)
+    assert np.allclose(y, xd @ Wd.T, rtol=1e-12, atol=1e-12)
+    vals = np.array([[[O.codebook(FP2S, c) for c in O.unpack_codes(FP2S, blocks[n, b])] for b in range(K // 32)]
+                     for n in range(N)])
+    for j in range(Q):
+        assert np.array_equal(dots[j], (vals * xq[j].reshape(1, K // 32, 32)).sum(-1))
+
+
+def test_fp2s_range_errors():
+    w = np.zeros(32, np.float32)
+    w[20] = np.float32(3.0e5)  # the second half's fp16 scale overflows
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP2S, w)
+    w[20] = 0.0
+    w[3] = np.nan
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP2S, w)
