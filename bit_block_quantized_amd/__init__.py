@@ -23,7 +23,10 @@ FORMATS = (FP2, FP3, FP4)
 FP2M = 12
 # A tier above FP4: 32 int8 codes + an fp16 scale (34 B), GEMV entry points only.
 Q8 = 8
-VARIANT_FORMATS = (FP2M, Q8)
+# Variant: FP2 codes with two fp16 sub-scales, one per 16-weight half (12 B),
+# GEMV entry points only.
+FP2S = 16
+VARIANT_FORMATS = (FP2M, Q8, FP2S)
 
 RFX_OK = 0
 _STATUS = {-1: "RFX_E_INVAL", -2: "RFX_E_ALIGN", -3: "RFX_E_RANGE", -4: "RFX_E_UNSUPPORTED",

@@ -32,9 +32,10 @@ __device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p) { return (sptr_
 
 template <int FMT>
 struct TileFmt {
-    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168 : FMT == RFX_FP2M ? 6144
-                               : FMT == RFX_Q8 ? 17408 : 8704;
-    static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M ? 4 : FMT == RFX_FP3 ? 6
+    static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168
+                               : FMT == RFX_FP2M || FMT == RFX_FP2S ? 6144 : FMT == RFX_Q8 ? 17408 : 8704;
+    static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M || FMT == RFX_FP2S ? 4
+                                     : FMT == RFX_FP3 ? 6
                                      : FMT == RFX_Q8 ? 16 : 8;
     // the activation block sums enter the result (codebook offset or minimum)
     static constexpr bool needs_sum = FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP2M;
@@ -61,6 +62,21 @@ __device__ __forceinline__ Sel8 sel_fp2(uint32_t w0, uint32_t w1)
     s.v[5] = (int)((w1 >> 2) & 0x03030303u);
     s.v[6] = (int)((w1 >> 4) & 0x03030303u);
     s.v[7] = (int)((w1 >> 6) & 0x03030303u);
+    return s;
+}
+
+// FP2S: the codes expanded through FP2's codebook {-3, -1, +1, +3} (bytes
+// FD FF 01 03) by one v_perm per four weights. With the signed values each
+// half's dot is a plain sum: dwords 0-3 are weights 0..15, dwords 4-7
+// weights 16..31, so neither half needs an activation sum.
+constexpr uint32_t kFp2Values = 0x0301FFFDu;
+
+__device__ __forceinline__ Sel8 sel_fp2s(uint32_t w0, uint32_t w1)
+{
+    Sel8 s = sel_fp2(w0, w1);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        s.v[i] = (int)__builtin_amdgcn_perm(0u, kFp2Values, (uint32_t)s.v[i]);
     return s;
 }
 
@@ -132,7 +148,7 @@ template <int FMT>
 struct TileRegs {
     u32x4 c[TileFmt<FMT>::code_chunks];
     u32x4 sc16; // FP2/FP3/FP2M/Q8: eight fp16 scales
-    u32x4 mn16; // FP2M: eight fp16 minima
+    u32x4 mn16; // FP2M: eight fp16 minima; FP2S: the eight second-half scales
     u32x2 sc8;  // FP4: eight e8m0 bytes
 };
 
@@ -170,7 +186,7 @@ __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ t
         RFX_LD(t.c[3], tp + 64 * 3);
     } else {
         RFX_LD(t.sc16, tp + 64 * 4);
-        if (FMT == RFX_FP2M)
+        if (FMT == RFX_FP2M || FMT == RFX_FP2S)
             RFX_LD(t.mn16, tp + 64 * 5);
 #pragma unroll
         for (int k = 0; k < 4; k++)
@@ -187,15 +203,17 @@ __device__ __forceinline__ float half_of(const u32x4 &v, int bi)
     return half_bits_to_float((bi & 1) ? (w2 >> 16) : (w2 & 0xffffu));
 }
 
-// The value added after the scale: FP2M's block minimum, 0 otherwise.
+// A block's second small value: FP2M's minimum (added after the scale),
+// FP2S's second-half scale; 0 for the one-scale formats.
 template <int FMT>
-__device__ __forceinline__ float block_min(const TileRegs<FMT> &t, int bi)
+__device__ __forceinline__ float block_second(const TileRegs<FMT> &t, int bi)
 {
-    return FMT == RFX_FP2M ? half_of(t.mn16, bi) : 0.0f;
+    return FMT == RFX_FP2M || FMT == RFX_FP2S ? half_of(t.mn16, bi) : 0.0f;
 }
 
 // Selector bytes and dequantization scale of block bi (0..7) of a tile.
 // FP2M shares FP2's code layout; its selector byte is the code c itself.
+// FP2S: the signed codebook values; sw is the first half's scale.
 template <int FMT>
 __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel8 &sel, float &sw)
 {
@@ -215,6 +233,8 @@ __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel
             const u32x4 h4 = t.c[4 + (bi >> 2)];
             const uint32_t h = (bi & 3) == 0 ? h4.x : (bi & 3) == 1 ? h4.y : (bi & 3) == 2 ? h4.z : h4.w;
             sel = sel_fp3(w0, w1, h);
+        } else if (FMT == RFX_FP2S) {
+            sel = sel_fp2s(w0, w1);
         } else {
             sel = sel_fp2(w0, w1);
         }
@@ -280,15 +300,24 @@ __device__ __forceinline__ int block_dot(const Sel8 &sel, const XBlock<Q> &xb, i
 }
 
 // FP2M: the block is s * c + m, so its dot is sx * (s D + m X), X the
-// activation block's code sum.
+// activation block's code sum (s2 = m). FP2S: sx * (s0 D0 + s1 D1) over the
+// two halves (sw = s0, s2 = s1).
 template <int FMT, int Q, int NQ>
 __device__ __forceinline__ void accumulate_block(const Sel8 &sel, float sw, const XBlock<Q> &xb,
-                                                 float (&acc)[Q], float mn = 0.0f)
+                                                 float (&acc)[Q], float s2 = 0.0f)
 {
 #pragma unroll
     for (int j = 0; j < NQ; j++) {
-        if (FMT == RFX_FP2M)
-            acc[j] += xb.sx[j] * (sw * (float)block_dot<FMT, Q>(sel, xb, j) + mn * (float)xb.sum[j]);
+        if (FMT == RFX_FP2S) {
+            int d0 = 0, d1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                d0 = __builtin_amdgcn_sdot4(sel.v[i], xb.x[j][i], d0, false);
+                d1 = __builtin_amdgcn_sdot4(sel.v[4 + i], xb.x[j][4 + i], d1, false);
+            }
+            acc[j] += xb.sx[j] * (sw * (float)d0 + s2 * (float)d1);
+        } else if (FMT == RFX_FP2M)
+            acc[j] += xb.sx[j] * (sw * (float)block_dot<FMT, Q>(sel, xb, j) + s2 * (float)xb.sum[j]);
         else
             acc[j] += (sw * xb.sx[j]) * (float)block_dot<FMT, Q>(sel, xb, j);
     }
@@ -312,12 +341,12 @@ __device__ __forceinline__ void tile_blocks(const TileRegs<FMT> &t, int b0, int 
         Sel8 sel;
         float sw;
         decode_block<FMT>(t, bi, sel, sw);
-        float mn = block_min<FMT>(t, bi);
+        float s2 = block_second<FMT>(t, bi);
         if (!FULL) {
             sw = b0 + bi < nb ? sw : 0.0f;
-            mn = b0 + bi < nb ? mn : 0.0f;
+            s2 = b0 + bi < nb ? s2 : 0.0f;
         }
-        accumulate_block<FMT, Q, NQ>(sel, sw, xb, acc, mn);
+        accumulate_block<FMT, Q, NQ>(sel, sw, xb, acc, s2);
         // keep each block's work after its own chunk wait (the scheduler
         // would otherwise hoist the decodes and wait for the whole tile)
         __builtin_amdgcn_sched_barrier(0);

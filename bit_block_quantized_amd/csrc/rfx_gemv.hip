@@ -27,7 +27,9 @@
 //     the selector bytes go straight into v_dot4 and the offset is folded in
 //     once per block with the precomputed activation block sum (the FP2M
 //     variant's block minimum enters the same way, as m times that sum,
-//     after the scale); FP4 (E2M1,
+//     after the scale; the FP2S variant expands its codes to the signed
+//     values with one v_perm_b32 per four weights and keeps the dots of
+//     its two 16-weight halves apart, one per sub-scale); FP4 (E2M1,
 //     not affine) expands through two v_perm_b32 table lookups and a v_perm
 //     merge on the sign bit;
 //   - the 256-column tiles of a row group are split into contiguous runs over
@@ -470,6 +472,7 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
         RFX_JOB(RFX_FP4, 1) RFX_JOB(RFX_FP4, 2) RFX_JOB(RFX_FP4, 3) RFX_JOB(RFX_FP4, 4)
         RFX_JOB(RFX_FP2M, 1) RFX_JOB(RFX_FP2M, 2) RFX_JOB(RFX_FP2M, 3) RFX_JOB(RFX_FP2M, 4)
         RFX_JOB(RFX_Q8, 1) RFX_JOB(RFX_Q8, 2) RFX_JOB(RFX_Q8, 3) RFX_JOB(RFX_Q8, 4)
+        RFX_JOB(RFX_FP2S, 1) RFX_JOB(RFX_FP2S, 2) RFX_JOB(RFX_FP2S, 3) RFX_JOB(RFX_FP2S, 4)
     default: break;
     }
 #undef RFX_JOB
@@ -529,6 +532,7 @@ int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
     case RFX_FP4: return full ? launch_q<RFX_FP4, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP4, DOTS, false>(a, q, G, W, st);
     case RFX_FP2M: return full ? launch_q<RFX_FP2M, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2M, DOTS, false>(a, q, G, W, st);
     case RFX_Q8: return full ? launch_q<RFX_Q8, DOTS, true>(a, q, G, W, st) : launch_q<RFX_Q8, DOTS, false>(a, q, G, W, st);
+    case RFX_FP2S: return full ? launch_q<RFX_FP2S, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2S, DOTS, false>(a, q, G, W, st);
     }
     return fail(RFX_E_INVAL, "unknown format");
 }
@@ -680,7 +684,7 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         order[j] = j;
     auto cost = [&](int j) {
         const int f = jobs[j].W.fmt, q = jobs[j].q;
-        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : f == RFX_FP2M ? 38 : f == RFX_Q8 ? 20 : 75;
+        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : f == RFX_FP2M || f == RFX_FP2S ? 38 : f == RFX_Q8 ? 20 : 75;
         return base + 12 * q;
     };
     for (int i = 1; i < n_jobs; i++) // stable insertion sort, n <= 16

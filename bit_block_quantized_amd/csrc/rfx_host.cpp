@@ -85,19 +85,20 @@ const char *rfx_version(void) { return "rfx 0.1 gfx950"; }
 
 int rfx_block_bytes(int fmt)
 {
-    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M ? 12
+    return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M || fmt == RFX_FP2S ? 12
          : fmt == RFX_Q8 ? 34 : RFX_E_INVAL;
 }
 
 int rfx_code_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP2M ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16
+    return fmt == RFX_FP2 || fmt == RFX_FP2M || fmt == RFX_FP2S ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16
          : fmt == RFX_Q8 ? 32 : RFX_E_INVAL;
 }
 
 int rfx_scale_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_Q8 ? 2 : fmt == RFX_FP4 ? 1 : fmt == RFX_FP2M ? 4
+    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_Q8 ? 2 : fmt == RFX_FP4 ? 1
+         : fmt == RFX_FP2M || fmt == RFX_FP2S ? 4
          : RFX_E_INVAL;
 }
 
@@ -140,7 +141,7 @@ inline void put_code(int fmt, uint8_t *codes, int t, int c)
 {
     if (fmt == RFX_Q8) {
         codes[t] = (uint8_t)c;
-    } else if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
+    } else if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         codes[4 * m + j] |= (uint8_t)((c & 3) << (2 * i));
         if (fmt == RFX_FP3)
@@ -155,7 +156,7 @@ inline int get_code(int fmt, const uint8_t *codes, int t)
 {
     if (fmt == RFX_Q8)
         return codes[t];
-    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M) {
+    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         int c = (codes[4 * m + j] >> (2 * i)) & 3;
         if (fmt == RFX_FP3)
@@ -169,7 +170,7 @@ inline int get_code(int fmt, const uint8_t *codes, int t)
 inline int code_value(int fmt, int c)
 {
     static const int mag[8] = {0, 1, 2, 3, 4, 6, 8, 12};
-    if (fmt == RFX_FP2)
+    if (fmt == RFX_FP2 || fmt == RFX_FP2S)
         return 2 * c - 3;
     if (fmt == RFX_FP3)
         return 2 * c - 7;
@@ -233,6 +234,25 @@ int encode_fp2m(const float *w, uint8_t *blk)
     return RFX_OK;
 }
 
+// FP2S: each 16-weight half is an FP2 block of its own: its scale is the
+// half's amax over three rounded to fp16, its codes are FP2's.
+int encode_fp2s(const float *w, uint8_t *blk)
+{
+    for (int h = 0; h < 2; h++) {
+        float amax = 0.0f;
+        for (int t = 16 * h; t < 16 * h + 16; t++)
+            amax = std::fmax(amax, std::fabs(w[t]));
+        const _Float16 sh = (_Float16)(amax / 3.0f); // fp32 division, then RNE to binary16
+        const float s = (float)sh;
+        if (std::isinf(s))
+            return fail(RFX_E_RANGE, "fp16 scale overflow (half %d, amax %g)", h, (double)amax);
+        for (int t = 16 * h; t < 16 * h + 16; t++)
+            put_code(RFX_FP2S, blk, t, s == 0.0f ? 2 : code_fp2(w[t] / s));
+        put_half(blk + 8 + 2 * h, sh);
+    }
+    return RFX_OK;
+}
+
 int encode_block(int fmt, const float *w, uint8_t *blk)
 {
     const int cb = rfx_code_bytes(fmt);
@@ -245,6 +265,8 @@ int encode_block(int fmt, const float *w, uint8_t *blk)
     std::memset(blk, 0, (size_t)rfx_block_bytes(fmt));
     if (fmt == RFX_FP2M)
         return encode_fp2m(w, blk);
+    if (fmt == RFX_FP2S)
+        return encode_fp2s(w, blk);
     if (fmt == RFX_Q8) {
         const _Float16 h = (_Float16)(amax / 127.0f); // fp32 division, then RNE to binary16
         const float s = (float)h;
@@ -293,7 +315,7 @@ struct TilePos {
     size_t code0;  // first 8 or 16 code bytes
     size_t code1;  // FP3: the 4 high-bit bytes
     size_t scale;  // scale byte(s)
-    size_t min;    // FP2M: the fp16 minimum
+    size_t second; // FP2M: the fp16 minimum; FP2S: the second half's fp16 scale
 };
 
 inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
@@ -317,7 +339,7 @@ inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
             p.scale = tile + 6 * kChunk + lane * 16 + bi * 2;
         } else {
             p.scale = tile + 4 * kChunk + lane * 16 + bi * 2;
-            p.min = tile + 5 * kChunk + lane * 16 + bi * 2;
+            p.second = tile + 5 * kChunk + lane * 16 + bi * 2;
         }
     }
     return p;
@@ -339,8 +361,8 @@ void place_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *blk
         if (fmt == RFX_FP3)
             std::memcpy(tiled + p.code1, blk + 8, 4);
         std::memcpy(tiled + p.scale, blk + cb, 2);
-        if (fmt == RFX_FP2M)
-            std::memcpy(tiled + p.min, blk + cb + 2, 2);
+        if (fmt == RFX_FP2M || fmt == RFX_FP2S)
+            std::memcpy(tiled + p.second, blk + cb + 2, 2);
     }
 }
 
@@ -360,8 +382,8 @@ void fetch_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *til
         if (fmt == RFX_FP3)
             std::memcpy(blk + 8, tiled + p.code1, 4);
         std::memcpy(blk + cb, tiled + p.scale, 2);
-        if (fmt == RFX_FP2M)
-            std::memcpy(blk + cb + 2, tiled + p.min, 2);
+        if (fmt == RFX_FP2M || fmt == RFX_FP2S)
+            std::memcpy(blk + cb + 2, tiled + p.second, 2);
     }
 }
 
@@ -435,8 +457,9 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32)
     const int cb = rfx_code_bytes(fmt);
     const float s = fmt == RFX_FP4 ? std::ldexp(1.0f, (int)blk[cb] - 128) : get_half(blk + cb);
     const float m = fmt == RFX_FP2M ? get_half(blk + cb + 2) : 0.0f;
+    const float s1 = fmt == RFX_FP2S ? get_half(blk + cb + 2) : s; // FP2S: weights 16..31
     for (int t = 0; t < 32; t++)
-        w32[t] = s * (float)code_value(fmt, get_code(fmt, blk, t)) + m;
+        w32[t] = (t < 16 ? s : s1) * (float)code_value(fmt, get_code(fmt, blk, t)) + m;
     return RFX_OK;
 }
 

@@ -55,8 +55,8 @@ __device__ __forceinline__ Sel8 sel2_fp3(uint32_t w0, uint32_t w1, uint32_t h)
     return s;
 }
 
-// Selector bytes (2c for FP2/FP3, c for FP2M, signed values for FP4) and
-// the weight scale of block BI of a tile.
+// Selector bytes (2c for FP2/FP3, c for FP2M, signed values for FP4 and
+// FP2S) and the weight scale of block BI of a tile (FP2S: its first half's).
 template <int FMT, int BI>
 __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel, float &sw)
 {
@@ -75,6 +75,8 @@ __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel,
             sel = sel2_fp3(w0, w1, h);
         } else if (FMT == RFX_FP2M) {
             sel = sel_fp2(w0, w1);
+        } else if (FMT == RFX_FP2S) {
+            sel = sel_fp2s(w0, w1);
         } else {
             sel = sel2_fp2(w0, w1);
         }
@@ -153,13 +155,15 @@ __device__ __forceinline__ i32x4 mfma_step(i32x4 d, const u32x4 &x, int w)
 }
 
 // Exact block dots of block BI for the four column slots (slot j is
-// column j for j < Q). Two accumulation chains of four steps each, so
-// consecutive matrix ops do not wait on one another; FP2 / FP3 start the
-// first chain at -off * sum(x) (the codebook offset).
+// column j for j < Q), as two accumulation chains of four steps each, so
+// consecutive matrix ops do not wait on one another: d0 takes weights
+// 0..15, d1 weights 16..31 (FP2S's two halves). FP2 / FP3 start d0 at
+// -off * sum(x) (the codebook offset), so only d0 + d1 means anything.
 template <int FMT, int Q, int BI>
-__device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt)
+__device__ __forceinline__ void block_half_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt, i32x4 &d0, i32x4 &d1)
 {
-    i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+    d0 = i32x4{0, 0, 0, 0};
+    d1 = i32x4{0, 0, 0, 0};
     if (FMT == RFX_FP2 || FMT == RFX_FP3) {
 #pragma unroll
         for (int j = 0; j < Q; j++)
@@ -173,6 +177,13 @@ __device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q
     d1 = mfma_step<BI, 6>(d1, xt.code, sel.v[6]);
     d0 = mfma_step<BI, 3>(d0, xt.code, sel.v[3]);
     d1 = mfma_step<BI, 7>(d1, xt.code, sel.v[7]);
+}
+
+template <int FMT, int Q, int BI>
+__device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt)
+{
+    i32x4 d0, d1;
+    block_half_dots_mfma<FMT, Q, BI>(sel, xt, d0, d1);
     return d0 + d1;
 }
 
@@ -183,17 +194,28 @@ __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XT
     Sel8 sel;
     float sw;
     decode_block2<FMT, BI>(t, sel, sw);
-    float mn = block_min<FMT>(t, BI);
+    float s2 = block_second<FMT>(t, BI);
     if (!FULL) {
         sw = b0 + BI < nb ? sw : 0.0f;
-        mn = b0 + BI < nb ? mn : 0.0f;
+        s2 = b0 + BI < nb ? s2 : 0.0f;
+    }
+    if (FMT == RFX_FP2S) { // sx * (s0 D0 + s1 D1)
+        i32x4 d0, d1;
+        block_half_dots_mfma<FMT, Q, BI>(sel, xt, d0, d1);
+#pragma unroll
+        for (int j = 0; j < Q; j++) {
+            const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+            acc[j] += sxb * (sw * (float)d0[j] + s2 * (float)d1[j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return;
     }
     const i32x4 d = block_dots_mfma<FMT, Q, BI>(sel, xt);
 #pragma unroll
     for (int j = 0; j < Q; j++) {
         const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
         if (FMT == RFX_FP2M) // sx * (s D + m X)
-            acc[j] += sxb * (sw * (float)d[j] + mn * (float)bcast_row<BI>(xt.nsum[j]));
+            acc[j] += sxb * (sw * (float)d[j] + s2 * (float)bcast_row<BI>(xt.nsum[j]));
         else
             acc[j] += (sw * sxb) * (float)d[j];
     }

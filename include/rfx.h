@@ -52,7 +52,7 @@ enum {
 /* Block formats. A block is 32 consecutive weights of one row along the
  * reduction dimension, stored as packed codes plus one scale ([HM] para 2
  * lets a block carry a single small scale or a pair; the three named formats
- * here use one, the FP2M variant two).
+ * here use one, the FP2M and FP2S variants two).
  *   RFX_FP2: 2-bit codes, codebook {-3,-1,+1,+3}, fp16 scale: 10 B / block
  *   RFX_FP3: 3-bit codes, codebook {-7,-5,...,+7}, fp16 scale: 14 B / block
  *   RFX_FP4: 4-bit OCP E2M1 codes (value = 2 x E2M1, |v| <= 12), one e8m0
@@ -68,16 +68,21 @@ enum {
  *   RFX_Q8:  a tier above FP4 (the same paragraph keeps dense and sensitive
  *            projections at FP4 or higher; this tier is a reading): 32 int8
  *            codes in weight order, then an fp16 scale s; weight = s * c:
- *            34 B / block (8.5 bits per weight). Same support as RFX_FP2M. */
-enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_Q8 = 8, RFX_FP2M = 12 };
+ *            34 B / block (8.5 bits per weight). Same support as RFX_FP2M.
+ *   RFX_FP2S: variant with two sub-scales (the same paragraph's pair of
+ *            small values read as two scales): FP2 codes and codebook;
+ *            weights 0..15 take fp16 scale s0, weights 16..31 fp16 scale
+ *            s1; codes, s0, s1: 12 B / block (3.0 bits per weight). Same
+ *            support as RFX_FP2M. */
+enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_Q8 = 8, RFX_FP2M = 12, RFX_FP2S = 16 };
 
 const char *rfx_status_str(int status);
 const char *rfx_last_error(void);
 const char *rfx_version(void);
 
-int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M) / 34 (Q8), or RFX_E_INVAL */
-int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 / 32 */
-int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 */
+int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M) / 34 (Q8) / 12 (FP2S), or RFX_E_INVAL */
+int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 / 32 / 8 */
+int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 / 4 */
 
 /* ------------------------------------------------------------------ */
 /* Host-side encoder (synchronous, host memory).                       */
@@ -97,8 +102,11 @@ int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 */
  * Q8: s = fp16_rne(amax / 127) in fp32; code = clamp(round half to even of
  * w / s in fp32, -127, 127) stored as the two's-complement byte; s = 0
  * codes every weight as 0. Code byte t is weight t.
+ * FP2S: each half h (weights 16h..16h+15) is encoded as an FP2 block with
+ * its own amax: s_h = fp16_rne(amax_h / 3) in fp32, FP2 codes and ties;
+ * s_h = 0 codes the half's weights as +1. Block: codes, s0, s1 (fp16 LE).
  * Bit layout of the code bytes, as little-endian 32-bit words:
- *   FP2 (and FP2M): weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
+ *   FP2 (and FP2M, FP2S): weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
  *   FP3: low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
  *        at word 2 bit 8j+i
  *   FP4: weight 8m+4i+j (m<4, i<2, j<4) at word m bits [8j+4i, 8j+4i+4)
@@ -124,6 +132,8 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
  *   FP4 (tile 8704 B): chunks 0-7 = codes of block c; then 64 rows x 8 B of
  *       e8m0 scales at byte 8192 + r * 8.
  *   FP2M (tile 6144 B): chunks 0-4 as FP2; chunk 5 = the eight fp16 minima.
+ *   FP2S (tile 6144 B): chunks 0-3 as FP2; chunk 4 = the eight first-half
+ *       scales s0; chunk 5 = the eight second-half scales s1.
  *   Q8 (tile 17408 B): chunk 2b + h = code bytes 16h..16h+15 of block b;
  *       chunk 16 = the eight fp16 scales.
  * Rows beyond `rows` and blocks beyond cols/32 are zero (scale 0). Block
@@ -214,7 +224,9 @@ size_t rfx_gemv_grouped_workspace_bytes(const rfx_gemv_job *jobs, int n_jobs);
 int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_bytes, void *stream);
 
 /* Test hook: the same decode path, storing every per-block integer dot
- * D[j][n][b] (int32 [q][N][K/32]) instead of the scaled sum. */
+ * D[j][n][b] (int32 [q][N][K/32]) instead of the scaled sum: the dot of the
+ * block's codebook values with the activation codes (FP2M: of the codes
+ * 0..3; FP2S: over both halves, D0 + D1). */
 int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,
                          int32_t *dots, void *stream);
 
@@ -233,7 +245,7 @@ int rfx_read_reference(const void *buf, size_t bytes, uint32_t *out, int n_out, 
 /* Routed experts: gate and up (rows = inter, cols = hidden) and down
  * (rows = hidden, cols = inter), `n_experts` stacked each ([HM] para 2 and
  * [KK] ROCmFPX section: gate/up in FP2, down in FP3; any of RFX_FP2, RFX_FP3
- * and RFX_FP4 is accepted, RFX_FP2M is not). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
+ * and RFX_FP4 is accepted, RFX_FP2M, RFX_FP2S and RFX_Q8 are not). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
  * or sh_gate.data == NULL for none. Router: fp32 [n_experts][hidden]
  * weights and an optional fp32 [n_experts] bias. */
 typedef struct rfx_moe_layer {

@@ -16,7 +16,9 @@ pytestmark = pytest.mark.gpu
 FMTS = (2, 3, 4)
 FP2M = R.FP2M
 Q8 = R.Q8
-GEMV_FMTS = FMTS + (FP2M, Q8)  # the GEMV entry points also take the FP2M variant and the Q8 tier
+FP2S = R.FP2S
+# the GEMV entry points also take the FP2M and FP2S variants and the Q8 tier
+GEMV_FMTS = FMTS + (FP2M, Q8, FP2S)
 
 
 def _sync(torch):
@@ -93,7 +95,7 @@ _BIG = {}
 
 def _big(fmt):
     if fmt not in _BIG:
-        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30, Q8: 40}[fmt], outliers=True)
+        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30, Q8: 40, FP2S: 50}[fmt], outliers=True)
         _BIG[fmt] = (W, O.quantize_matrix(fmt, W))
     return _BIG[fmt]
 
@@ -168,6 +170,24 @@ def test_gemv_fp2m_offset_rows(q):
         assert rel_err(y, yo) <= TOL, (split, rel_err(y, yo))
 
 
+@pytest.mark.parametrize("q", [1, 4])
+def test_gemv_fp2s_halves_on_different_scales(q):
+    """FP2S with the two halves of every block on scales 2^4 apart (the
+    case the second scale is for; a half dot over the wrong weights or the
+    scales swapped is far off), ragged K so both scales of blocks past K
+    must be dropped."""
+    torch = need_gpu()
+    say(f"gemv fp2s half scales q={q}")
+    N, K = 300, 1312
+    W = inputgen.dense_weight(N, K, seed=95)
+    W.reshape(N, K // 32, 32)[:, :, 16:] *= np.float32(16.0)
+    x = inputgen.activations(q, K, seed=96)
+    for split in (False, True):
+        y, d, yo, do = _run(torch, FP2S, W, x, q, split)
+        assert np.array_equal(d, do)
+        assert rel_err(y, yo) <= TOL, (split, rel_err(y, yo))
+
+
 def test_read_reference_folds_every_word():
     """The streaming-read reference (a measurement aid) reads every word:
     the XOR of its per-workgroup folds equals numpy's XOR of the buffer,
@@ -228,6 +248,8 @@ def _grouped(torch, specs, seed, big=False):
     [(12, 1, 200, 544), (2, 4, 130, 2080), (12, 4, 65, 1024), (12, 2, 1, 32), (4, 1, 256, 512)],
     # the Q8 tier (one tile buffer) beside the others, a multi-tile K split
     [(8, 1, 300, 4096), (8, 4, 65, 1312), (3, 2, 130, 2048), (8, 3, 1, 32)],
+    # the FP2S variant beside the others, ragged and full tiles
+    [(16, 1, 200, 544), (16, 4, 130, 2080), (12, 2, 65, 1024), (16, 3, 1, 32), (2, 4, 256, 512)],
 ])
 def test_gemv_grouped_small(specs):
     torch = need_gpu()

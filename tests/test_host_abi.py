@@ -16,7 +16,7 @@ import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FMTS = (2, 3, 4)
-ALL_FMTS = (2, 3, 4, 12, 8)  # the three named formats, the FP2M variant, the Q8 tier
+ALL_FMTS = (2, 3, 4, 12, 8, 16)  # the named formats, the FP2M variant, the Q8 tier, the FP2S variant
 
 
 def _header_functions():
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def test_sizes():
     for fmt, (bb, cb, sb, tile) in {2: (10, 8, 2, 5120), 3: (14, 12, 2, 7168),
                                      4: (17, 16, 1, 8704), 12: (12, 8, 4, 6144),
-                                     8: (34, 32, 2, 17408)}.items():
+                                     8: (34, 32, 2, 17408), 16: (12, 8, 4, 6144)}.items():
         assert R.block_bytes(fmt) == bb == O.block_bytes(fmt)
         assert R.code_bytes(fmt) == cb and R.scale_bytes(fmt) == sb
         assert R.qmat_bytes(fmt, 64, 256) == tile == 64 * 8 * bb
@@ -80,6 +80,15 @@ def _adversarial_blocks():
         blocks.append(w)
     blocks.append((rng.standard_normal(32) * 0.01 + 40.0).astype(np.float32))
     blocks.append(np.linspace(-65000.0, 60000.0, 32).astype(np.float32))
+    # FP2S: halves on scales 2^33 apart, one half zero, one half underflowing
+    # to a zero fp16 scale, exact ties in the second half only
+    blocks.append(np.r_[np.full(16, 1e-6), np.full(16, 1e4)].astype(np.float32))
+    blocks.append(np.r_[np.zeros(16), rng.standard_normal(16)].astype(np.float32))
+    blocks.append(np.r_[np.full(16, 1e-9), rng.standard_normal(16)].astype(np.float32))
+    w = np.zeros(32, np.float32)
+    w[16:22] = [3.0, 2.0, -2.0, 0.0, -0.0, 1.0]
+    w[0] = 0.7
+    blocks.append(w)
     return blocks
 
 
@@ -89,8 +98,13 @@ def test_host_encoder_matches_oracle(fmt):
         a = R.quantize_block(fmt, w)
         b = O.quantize_block(fmt, w)
         assert bytes(a) == bytes(b), (fmt, w)
-        assert np.array_equal(R.dequantize_block(fmt, a).astype(np.float64),
-                              O.dequantize_block(fmt, b))
+        # the host decoder returns fp32: exact for s * v (an fp16 times a
+        # small integer); FP2M's s * c + m is the fp32 rounding of the exact
+        # value (one rounding, the product being exact)
+        ref = O.dequantize_block(fmt, b)
+        if fmt == 12:
+            ref = ref.astype(np.float32).astype(np.float64)
+        assert np.array_equal(R.dequantize_block(fmt, a).astype(np.float64), ref)
 
 
 @pytest.mark.parametrize("fmt", ALL_FMTS)
@@ -139,7 +153,7 @@ def test_tiled_layout_positions():
             else:
                 sc = tile + 4 * 1024 + lane * 16 + bi * 2
                 assert list(t[sc:sc + 2]) == [9, 10]
-                if fmt == 12:
+                if fmt in (12, 16):  # FP2M's minimum, FP2S's second scale
                     mn = tile + 5 * 1024 + lane * 16 + bi * 2
                     assert list(t[mn:mn + 2]) == [11, 12]
         assert int(t.astype(np.int64).sum()) == int(np.arange(1, bb + 1).sum())
@@ -225,7 +239,7 @@ def test_device_entry_validation_without_gpu():
 
 
 def test_moe_rejects_the_gemv_only_variant():
-    """The MoE and prefill layers refuse FP2M before any HIP call."""
+    """The MoE and prefill layers refuse FP2M and FP2S before any HIP call."""
     L = R.lib()
     good = 0x7f0000000000
     f = _fake(good)
@@ -239,6 +253,9 @@ def test_moe_rejects_the_gemv_only_variant():
     lay.down.fmt = 12
     st = L.rfx_moe_route_topk(ctypes.byref(lay), f, 1, 2, f, f, f, f, f, f, f, f, 1 << 20, None)
     assert st == -4
+    lay.down.fmt = 16
+    st = L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, 1 << 20, None)
+    assert st == -4 and b"FP2S" in L.rfx_last_error()
 
 
 def test_read_reference_validation_without_gpu():
