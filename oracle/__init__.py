@@ -43,7 +43,10 @@ Q8 = 8
 # 12 B): the second of the two small values a block may carry is a second
 # scale; a reading.
 FP2S = 16
-VARIANT_FORMATS = (FP2M, Q8, FP2S)
+# A 3-bit tier at about 3.3 bits per weight (the figure another system on
+# the pages gives for its 3-bit experts): FP3 codes + an e8m0 byte, 13 B.
+FP3E = 13
+VARIANT_FORMATS = (FP2M, Q8, FP2S, FP3E)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIBPATH = os.path.join(_HERE, "liboracle.so")

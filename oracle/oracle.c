@@ -48,6 +48,12 @@
  *         s1 of weights 16..31 = 12 bytes (3.0 bits per weight);
  *         weight t = s_(t/16) * (2c - 3), each half encoded as FP2 is.
  *
+ * A 3-bit tier at about 3.3 bits per weight including scales (the figure
+ * another system on the pages gives for its 3-bit experts, without a
+ * layout; this one is a reading):
+ *   FP3E: the FP3 code bytes + one e8m0 exponent byte E = 13 bytes
+ *         (3.25 bits per weight); weight = 2^(E - 127) * (2c - 7).
+ *
  * A tier above FP4 for the dense and sensitive projections (the same
  * paragraph keeps those at FP4 or a wider format without naming one; this
  * tier is a reading):
@@ -65,6 +71,7 @@
 #define ORC_FP2M 12
 #define ORC_Q8 8
 #define ORC_FP2S 16
+#define ORC_FP3E 13
 
 #define ORC_OK 0
 #define ORC_E_INVAL (-1)
@@ -80,6 +87,7 @@ int orc_block_bytes(int fmt)
     case ORC_FP2M: return 12; /* Reading: 8 code bytes + two fp16 values */
     case ORC_Q8: return 34;   /* Reading: 32 int8 codes + an fp16 scale */
     case ORC_FP2S: return 12; /* Reading: 8 code bytes + two fp16 scales */
+    case ORC_FP3E: return 13; /* Reading: 12 code bytes + an e8m0 byte */
     }
     return ORC_E_INVAL;
 }
@@ -93,6 +101,7 @@ int orc_code_bytes(int fmt)
     case ORC_FP2M: return 8;
     case ORC_Q8: return 32;
     case ORC_FP2S: return 8;
+    case ORC_FP3E: return 12;
     }
     return ORC_E_INVAL;
 }
@@ -168,14 +177,16 @@ uint16_t orc_f32_to_f16(float f)
  *      decodes to 0 and the encoder never emits it.
  * FP2M: the integer part is the code itself, 0..3; the block's minimum is
  *      added after the scale (weight = s * c + m).
- * FP2S: FP2's codebook; the scale depends on the half of the block. */
+ * FP2S: FP2's codebook; the scale depends on the half of the block.
+ * FP3E: FP3's codebook; the scale is a power of two. */
 int orc_codebook(int fmt, int code)
 {
     static const int fp4_mag[8] = {0, 1, 2, 3, 4, 6, 8, 12};
     switch (fmt) {
     case ORC_FP2:
     case ORC_FP2S: return 2 * code - 3;
-    case ORC_FP3: return 2 * code - 7;
+    case ORC_FP3:
+    case ORC_FP3E: return 2 * code - 7;
     case ORC_FP4: return (code & 8) ? -fp4_mag[code & 7] : fp4_mag[code & 7];
     case ORC_FP2M: return code;
     case ORC_Q8: return (int)(int8_t)(uint8_t)code; /* the byte as two's complement */
@@ -185,7 +196,7 @@ int orc_codebook(int fmt, int code)
 
 static int n_codes(int fmt)
 {
-    return fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S ? 4 : fmt == ORC_FP3 ? 8 : fmt == ORC_Q8 ? 256 : 16;
+    return fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S ? 4 : fmt == ORC_FP3 || fmt == ORC_FP3E ? 8 : fmt == ORC_Q8 ? 256 : 16;
 }
 
 /* Nearest codebook value to t, by brute force over every code.
@@ -235,7 +246,7 @@ int orc_nearest_code(int fmt, double t)
 /* Code words are little-endian 32-bit words.
  * FP2 (and FP2M, FP2S): word m (0..1) holds weights 16m..16m+15; weight
  *      16m + 4i + j (i, j in 0..3) occupies bits [8j + 2i, 8j + 2i + 2).
- * FP3: words 0..1 hold the low two bits of every code exactly as FP2;
+ * FP3 (and FP3E): words 0..1 hold the low two bits of every code exactly as FP2;
  *      word 2 holds the high bit, weight 4i + j (i in 0..7, j in 0..3) at
  *      bit 8j + i.
  * FP4: word m (0..3) holds weights 8m..8m+7; weight 8m + 4i + j (i in 0..1)
@@ -260,7 +271,7 @@ void orc_unpack_codes(int fmt, const uint8_t *blk, int *codes)
         if (fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             codes[t] = (int)((rd32(blk + 4 * m) >> (8 * j + 2 * i)) & 3u);
-        } else if (fmt == ORC_FP3) {
+        } else if (fmt == ORC_FP3 || fmt == ORC_FP3E) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             int lo = (int)((rd32(blk + 4 * m) >> (8 * j + 2 * i)) & 3u);
             int ih = t / 4, jh = t % 4;
@@ -287,7 +298,7 @@ void orc_pack_codes(int fmt, const int *codes, uint8_t *blk)
         if (fmt == ORC_FP2 || fmt == ORC_FP2M || fmt == ORC_FP2S) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             w[m] |= (uint32_t)(codes[t] & 3) << (8 * j + 2 * i);
-        } else if (fmt == ORC_FP3) {
+        } else if (fmt == ORC_FP3 || fmt == ORC_FP3E) {
             int m = t / 16, r = t % 16, i = r / 4, j = r % 4;
             w[m] |= (uint32_t)(codes[t] & 3) << (8 * j + 2 * i);
             int ih = t / 4, jh = t % 4;
@@ -304,12 +315,15 @@ void orc_pack_codes(int fmt, const int *codes, uint8_t *blk)
 /* Dequantization scale S of a block, in int8-codebook units: a weight's
  * value is S * codebook(code).
  * FP2/FP3: S = the fp16 scale. FP4: S = 2^(E - 128) (E the e8m0 byte;
- * the MX scale 2^(E - 127) halved because the codebook is 2 x E2M1). */
+ * the MX scale 2^(E - 127) halved because the codebook is 2 x E2M1).
+ * FP3E: S = 2^(E - 127). */
 double orc_block_scale(int fmt, const uint8_t *blk)
 {
     int cb = orc_code_bytes(fmt);
     if (fmt == ORC_FP4)
         return ldexp(1.0, (int)blk[cb] - 128);
+    if (fmt == ORC_FP3E)
+        return ldexp(1.0, (int)blk[cb] - 127);
     return orc_f16_to_f64((uint16_t)(blk[cb] | (blk[cb + 1] << 8)));
 }
 
@@ -414,6 +428,28 @@ int orc_quantize_block(int fmt, const float *w, uint8_t *blk)
             double tt = ldexp((double)w[t], 128 - E); /* exact */
             codes[t] = orc_nearest_code(fmt, tt);
         }
+        orc_pack_codes(fmt, codes, blk);
+        blk[cb] = (uint8_t)E;
+        return ORC_OK;
+    }
+    if (fmt == ORC_FP3E) {
+        /* Reading: the OCP MX shared-exponent rule with FP3's largest value
+         * 7 (floor(log2 7) = 2): E = floor(log2 amax) - 2 + 127, clamped
+         * to [0, 254], amax = 0 gives E = 0; t = w * 2^(127 - E) (exact);
+         * code = FP3's nearest value, ties to the larger magnitude, 0 to
+         * +1; |t| in [7, 8) saturates at 7. */
+        int E = 0;
+        if (amax > 0.0f) {
+            int ex;
+            frexp((double)amax, &ex);
+            E = (ex - 1) - 2 + 127;
+            if (E < 0)
+                E = 0;
+            if (E > 254)
+                E = 254;
+        }
+        for (int t = 0; t < 32; t++)
+            codes[t] = orc_nearest_code(fmt, ldexp((double)w[t], 127 - E));
         orc_pack_codes(fmt, codes, blk);
         blk[cb] = (uint8_t)E;
         return ORC_OK;

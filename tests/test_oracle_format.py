@@ -598,3 +598,97 @@ def test_fp2s_range_errors():
     w[3] = np.nan
     with pytest.raises(O.OracleError):
         O.quantize_block(FP2S, w)
+
+
+# ------------------------------------------- FP3E (3-bit, e8m0 scale byte)
+# FP3's codes and codebook with a power-of-two scale 2^(E - 127): 13 bytes.
+
+FP3E = O.FP3E
+
+
+def test_fp3e_sizes_codebook_and_layout():
+    assert O.block_bytes(FP3E) == 13 and O.code_bytes(FP3E) == 12
+    assert [O.codebook(FP3E, c) for c in range(8)] == [O.codebook(3, c) for c in range(8)]
+    rng = np.random.default_rng(100)
+    for _ in range(20):
+        codes = rng.integers(0, 8, 32)
+        assert bytes(O.pack_codes(FP3E, codes)) == bytes(O.pack_codes(3, codes))
+
+
+@pytest.mark.parametrize("amax,E", [(1.0, 125), (7.9, 127), (8.0, 128), (3.9, 126), (2.0 ** -126, 0),
+                                    (2.0 ** -100 * 1.5, 25), (3.0e38, 252), (0.0, 0)])
+def test_fp3e_exponent_hand_values(amax, E):
+    """E = floor(log2 amax) - 2 + 127, clamped at 0 (2 = floor(log2 7))."""
+    w = np.zeros(32, np.float32)
+    w[5] = np.float32(amax)
+    assert O.quantize_block(FP3E, w)[12] == E
+
+
+def _fp3e_code(t):
+    """The nearest of -7, -5, ..., 7 to t with ties to the larger magnitude
+    (0 to +1), as a code c = (v + 7) / 2: a closed form, not a search."""
+    u = (t + 7.0) / 2.0
+    c = np.floor(u + 0.5) if t >= 0 else np.ceil(u - 0.5)
+    return int(np.clip(c, 0, 7))
+
+
+def test_fp3e_codes_closed_form_and_error_bound():
+    for w in _random_blocks(101) + [np.zeros(32, np.float32)]:
+        blk = O.quantize_block(FP3E, w)
+        E = int(blk[12])
+        S = 2.0 ** (E - 127)
+        assert O.block_scale(FP3E, blk) == S
+        codes = O.unpack_codes(FP3E, blk)
+        for t in range(32):
+            assert codes[t] == _fp3e_code(float(w[t]) / S), (t, w[t], S)
+        d = O.dequantize_block(FP3E, blk)
+        # half a step inside the codebook's range; amax / S < 8 saturates by < 1
+        assert np.all(np.abs(w.astype(np.float64) - d) <= S)
+
+
+def test_fp3e_equals_fp3_when_its_scale_is_a_power_of_two():
+    """amax = 7 * 2^j: FP3's fp16 scale is exactly 2^j, FP3E's 2^(E-127)
+    is the same, so both decode every weight alike."""
+    rng = np.random.default_rng(102)
+    for j in (-10, -3, 0, 2, 5):
+        for _ in range(10):
+            w = (rng.uniform(-1, 1, 32) * 7 * 2.0 ** j).astype(np.float32)
+            w[rng.integers(0, 32)] = np.float32(7 * 2.0 ** j)
+            b3, be = O.quantize_block(3, w), O.quantize_block(FP3E, w)
+            assert O.block_scale(3, b3) == O.block_scale(FP3E, be) == 2.0 ** j
+            assert np.array_equal(O.dequantize_block(3, b3), O.dequantize_block(FP3E, be))
+
+
+def test_fp3e_power_of_two_equivariance():
+    for w in _random_blocks(103, 100):
+        b = O.quantize_block(FP3E, w)
+        for k in (-3, 2):
+            if not 0 < int(b[12]) + k < 254:
+                continue
+            bk = O.quantize_block(FP3E, (w * np.float32(2.0 ** k)).astype(np.float32))
+            assert np.array_equal(O.unpack_codes(FP3E, bk), O.unpack_codes(FP3E, b))
+            assert int(bk[12]) == int(b[12]) + k
+
+
+def test_fp3e_gemv_is_the_dequantized_product():
+    rng = np.random.default_rng(104)
+    N, K, Q = 5, 128, 3
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    blocks = O.quantize_matrix(FP3E, W)
+    x = rng.standard_normal((Q, K)).astype(np.float32)
+    xq, xs = O.quantize_act(x)
+    y, dots = O.gemv(FP3E, blocks, xq, xs, want_dots=True)
+    Wd = O.dequantize_matrix(FP3E, blocks)
+    xd = xq.astype(np.float64) * np.repeat(xs.astype(np.float64), 32, axis=1)
+    assert np.allclose(y, xd @ Wd.T, rtol=1e-12, atol=1e-12)
+    vals = np.array([[[O.codebook(FP3E, c) for c in O.unpack_codes(FP3E, blocks[n, b])] for b in range(K // 32)]
+                     for n in range(N)])
+    for j in range(Q):
+        assert np.array_equal(dots[j], (vals * xq[j].reshape(1, K // 32, 32)).sum(-1))
+
+
+def test_fp3e_nonfinite_rejected():
+    w = np.zeros(32, np.float32)
+    w[9] = np.inf
+    with pytest.raises(O.OracleError):
+        O.quantize_block(FP3E, w)
