@@ -41,9 +41,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 N = K = 7168
 FORMATS = (2, 3, 4)
-VARIANTS = (12, 8, 16)  # FP2M, Q8 and FP2S: timed per kernel, not part of the step
-SEEDS = {2: 0, 3: 10, 4: 20, 12: 30, 8: 40, 16: 50}
-FMT_NAME = {2: "FP2", 3: "FP3", 4: "FP4", 12: "FP2M", 8: "Q8", 16: "FP2S"}
+VARIANTS = (12, 8, 16, 13)  # FP2M, Q8, FP2S and FP3E: timed per kernel, not part of the step
+SEEDS = {2: 0, 3: 10, 4: 20, 12: 30, 8: 40, 16: 50, 13: 60}
+FMT_NAME = {2: "FP2", 3: "FP3", 4: "FP4", 12: "FP2M", 8: "Q8", 16: "FP2S", 13: "FP3E"}
 LLC_BYTES = 256 << 20
 MOE_H, MOE_I, MOE_E = 4096, 2048, 256
 

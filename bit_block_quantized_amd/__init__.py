@@ -26,7 +26,10 @@ Q8 = 8
 # Variant: FP2 codes with two fp16 sub-scales, one per 16-weight half (12 B),
 # GEMV entry points only.
 FP2S = 16
-VARIANT_FORMATS = (FP2M, Q8, FP2S)
+# A 3-bit tier at about 3.3 bits per weight: FP3 codes + an e8m0 byte (13 B),
+# GEMV entry points only.
+FP3E = 13
+VARIANT_FORMATS = (FP2M, Q8, FP2S, FP3E)
 
 RFX_OK = 0
 _STATUS = {-1: "RFX_E_INVAL", -2: "RFX_E_ALIGN", -3: "RFX_E_RANGE", -4: "RFX_E_UNSUPPORTED",

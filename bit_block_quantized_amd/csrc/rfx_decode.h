@@ -33,12 +33,13 @@ __device__ __forceinline__ sptr_f32 as_scalar_f32(const void *p) { return (sptr_
 template <int FMT>
 struct TileFmt {
     static constexpr int bytes = FMT == RFX_FP2 ? 5120 : FMT == RFX_FP3 ? 7168
-                               : FMT == RFX_FP2M || FMT == RFX_FP2S ? 6144 : FMT == RFX_Q8 ? 17408 : 8704;
+                               : FMT == RFX_FP2M || FMT == RFX_FP2S ? 6144 : FMT == RFX_Q8 ? 17408
+                               : FMT == RFX_FP3E ? 6656 : 8704;
     static constexpr int code_chunks = FMT == RFX_FP2 || FMT == RFX_FP2M || FMT == RFX_FP2S ? 4
-                                     : FMT == RFX_FP3 ? 6
+                                     : FMT == RFX_FP3 || FMT == RFX_FP3E ? 6
                                      : FMT == RFX_Q8 ? 16 : 8;
     // the activation block sums enter the result (codebook offset or minimum)
-    static constexpr bool needs_sum = FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP2M;
+    static constexpr bool needs_sum = FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP2M || FMT == RFX_FP3E;
 };
 
 // ------------------------------------------------------------------
@@ -149,7 +150,7 @@ struct TileRegs {
     u32x4 c[TileFmt<FMT>::code_chunks];
     u32x4 sc16; // FP2/FP3/FP2M/Q8: eight fp16 scales
     u32x4 mn16; // FP2M: eight fp16 minima; FP2S: the eight second-half scales
-    u32x2 sc8;  // FP4: eight e8m0 bytes
+    u32x2 sc8;  // FP4 / FP3E: eight e8m0 bytes
 };
 
 // Issue order = use order: the scales first, then the code chunks in the
@@ -176,8 +177,11 @@ __device__ __forceinline__ TileRegs<FMT> load_tile(const uint8_t *__restrict__ t
 #pragma unroll
         for (int k = 0; k < 16; k++)
             RFX_LD(t.c[k], tp + 64 * k);
-    } else if (FMT == RFX_FP3) {
-        RFX_LD(t.sc16, tp + 64 * 6);
+    } else if (FMT == RFX_FP3 || FMT == RFX_FP3E) {
+        if (FMT == RFX_FP3E)
+            RFX_LD(t.sc8, reinterpret_cast<const u32x2 *>(tile + 6 * 1024) + lane);
+        else
+            RFX_LD(t.sc16, tp + 64 * 6);
         RFX_LD(t.c[4], tp + 64 * 4); // high bits, blocks 0..3
         RFX_LD(t.c[0], tp);
         RFX_LD(t.c[1], tp + 64);
@@ -229,7 +233,7 @@ __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel
     } else {
         const uint32_t w0 = (bi & 1) ? t.c[bi >> 1].z : t.c[bi >> 1].x;
         const uint32_t w1 = (bi & 1) ? t.c[bi >> 1].w : t.c[bi >> 1].y;
-        if (FMT == RFX_FP3) {
+        if (FMT == RFX_FP3 || FMT == RFX_FP3E) {
             const u32x4 h4 = t.c[4 + (bi >> 2)];
             const uint32_t h = (bi & 3) == 0 ? h4.x : (bi & 3) == 1 ? h4.y : (bi & 3) == 2 ? h4.z : h4.w;
             sel = sel_fp3(w0, w1, h);
@@ -238,8 +242,13 @@ __device__ __forceinline__ void decode_block(const TileRegs<FMT> &t, int bi, Sel
         } else {
             sel = sel_fp2(w0, w1);
         }
-        const uint32_t sw2 = (bi >> 1) == 0 ? t.sc16.x : (bi >> 1) == 1 ? t.sc16.y : (bi >> 1) == 2 ? t.sc16.z : t.sc16.w;
-        sw = half_bits_to_float((bi & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        if (FMT == RFX_FP3E) { // a power-of-two scale 2^(E - 127)
+            const uint32_t e = ((bi < 4 ? t.sc8.x : t.sc8.y) >> (8 * (bi & 3))) & 0xffu;
+            sw = ldexpf(1.0f, (int)e - 127);
+        } else {
+            const uint32_t sw2 = (bi >> 1) == 0 ? t.sc16.x : (bi >> 1) == 1 ? t.sc16.y : (bi >> 1) == 2 ? t.sc16.z : t.sc16.w;
+            sw = half_bits_to_float((bi & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        }
     }
 }
 
@@ -292,7 +301,7 @@ __device__ __forceinline__ int block_dot(const Sel8 &sel, const XBlock<Q> &xb, i
 #pragma unroll
     for (int i = 0; i < 8; i++)
         d = __builtin_amdgcn_sdot4(sel.v[i], xb.x[j][i], d, false);
-    if (FMT == RFX_FP2 || FMT == RFX_FP3) {
+    if (FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP3E) {
         const int off = FMT == RFX_FP2 ? 3 : 7; // v = 2c - off
         d = 2 * d - off * xb.sum[j];
     }

@@ -473,6 +473,7 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
         RFX_JOB(RFX_FP2M, 1) RFX_JOB(RFX_FP2M, 2) RFX_JOB(RFX_FP2M, 3) RFX_JOB(RFX_FP2M, 4)
         RFX_JOB(RFX_Q8, 1) RFX_JOB(RFX_Q8, 2) RFX_JOB(RFX_Q8, 3) RFX_JOB(RFX_Q8, 4)
         RFX_JOB(RFX_FP2S, 1) RFX_JOB(RFX_FP2S, 2) RFX_JOB(RFX_FP2S, 3) RFX_JOB(RFX_FP2S, 4)
+        RFX_JOB(RFX_FP3E, 1) RFX_JOB(RFX_FP3E, 2) RFX_JOB(RFX_FP3E, 3) RFX_JOB(RFX_FP3E, 4)
     default: break;
     }
 #undef RFX_JOB
@@ -533,6 +534,7 @@ int launch(int fmt, const GemvArgs &a, int q, int G, int W, hipStream_t st)
     case RFX_FP2M: return full ? launch_q<RFX_FP2M, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2M, DOTS, false>(a, q, G, W, st);
     case RFX_Q8: return full ? launch_q<RFX_Q8, DOTS, true>(a, q, G, W, st) : launch_q<RFX_Q8, DOTS, false>(a, q, G, W, st);
     case RFX_FP2S: return full ? launch_q<RFX_FP2S, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP2S, DOTS, false>(a, q, G, W, st);
+    case RFX_FP3E: return full ? launch_q<RFX_FP3E, DOTS, true>(a, q, G, W, st) : launch_q<RFX_FP3E, DOTS, false>(a, q, G, W, st);
     }
     return fail(RFX_E_INVAL, "unknown format");
 }
@@ -684,7 +686,8 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         order[j] = j;
     auto cost = [&](int j) {
         const int f = jobs[j].W.fmt, q = jobs[j].q;
-        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 ? 45 : f == RFX_FP2M || f == RFX_FP2S ? 38 : f == RFX_Q8 ? 20 : 75;
+        const int base = f == RFX_FP2 ? 30 : f == RFX_FP3 || f == RFX_FP3E ? 45 : f == RFX_FP2M || f == RFX_FP2S ? 38
+                       : f == RFX_Q8 ? 20 : 75;
         return base + 12 * q;
     };
     for (int i = 1; i < n_jobs; i++) // stable insertion sort, n <= 16

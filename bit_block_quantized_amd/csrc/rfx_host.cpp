@@ -86,18 +86,19 @@ const char *rfx_version(void) { return "rfx 0.1 gfx950"; }
 int rfx_block_bytes(int fmt)
 {
     return fmt == RFX_FP2 ? 10 : fmt == RFX_FP3 ? 14 : fmt == RFX_FP4 ? 17 : fmt == RFX_FP2M || fmt == RFX_FP2S ? 12
-         : fmt == RFX_Q8 ? 34 : RFX_E_INVAL;
+         : fmt == RFX_Q8 ? 34 : fmt == RFX_FP3E ? 13 : RFX_E_INVAL;
 }
 
 int rfx_code_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP2M || fmt == RFX_FP2S ? 8 : fmt == RFX_FP3 ? 12 : fmt == RFX_FP4 ? 16
+    return fmt == RFX_FP2 || fmt == RFX_FP2M || fmt == RFX_FP2S ? 8 : fmt == RFX_FP3 || fmt == RFX_FP3E ? 12
+         : fmt == RFX_FP4 ? 16
          : fmt == RFX_Q8 ? 32 : RFX_E_INVAL;
 }
 
 int rfx_scale_bytes(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_Q8 ? 2 : fmt == RFX_FP4 ? 1
+    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_Q8 ? 2 : fmt == RFX_FP4 || fmt == RFX_FP3E ? 1
          : fmt == RFX_FP2M || fmt == RFX_FP2S ? 4
          : RFX_E_INVAL;
 }
@@ -141,10 +142,10 @@ inline void put_code(int fmt, uint8_t *codes, int t, int c)
 {
     if (fmt == RFX_Q8) {
         codes[t] = (uint8_t)c;
-    } else if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S) {
+    } else if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S || fmt == RFX_FP3E) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         codes[4 * m + j] |= (uint8_t)((c & 3) << (2 * i));
-        if (fmt == RFX_FP3)
+        if (fmt == RFX_FP3 || fmt == RFX_FP3E)
             codes[8 + j] |= (uint8_t)(((c >> 2) & 1) << (t >> 2));
     } else {
         int m = t >> 3, i = (t >> 2) & 1, j = t & 3;
@@ -156,10 +157,10 @@ inline int get_code(int fmt, const uint8_t *codes, int t)
 {
     if (fmt == RFX_Q8)
         return codes[t];
-    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S) {
+    if (fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP2M || fmt == RFX_FP2S || fmt == RFX_FP3E) {
         int m = t >> 4, i = (t >> 2) & 3, j = t & 3;
         int c = (codes[4 * m + j] >> (2 * i)) & 3;
-        if (fmt == RFX_FP3)
+        if (fmt == RFX_FP3 || fmt == RFX_FP3E)
             c |= ((codes[8 + j] >> (t >> 2)) & 1) << 2;
         return c;
     }
@@ -172,7 +173,7 @@ inline int code_value(int fmt, int c)
     static const int mag[8] = {0, 1, 2, 3, 4, 6, 8, 12};
     if (fmt == RFX_FP2 || fmt == RFX_FP2S)
         return 2 * c - 3;
-    if (fmt == RFX_FP3)
+    if (fmt == RFX_FP3 || fmt == RFX_FP3E)
         return 2 * c - 7;
     if (fmt == RFX_FP2M)
         return c;
@@ -280,6 +281,19 @@ int encode_block(int fmt, const float *w, uint8_t *blk)
         put_half(blk + cb, h);
         return RFX_OK;
     }
+    if (fmt == RFX_FP3E) {
+        // the OCP MX rule with FP3's largest value 7 (floor(log2 7) = 2);
+        // the scale 2^(E - 127) applied exactly by ldexp
+        int E = 0;
+        if (amax > 0.0f) {
+            E = std::ilogb(amax) - 2 + 127;
+            E = E < 0 ? 0 : E > 254 ? 254 : E;
+        }
+        for (int t = 0; t < 32; t++)
+            put_code(fmt, blk, t, code_fp3(std::ldexp(w[t], 127 - E)));
+        blk[cb] = (uint8_t)E;
+        return RFX_OK;
+    }
     if (fmt == RFX_FP4) {
         // OCP MX: E = floor(log2 amax) - 2 + 127, clamped; ilogb is exact,
         // subnormals included.
@@ -328,6 +342,10 @@ inline TilePos tile_pos(int fmt, int64_t cols, int64_t r, int64_t b)
     if (fmt == RFX_FP4) {
         p.code0 = tile + bi * kChunk + lane * 16;
         p.scale = tile + 8 * kChunk + lane * 8 + bi;
+    } else if (fmt == RFX_FP3E) { // FP3's code chunks, then FP4's scale area
+        p.code0 = tile + (bi / 2) * kChunk + lane * 16 + (bi % 2) * 8;
+        p.code1 = tile + (4 + bi / 4) * kChunk + lane * 16 + (bi % 4) * 4;
+        p.scale = tile + 6 * kChunk + lane * 8 + bi;
     } else if (fmt == RFX_Q8) {
         p.code0 = tile + (2 * bi) * kChunk + lane * 16;
         p.code1 = tile + (2 * bi + 1) * kChunk + lane * 16;
@@ -352,6 +370,10 @@ void place_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *blk
     if (fmt == RFX_FP4) {
         std::memcpy(tiled + p.code0, blk, 16);
         tiled[p.scale] = blk[16];
+    } else if (fmt == RFX_FP3E) {
+        std::memcpy(tiled + p.code0, blk, 8);
+        std::memcpy(tiled + p.code1, blk + 8, 4);
+        tiled[p.scale] = blk[12];
     } else if (fmt == RFX_Q8) {
         std::memcpy(tiled + p.code0, blk, 16);
         std::memcpy(tiled + p.code1, blk + 16, 16);
@@ -373,6 +395,10 @@ void fetch_block(int fmt, int64_t cols, int64_t r, int64_t b, const uint8_t *til
     if (fmt == RFX_FP4) {
         std::memcpy(blk, tiled + p.code0, 16);
         blk[16] = tiled[p.scale];
+    } else if (fmt == RFX_FP3E) {
+        std::memcpy(blk, tiled + p.code0, 8);
+        std::memcpy(blk + 8, tiled + p.code1, 4);
+        blk[12] = tiled[p.scale];
     } else if (fmt == RFX_Q8) {
         std::memcpy(blk, tiled + p.code0, 16);
         std::memcpy(blk + 16, tiled + p.code1, 16);
@@ -455,7 +481,9 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32)
     if (!w32 || !blk)
         return fail(RFX_E_INVAL, "NULL buffer");
     const int cb = rfx_code_bytes(fmt);
-    const float s = fmt == RFX_FP4 ? std::ldexp(1.0f, (int)blk[cb] - 128) : get_half(blk + cb);
+    const float s = fmt == RFX_FP4    ? std::ldexp(1.0f, (int)blk[cb] - 128)
+                  : fmt == RFX_FP3E ? std::ldexp(1.0f, (int)blk[cb] - 127)
+                                    : get_half(blk + cb);
     const float m = fmt == RFX_FP2M ? get_half(blk + cb + 2) : 0.0f;
     const float s1 = fmt == RFX_FP2S ? get_half(blk + cb + 2) : s; // FP2S: weights 16..31
     for (int t = 0; t < 32; t++)

@@ -20,12 +20,14 @@ constexpr int kMaxBlockBytes = 34;                          // the largest canon
 constexpr int tile_bytes(int fmt)
 {
     return fmt == RFX_FP2 ? 5 * kChunk : fmt == RFX_FP3 ? 7 * kChunk : fmt == RFX_FP4 ? 8 * kChunk + 512
-         : fmt == RFX_FP2M || fmt == RFX_FP2S ? 6 * kChunk : fmt == RFX_Q8 ? 17 * kChunk : 0;
+         : fmt == RFX_FP2M || fmt == RFX_FP2S ? 6 * kChunk : fmt == RFX_Q8 ? 17 * kChunk
+         : fmt == RFX_FP3E ? 6 * kChunk + 512 : 0;
 }
 
 inline bool fmt_ok(int fmt)
 {
-    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP4 || fmt == RFX_FP2M || fmt == RFX_Q8 || fmt == RFX_FP2S;
+    return fmt == RFX_FP2 || fmt == RFX_FP3 || fmt == RFX_FP4 || fmt == RFX_FP2M || fmt == RFX_Q8 || fmt == RFX_FP2S ||
+           fmt == RFX_FP3E;
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

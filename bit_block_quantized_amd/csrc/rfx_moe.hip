@@ -1009,8 +1009,9 @@ int check_layer(const rfx_moe_layer *L)
     if (L->gate.fmt != L->up.fmt)
         return fail(RFX_E_UNSUPPORTED, "gate and up must share a block format (fused gate/up kernel)");
     for (const rfx_qmat *m : {&L->gate, &L->up, &L->down, &L->sh_gate, &L->sh_up, &L->sh_down})
-        if (m->data && (m->fmt == RFX_FP2M || m->fmt == RFX_Q8 || m->fmt == RFX_FP2S))
-            return fail(RFX_E_UNSUPPORTED, "the FP2M, FP2S and Q8 formats are supported by the GEMV entry points only");
+        if (m->data && (m->fmt == RFX_FP2M || m->fmt == RFX_Q8 || m->fmt == RFX_FP2S || m->fmt == RFX_FP3E))
+            return fail(RFX_E_UNSUPPORTED,
+                        "the FP2M, FP2S, FP3E and Q8 formats are supported by the GEMV entry points only");
     if (L->sh_gate.data && L->sh_gate.fmt != L->sh_up.fmt)
         return fail(RFX_E_UNSUPPORTED, "shared gate and up must share a block format");
     if (L->gate.count != L->n_experts || L->up.count != L->n_experts || L->down.count != L->n_experts)

@@ -69,7 +69,7 @@ __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel,
     } else {
         const uint32_t w0 = (BI & 1) ? t.c[BI >> 1].z : t.c[BI >> 1].x;
         const uint32_t w1 = (BI & 1) ? t.c[BI >> 1].w : t.c[BI >> 1].y;
-        if (FMT == RFX_FP3) {
+        if (FMT == RFX_FP3 || FMT == RFX_FP3E) {
             const u32x4 h4 = t.c[4 + (BI >> 2)];
             const uint32_t h = (BI & 3) == 0 ? h4.x : (BI & 3) == 1 ? h4.y : (BI & 3) == 2 ? h4.z : h4.w;
             sel = sel2_fp3(w0, w1, h);
@@ -80,8 +80,13 @@ __device__ __forceinline__ void decode_block2(const TileRegs<FMT> &t, Sel8 &sel,
         } else {
             sel = sel2_fp2(w0, w1);
         }
-        const uint32_t sw2 = (BI >> 1) == 0 ? t.sc16.x : (BI >> 1) == 1 ? t.sc16.y : (BI >> 1) == 2 ? t.sc16.z : t.sc16.w;
-        sw = half_bits_to_float((BI & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        if (FMT == RFX_FP3E) {
+            const uint32_t e = ((BI < 4 ? t.sc8.x : t.sc8.y) >> (8 * (BI & 3))) & 0xffu;
+            sw = ldexpf(1.0f, (int)e - 127);
+        } else {
+            const uint32_t sw2 = (BI >> 1) == 0 ? t.sc16.x : (BI >> 1) == 1 ? t.sc16.y : (BI >> 1) == 2 ? t.sc16.z : t.sc16.w;
+            sw = half_bits_to_float((BI & 1) ? (sw2 >> 16) : (sw2 & 0xffffu));
+        }
     }
 }
 
@@ -138,7 +143,7 @@ __device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int
     for (int j = 0; j < Q; j++)
         xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
     if (TileFmt<FMT>::needs_sum) {
-        constexpr int off = FMT == RFX_FP2 ? 3 : FMT == RFX_FP3 ? 7 : -1; // FP2M: +sum
+        constexpr int off = FMT == RFX_FP2 ? 3 : FMT == RFX_FP3 || FMT == RFX_FP3E ? 7 : -1; // FP2M: +sum
 #pragma unroll
         for (int j = 0; j < Q; j++)
             xt.nsum[j] = -off * xc.xsum[xc.moff[j] + (uint32_t)bs];
@@ -164,7 +169,7 @@ __device__ __forceinline__ void block_half_dots_mfma(const Sel8 &sel, const XTil
 {
     d0 = i32x4{0, 0, 0, 0};
     d1 = i32x4{0, 0, 0, 0};
-    if (FMT == RFX_FP2 || FMT == RFX_FP3) {
+    if (FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP3E) {
 #pragma unroll
         for (int j = 0; j < Q; j++)
             d0[j] = bcast_row<BI>(xt.nsum[j]);

@@ -73,16 +73,21 @@ enum {
  *            small values read as two scales): FP2 codes and codebook;
  *            weights 0..15 take fp16 scale s0, weights 16..31 fp16 scale
  *            s1; codes, s0, s1: 12 B / block (3.0 bits per weight). Same
- *            support as RFX_FP2M. */
-enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_Q8 = 8, RFX_FP2M = 12, RFX_FP2S = 16 };
+ *            support as RFX_FP2M.
+ *   RFX_FP3E: a 3-bit tier at about 3.3 bits per weight (the figure
+ *            another system on the pages gives for its 3-bit experts,
+ *            without a layout; this one is a reading): FP3's codes and
+ *            codebook, then one e8m0 byte E, weight = 2^(E-127) x value:
+ *            13 B / block (3.25 bits per weight). Same support as RFX_FP2M. */
+enum { RFX_FP2 = 2, RFX_FP3 = 3, RFX_FP4 = 4, RFX_Q8 = 8, RFX_FP2M = 12, RFX_FP3E = 13, RFX_FP2S = 16 };
 
 const char *rfx_status_str(int status);
 const char *rfx_last_error(void);
 const char *rfx_version(void);
 
-int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M) / 34 (Q8) / 12 (FP2S), or RFX_E_INVAL */
-int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 / 32 / 8 */
-int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 / 4 */
+int rfx_block_bytes(int fmt); /* 10 / 14 / 17 / 12 (FP2M) / 34 (Q8) / 12 (FP2S) / 13 (FP3E), or RFX_E_INVAL */
+int rfx_code_bytes(int fmt);  /* 8 / 12 / 16 / 8 / 32 / 8 / 12 */
+int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 / 4 / 1 */
 
 /* ------------------------------------------------------------------ */
 /* Host-side encoder (synchronous, host memory).                       */
@@ -105,9 +110,12 @@ int rfx_scale_bytes(int fmt); /* bytes after the codes: 2 / 2 / 1 / 4 / 2 / 4 */
  * FP2S: each half h (weights 16h..16h+15) is encoded as an FP2 block with
  * its own amax: s_h = fp16_rne(amax_h / 3) in fp32, FP2 codes and ties;
  * s_h = 0 codes the half's weights as +1. Block: codes, s0, s1 (fp16 LE).
+ * FP3E: E = clamp(floor(log2 amax) - 2 + 127, 0, 254), amax = 0 -> 0;
+ * code = FP3's nearest value to w * 2^(127-E) (exact), ties to the larger
+ * magnitude, saturating at +-7. Block: codes, E.
  * Bit layout of the code bytes, as little-endian 32-bit words:
  *   FP2 (and FP2M, FP2S): weight 16m+4i+j (m<2, i,j<4) at word m bits [8j+2i, 8j+2i+2)
- *   FP3: low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
+ *   FP3 (and FP3E): low two bits as FP2 in words 0-1; high bit of weight 4i+j (i<8)
  *        at word 2 bit 8j+i
  *   FP4: weight 8m+4i+j (m<4, i<2, j<4) at word m bits [8j+4i, 8j+4i+4)
  * Returns RFX_E_RANGE for a non-finite weight or an fp16 scale (or FP2M
@@ -134,6 +142,8 @@ int rfx_dequantize_block(int fmt, const uint8_t *blk, float *w32);
  *   FP2M (tile 6144 B): chunks 0-4 as FP2; chunk 5 = the eight fp16 minima.
  *   FP2S (tile 6144 B): chunks 0-3 as FP2; chunk 4 = the eight first-half
  *       scales s0; chunk 5 = the eight second-half scales s1.
+ *   FP3E (tile 6656 B): chunks 0-5 as FP3; then 64 rows x 8 B of e8m0
+ *       bytes at byte 6144 + r * 8.
  *   Q8 (tile 17408 B): chunk 2b + h = code bytes 16h..16h+15 of block b;
  *       chunk 16 = the eight fp16 scales.
  * Rows beyond `rows` and blocks beyond cols/32 are zero (scale 0). Block
@@ -245,7 +255,7 @@ int rfx_read_reference(const void *buf, size_t bytes, uint32_t *out, int n_out, 
 /* Routed experts: gate and up (rows = inter, cols = hidden) and down
  * (rows = hidden, cols = inter), `n_experts` stacked each ([HM] para 2 and
  * [KK] ROCmFPX section: gate/up in FP2, down in FP3; any of RFX_FP2, RFX_FP3
- * and RFX_FP4 is accepted, RFX_FP2M, RFX_FP2S and RFX_Q8 are not). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
+ * and RFX_FP4 is accepted, RFX_FP2M, RFX_FP2S, RFX_FP3E and RFX_Q8 are not). Shared expert: sh_* with count 1 (FP4 for sensitive layers),
  * or sh_gate.data == NULL for none. Router: fp32 [n_experts][hidden]
  * weights and an optional fp32 [n_experts] bias. */
 typedef struct rfx_moe_layer {

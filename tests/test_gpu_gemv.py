@@ -17,8 +17,10 @@ FMTS = (2, 3, 4)
 FP2M = R.FP2M
 Q8 = R.Q8
 FP2S = R.FP2S
-# the GEMV entry points also take the FP2M and FP2S variants and the Q8 tier
-GEMV_FMTS = FMTS + (FP2M, Q8, FP2S)
+FP3E = R.FP3E
+# the GEMV entry points also take the FP2M and FP2S variants and the Q8 and
+# FP3E tiers
+GEMV_FMTS = FMTS + (FP2M, Q8, FP2S, FP3E)
 
 
 def _sync(torch):
@@ -95,7 +97,7 @@ _BIG = {}
 
 def _big(fmt):
     if fmt not in _BIG:
-        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30, Q8: 40, FP2S: 50}[fmt], outliers=True)
+        W = inputgen.dense_weight(7168, 7168, seed={2: 0, 3: 10, 4: 20, FP2M: 30, Q8: 40, FP2S: 50, FP3E: 60}[fmt], outliers=True)
         _BIG[fmt] = (W, O.quantize_matrix(fmt, W))
     return _BIG[fmt]
 
@@ -250,6 +252,8 @@ def _grouped(torch, specs, seed, big=False):
     [(8, 1, 300, 4096), (8, 4, 65, 1312), (3, 2, 130, 2048), (8, 3, 1, 32)],
     # the FP2S variant beside the others, ragged and full tiles
     [(16, 1, 200, 544), (16, 4, 130, 2080), (12, 2, 65, 1024), (16, 3, 1, 32), (2, 4, 256, 512)],
+    # the FP3E tier beside FP3 (same code chunks, different scale area)
+    [(13, 1, 300, 4096), (3, 1, 300, 4096), (13, 4, 65, 1312), (13, 2, 1, 32), (4, 3, 130, 2080)],
 ])
 def test_gemv_grouped_small(specs):
     torch = need_gpu()

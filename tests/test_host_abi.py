@@ -16,7 +16,8 @@ import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FMTS = (2, 3, 4)
-ALL_FMTS = (2, 3, 4, 12, 8, 16)  # the named formats, the FP2M variant, the Q8 tier, the FP2S variant
+# the named formats, the FP2M variant, the Q8 tier, the FP2S variant, the FP3E tier
+ALL_FMTS = (2, 3, 4, 12, 8, 16, 13)
 
 
 def _header_functions():
@@ -38,7 +39,8 @@ def test_library_exports_every_declared_symbol():
 def test_sizes():
     for fmt, (bb, cb, sb, tile) in {2: (10, 8, 2, 5120), 3: (14, 12, 2, 7168),
                                      4: (17, 16, 1, 8704), 12: (12, 8, 4, 6144),
-                                     8: (34, 32, 2, 17408), 16: (12, 8, 4, 6144)}.items():
+                                     8: (34, 32, 2, 17408), 16: (12, 8, 4, 6144),
+                                     13: (13, 12, 1, 6656)}.items():
         assert R.block_bytes(fmt) == bb == O.block_bytes(fmt)
         assert R.code_bytes(fmt) == cb and R.scale_bytes(fmt) == sb
         assert R.qmat_bytes(fmt, 64, 256) == tile == 64 * 8 * bb
@@ -136,6 +138,12 @@ def test_tiled_layout_positions():
         if fmt == 4:
             assert list(t[tile + bi * 1024 + lane * 16: tile + bi * 1024 + lane * 16 + 16]) == list(range(1, 17))
             assert t[tile + 8192 + lane * 8 + bi] == 17
+        elif fmt == 13:  # FP3's code chunks, then one e8m0 byte per block
+            c0 = tile + (bi // 2) * 1024 + lane * 16 + (bi % 2) * 8
+            assert list(t[c0:c0 + 8]) == list(range(1, 9))
+            c1 = tile + (4 + bi // 4) * 1024 + lane * 16 + (bi % 4) * 4
+            assert list(t[c1:c1 + 4]) == [9, 10, 11, 12]
+            assert t[tile + 6144 + lane * 8 + bi] == 13
         elif fmt == 8:
             for h in range(2):
                 c = tile + (2 * bi + h) * 1024 + lane * 16
@@ -253,9 +261,10 @@ def test_moe_rejects_the_gemv_only_variant():
     lay.down.fmt = 12
     st = L.rfx_moe_route_topk(ctypes.byref(lay), f, 1, 2, f, f, f, f, f, f, f, f, 1 << 20, None)
     assert st == -4
-    lay.down.fmt = 16
-    st = L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, 1 << 20, None)
-    assert st == -4 and b"FP2S" in L.rfx_last_error()
+    for fmt in (16, 13):
+        lay.down.fmt = fmt
+        st = L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, 1 << 20, None)
+        assert st == -4 and b"FP3E" in L.rfx_last_error()
 
 
 def test_read_reference_validation_without_gpu():
