@@ -18,8 +18,9 @@
 // weight and activation block scales in fp32 (the same sum as the decode
 // kernels, over the same blocks in the same order per output).
 //
-// Launches per layer: route (act quant + fused logits / softmax / top-k),
-// bucket (one workgroup), gate/up (+ SwiGLU + requantization), down, combine.
+// Launches per layer: act quant, router logits (fp32 matrix core), softmax /
+// top-k, bucket (one workgroup), gate/up (+ SwiGLU + requantization), down,
+// combine.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -36,67 +37,104 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------
-// Router: logits x . Wr (+ b) in fp32, softmax over all experts, top-k by
-// logit with ties to the lower id, weights = the chosen probabilities.
-// One workgroup per 8 tokens; thread e owns expert e and accumulates its
-// 8 dot products over H in fixed order (the x chunk comes from LDS).
+// Router logits x . Wr^T (+ b) in fp32 on the matrix core
+// (v_mfma_f32_16x16x4_f32): one workgroup per 16 tokens x 32 experts, its
+// four waves splitting H into contiguous runs of 32 columns (so each SIMD
+// has four independent load streams in flight) and summed in fixed order
+// through LDS. Per 16-column chunk, lane l holds x[t0 + l%16][k0 +
+// 4(l/16) ..+3] and the same four columns of expert rows e0 + l%16 and
+// e0 + 16 + l%16; step s of the chunk feeds component s of each, so the
+// matrix op's K index l/16 stands for column k0 + 4(l/16) + s on both
+// operands and every product pairs equal columns. Output lane l, register
+// v: token t0 + 4(l/16) + v, expert e0 + l%16 (second tile: + 16). Rows
+// past T or E are read clamped and never stored.
 // ------------------------------------------------------------------
-constexpr int kRouteTB = 8;   // tokens per workgroup
-constexpr int kRouteHC = 256; // hidden columns per LDS chunk
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-struct RouteArgs {
+struct LogitArgs {
     const float *x;  // [T][H]
     const float *wr; // [E][H]
     const float *wb; // [E] or null
-    int T, k, E, H;
+    int T, E, H;     // H % 32 == 0
+    float *logits;   // [T][E]
+};
+
+constexpr int kLogitWaves = 4;
+
+__global__ __launch_bounds__(64 * kLogitWaves) void prefill_logits_kernel(LogitArgs a)
+{
+    __shared__ f32x4 red[kLogitWaves][2][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 32;
+    const int r = lane & 15, kq = (lane >> 4) * 4;
+    const float *xp = a.x + (size_t)min(t0 + r, a.T - 1) * a.H + kq;
+    const float *w0 = a.wr + (size_t)min(e0 + r, a.E - 1) * a.H + kq;
+    const float *w1 = a.wr + (size_t)min(e0 + 16 + r, a.E - 1) * a.H + kq;
+    const int nc = a.H / 32;
+    const int c_begin = nc * wave / kLogitWaves, c_end = nc * (wave + 1) / kLogitWaves;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int c32 = c_begin; c32 < c_end; c32++) {
+        const int k0 = 32 * c32;
+        f32x4 xv[2], wv0[2], wv1[2];
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            xv[c] = *reinterpret_cast<const f32x4 *>(xp + k0 + 16 * c);
+            wv0[c] = *reinterpret_cast<const f32x4 *>(w0 + k0 + 16 * c);
+            wv1[c] = *reinterpret_cast<const f32x4 *>(w1 + k0 + 16 * c);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; c++)
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[c][st], wv0[c][st], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[c][st], wv1[c][st], acc1, 0, 0, 0);
+            }
+    }
+    red[wave][0][lane] = acc0;
+    red[wave][1][lane] = acc1;
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int w = 1; w < kLogitWaves; w++) { // fixed order: wave 0, 1, 2, 3
+        acc0 += red[w][0][lane];
+        acc1 += red[w][1][lane];
+    }
+    const int ea = e0 + r, eb = e0 + 16 + r;
+    const float ba = a.wb && ea < a.E ? a.wb[ea] : 0.0f, bb = a.wb && eb < a.E ? a.wb[eb] : 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+        const int t = t0 + 4 * (lane >> 4) + v;
+        if (t < a.T) {
+            if (ea < a.E)
+                a.logits[(size_t)t * a.E + ea] = acc0[v] + ba;
+            if (eb < a.E)
+                a.logits[(size_t)t * a.E + eb] = acc1[v] + bb;
+        }
+    }
+}
+
+// ------------------------------------------------------------------
+// Router selection: softmax over all experts, top-k by logit with ties to
+// the lower id, weights = the chosen probabilities. One wave per token,
+// kRouteTB tokens per workgroup, logits from prefill_logits_kernel.
+// ------------------------------------------------------------------
+constexpr int kRouteTB = 8; // tokens per workgroup
+
+struct RouteArgs {
+    const float *logits; // [T][E]
+    int T, k, E;
     int32_t *topk_idx;
     float *topk_w;
 };
 
 __global__ __launch_bounds__(256) void prefill_route_kernel(RouteArgs a)
 {
-    __shared__ float xs[kRouteTB][kRouteHC];
-    __shared__ float lg[kRouteTB][kMaxE];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t0 = blockIdx.x * kRouteTB;
-    const int e = tid;
-    float acc[kRouteTB];
-#pragma unroll
-    for (int t = 0; t < kRouteTB; t++)
-        acc[t] = 0.0f;
-    for (int h0 = 0; h0 < a.H; h0 += kRouteHC) {
-        const int hc = min(kRouteHC, a.H - h0); // multiple of 32
-        for (int i = tid; i < kRouteTB * kRouteHC / 4; i += 256) {
-            const int t = i / (kRouteHC / 4), c = (i % (kRouteHC / 4)) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t0 + t < a.T && c < hc)
-                v = *reinterpret_cast<const float4 *>(a.x + (size_t)(t0 + t) * a.H + h0 + c);
-            *reinterpret_cast<float4 *>(&xs[t][c]) = v;
-        }
-        __syncthreads();
-        if (e < a.E) {
-            const float *wrow = a.wr + (size_t)e * a.H + h0;
-            for (int c = 0; c < hc; c += 4) {
-                const float4 w = *reinterpret_cast<const float4 *>(wrow + c);
-#pragma unroll
-                for (int t = 0; t < kRouteTB; t++) {
-                    acc[t] = fmaf(xs[t][c], w.x, acc[t]);
-                    acc[t] = fmaf(xs[t][c + 1], w.y, acc[t]);
-                    acc[t] = fmaf(xs[t][c + 2], w.z, acc[t]);
-                    acc[t] = fmaf(xs[t][c + 3], w.w, acc[t]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    if (e < a.E) {
-        const float b = a.wb ? a.wb[e] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < kRouteTB; t++)
-            lg[t][e] = acc[t] + b;
-    }
-    __syncthreads();
 
     // one wave per token: softmax and top-k
     for (int tt = wave; tt < kRouteTB; tt += 4) {
@@ -108,7 +146,7 @@ __global__ __launch_bounds__(256) void prefill_route_kernel(RouteArgs a)
         float m = -INFINITY;
         for (int r = 0; r < 4; r++) {
             const int ee = lane + 64 * r;
-            l[r] = ee < a.E ? lg[tt][ee] : -INFINITY;
+            l[r] = ee < a.E ? a.logits[(size_t)t * a.E + ee] : -INFINITY;
             taken[r] = ee >= a.E;
             m = fmaxf(m, l[r]);
         }
@@ -709,14 +747,23 @@ int prefill_route(const rfx_moe_layer *L, const float *x, int q, int k, int32_t 
     int st = rfx_quantize_act(x, q, L->hidden, xq, xs, xsum, stream);
     if (st)
         return st;
+    LogitArgs la{};
+    la.x = x;
+    la.wr = L->router_w;
+    la.wb = L->router_b;
+    la.T = q;
+    la.E = L->n_experts;
+    la.H = L->hidden;
+    la.logits = w.logits;
+    hipLaunchKernelGGL(prefill_logits_kernel, dim3((q + 15) / 16, (L->n_experts + 31) / 32), dim3(64 * kLogitWaves),
+                       0, stream, la);
+    if ((st = hip_status("prefill logits launch")))
+        return st;
     RouteArgs ra{};
-    ra.x = x;
-    ra.wr = L->router_w;
-    ra.wb = L->router_b;
+    ra.logits = w.logits;
     ra.T = q;
     ra.k = k;
     ra.E = L->n_experts;
-    ra.H = L->hidden;
     ra.topk_idx = topk_idx;
     ra.topk_w = topk_w;
     hipLaunchKernelGGL(prefill_route_kernel, dim3((q + kRouteTB - 1) / kRouteTB), dim3(256), 0, stream, ra);
