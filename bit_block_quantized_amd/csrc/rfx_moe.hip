@@ -619,9 +619,9 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
         gateup_finish<NE>(a, cols, g, lane, W, red);
 }
 
-// FP4 gate and up with one or two tokens on the block-scaled matrix core
-// (rfx_mx4.h): both matrices' products take the same activation operand,
-// built once per (half, column pair). Same tile split, reduction and
+// FP4 gate and up on the block-scaled matrix core (rfx_mx4.h), one column
+// pair per two tokens: both matrices' products take the same activation
+// operand, built once per (half, column pair). Same tile split, reduction and
 // epilogue as gateup_body. SINGLE: one tile buffer (see gateup_body).
 template <int NE, bool SINGLE = true>
 __device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
@@ -711,7 +711,9 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
-    // FP4 with one or two tokens: the block-scaled matrix core
+    // FP4 on the block-scaled matrix core: the shared expert (every token,
+    // the heaviest slot, whose workgroups share CUs with routed ones) at
+    // any token count, routed slots with one or two tokens
     if (si.kind == 2) {
         switch (ne) {
         case 1:
@@ -726,8 +728,18 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
             else
                 gateup_body<FS, 2>(a, si, blockIdx.x, lane, wave, W, red);
             break;
-        case 3: gateup_body<FS, 3>(a, si, blockIdx.x, lane, wave, W, red); break;
-        case 4: gateup_body<FS, 4>(a, si, blockIdx.x, lane, wave, W, red); break;
+        case 3:
+            if constexpr (FS == RFX_FP4)
+                gateup_body_mx<3>(a, si, blockIdx.x, lane, wave, W, red);
+            else
+                gateup_body<FS, 3>(a, si, blockIdx.x, lane, wave, W, red);
+            break;
+        case 4:
+            if constexpr (FS == RFX_FP4)
+                gateup_body_mx<4>(a, si, blockIdx.x, lane, wave, W, red);
+            else
+                gateup_body<FS, 4>(a, si, blockIdx.x, lane, wave, W, red);
+            break;
         default: break;
         }
     } else {
@@ -899,7 +911,9 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
-    // FP4 with one or two tokens: the block-scaled matrix core
+    // FP4 on the block-scaled matrix core: the shared expert (every token,
+    // the heaviest slot, whose workgroups share CUs with routed ones) at
+    // any token count, routed slots with one or two tokens
     if (si.kind == 2) {
         switch (ne) {
         case 1:
