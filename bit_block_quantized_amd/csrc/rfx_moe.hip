@@ -911,9 +911,8 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
-    // FP4 on the block-scaled matrix core: the shared expert (every token,
-    // the heaviest slot, whose workgroups share CUs with routed ones) at
-    // any token count, routed slots with one or two tokens
+    // FP4 with one or two tokens on the block-scaled matrix core (for the
+    // shared expert's three or four tokens it measured no faster here)
     if (si.kind == 2) {
         switch (ne) {
         case 1:
