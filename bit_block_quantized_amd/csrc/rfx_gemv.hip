@@ -71,36 +71,45 @@ namespace {
 using namespace rfx::dev;
 
 // ------------------------------------------------------------------
-// Activation quantization: one lane per element, two 32-element blocks
-// per wave. s = amax/127 (IEEE division), code = clamp(rne(x/s)).
+// Activation quantization: one lane per four elements (a 16-byte load and
+// one packed 4-byte store), eight lanes per 32-element block. s = amax/127
+// (IEEE division), code = clamp(rne(x/s)); the max and the integer sum are
+// order-free, so the result is the same as element by element.
 // ------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_quant_kernel(const float *__restrict__ x, int64_t n,
-                                                        int8_t *__restrict__ xq,
+__global__ __launch_bounds__(256) void act_quant_kernel(const float4 *__restrict__ x, int64_t n4,
+                                                        uint32_t *__restrict__ xq,
                                                         float *__restrict__ xs,
                                                         int32_t *__restrict__ xsum)
 {
 #pragma clang fp contract(off)
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool valid = i < n;
-    const float v = valid ? x[i] : 0.0f;
-    float a = fabsf(v);
-    for (int o = 16; o > 0; o >>= 1)
-        a = fmaxf(a, __shfl_xor(a, o, 32));
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // group of four
+    const bool valid = i < n4; // n4 is a multiple of 8: blocks are whole
+    const float4 v4 = valid ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    for (int o = 4; o > 0; o >>= 1)
+        a = fmaxf(a, __shfl_xor(a, o, 8));
     const float s = a / 127.0f;
-    int qv = 0;
-    if (s != 0.0f) {
-        float r = rintf(v / s);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        qv = (int)r;
+    uint32_t packed = 0u;
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        int qv = 0;
+        if (s != 0.0f) {
+            float r = rintf(v[k] / s);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            qv = (int)r;
+        }
+        sum += qv;
+        packed |= ((uint32_t)qv & 0xffu) << (8 * k);
     }
-    int sum = qv;
-    for (int o = 16; o > 0; o >>= 1)
-        sum += __shfl_xor(sum, o, 32);
+    for (int o = 4; o > 0; o >>= 1)
+        sum += __shfl_xor(sum, o, 8);
     if (valid) {
-        xq[i] = (int8_t)qv;
-        if ((threadIdx.x & 31) == 0) {
-            xs[i >> 5] = s;
-            xsum[i >> 5] = sum;
+        xq[i] = packed;
+        if ((threadIdx.x & 7) == 0) {
+            xs[i >> 3] = s;
+            xsum[i >> 3] = sum;
         }
     }
 }
@@ -580,18 +589,19 @@ int rfx_quantize_act(const float *x, int q, int K, int8_t *xq, float *xs, int32_
 {
     if (q < 1 || K < 32 || K % 32)
         return fail(RFX_E_INVAL, "rfx_quantize_act: bad shape q=%d K=%d", q, K);
-    int st = check_ptr(x, 4, "x");
+    int st = check_ptr(x, 16, "x");
     if (!st)
-        st = check_ptr(xq, 4, "xq");
+        st = check_ptr(xq, 16, "xq");
     if (!st)
         st = check_ptr(xs, 4, "xs");
     if (!st)
         st = check_ptr(xsum, 4, "xsum");
     if (st)
         return st;
-    const int64_t n = (int64_t)q * K;
-    dim3 grid((unsigned)((n + 255) / 256)), block(256);
-    hipLaunchKernelGGL(act_quant_kernel, grid, block, 0, (hipStream_t)stream, x, n, xq, xs, xsum);
+    const int64_t n4 = (int64_t)q * K / 4;
+    dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+    hipLaunchKernelGGL(act_quant_kernel, grid, block, 0, (hipStream_t)stream, reinterpret_cast<const float4 *>(x),
+                       n4, reinterpret_cast<uint32_t *>(xq), xs, xsum);
     return hip_status("act_quant launch");
 }
 

@@ -179,7 +179,7 @@ int rfx_import_blocks(int fmt, const uint8_t *blocks, int64_t rows, int64_t cols
  * codebooks are affine in the code). Integer activations feed the integer
  * dot products ([HM] para 3).
  * x fp32 [q][K]; xq int8 [q][K]; xs fp32 [q][K/32]; xsum int32 [q][K/32].
- * q >= 1. xq needs 16-B alignment, xs and xsum 4-B. */
+ * q >= 1. x and xq need 16-B alignment, xs and xsum 4-B (RFX_E_ALIGN). */
 int rfx_quantize_act(const float *x, int q, int K, int8_t *xq, float *xs, int32_t *xsum,
                      void *stream);
 

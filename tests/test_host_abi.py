@@ -242,6 +242,9 @@ def test_device_entry_validation_without_gpu():
     assert b"jobs[0]" in L.rfx_last_error()
     assert L.rfx_quantize_act(_fake(good), 1, 40, _fake(good), _fake(good), _fake(good), null) == -1
     assert L.rfx_quantize_act(None, 1, 64, _fake(good), _fake(good), _fake(good), null) == -1
+    # x and xq are read and written 16 bytes at a time
+    assert L.rfx_quantize_act(_fake(good + 4), 1, 64, _fake(good), _fake(good), _fake(good), null) == -2
+    assert L.rfx_quantize_act(_fake(good), 1, 64, _fake(good + 8), _fake(good), _fake(good), null) == -2
     assert L.rfx_debug_block_dots(ctypes.byref(W), _fake(good), _fake(good), 0, _fake(good), null) == -1
     assert b"q" in L.rfx_last_error()
 
