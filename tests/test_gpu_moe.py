@@ -205,3 +205,20 @@ def test_moe_router_exact_ties_go_to_lower_id():
         gpu = _run_layer(torch, spec, dev, x, k)
         assert np.array_equal(gpu["topk_idx"], ref["idx"]), (gpu["topk_idx"], ref["idx"])
         _check_layer(spec, gpu, x, k, orc)
+
+
+@pytest.mark.parametrize("n_experts", [200, 100])
+@pytest.mark.parametrize("q", [1, 4])
+def test_moe_uneven_expert_count_and_hidden(n_experts, q):
+    """Expert counts that leave the router's last arrival group partial
+    (200: 13 groups of 16, the last of 8) and the last candidate row of
+    its top-k wave partly empty, with a hidden size that is no multiple of
+    the 256-column tile (800) and top-6."""
+    torch = need_gpu()
+    say(f"moe uneven E={n_experts} q={q}")
+    spec = LayerSpec(layer=12, hidden=800, inter=320, n_experts=n_experts, shared=True)
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    x = inputgen.tokens(12, n_experts + q, q, spec.hidden)
+    gpu = _run_layer(torch, spec, dev, x, k=6)
+    _check_layer(spec, gpu, x, 6, orc)

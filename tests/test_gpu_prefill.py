@@ -237,3 +237,16 @@ def test_prefill_full_2048_tokens_top6():
     err = rel_err(gpu["y"][sample_t], y_ref)
     say(f"  y err on tokens {sample_t} (fed h~): {err:.2e}")
     assert err <= TOL
+
+
+def test_prefill_uneven_expert_and_token_counts():
+    """40 experts (the router's second 32-expert tile partial) and 77 tokens
+    (the last 16-token tile partial), hidden 800 (no multiple of 256)."""
+    torch = need_gpu()
+    say("prefill uneven E=40 q=77")
+    spec = LayerSpec(layer=13, hidden=800, inter=320, n_experts=40, shared=True)
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    x = inputgen.tokens(13, 77, 77, spec.hidden)
+    gpu = _run(torch, spec, dev, x, 3)
+    _check_all(spec, gpu, x, 3, orc)
