@@ -281,10 +281,11 @@ size_t rfx_moe_workspace_bytes(const rfx_moe_layer *L, int q, int k);
  * x fp32 [q][H]; topk_idx int32 [q][k]; topk_w fp32 [q][k]; 1 <= k <= 8.
  * q in 1..4 (decode and speculative verification): one launch, every
  * expert row of Wr read once for all q tokens. q in 5..65536 (prefill):
- * act quant, a router with one workgroup per 8 tokens, and a one-workgroup
- * stable bucketing that also writes the FFN's work items (chunks of up to
- * 64 tokens of one expert) into ws; rfx_moe_ffn must then get the same ws,
- * q and k. */
+ * act quant, the logits on the fp32 matrix core into ws, a softmax / top-k
+ * kernel (one wave per token) and a one-workgroup stable bucketing that
+ * also writes the FFN's work items (chunks of up to 64 tokens of one
+ * expert) into ws; rfx_moe_ffn must then get the same ws, q and k. The
+ * router reads x in 16-byte words: x needs 16-B alignment. */
 int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx,
                        float *topk_w, int32_t *pairs_sorted, int32_t *expert_off, int8_t *xq,
                        float *xs, int32_t *xsum, void *ws, size_t ws_bytes, void *stream);
