@@ -89,6 +89,8 @@ def lib():
     L.orc_weight_scale.restype = ctypes.c_double
     L.orc_dequantize_block.argtypes = [ctypes.c_int, _u8p, _f64p]
     L.orc_dequantize_block.restype = None
+    L.orc_dequantize_matrix.argtypes = [ctypes.c_int, _u8p, ctypes.c_int64, ctypes.c_int64, _f64p]
+    L.orc_dequantize_matrix.restype = None
     L.orc_quantize_block.argtypes = [ctypes.c_int, _f32p, _u8p]
     L.orc_quantize_matrix.argtypes = [ctypes.c_int, _f32p, ctypes.c_int64, ctypes.c_int64, _u8p]
     L.orc_quantize_act.argtypes = [_f32p, ctypes.c_int64, _i8p, _f32p]
@@ -195,12 +197,13 @@ def quantize_matrix(fmt: int, W) -> np.ndarray:
 
 
 def dequantize_matrix(fmt: int, blocks) -> np.ndarray:
-    """Canonical blocks [N][K/32][bb] -> fp64 [N][K] (slow; small sizes)."""
-    N, nb, _ = blocks.shape
+    """Canonical blocks [N][K/32][bb] -> fp64 [N][K]: dequantize_block on
+    every block (one C loop)."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    N, nb, bb = blocks.shape
+    assert bb == block_bytes(fmt)
     out = np.zeros((N, nb * 32), np.float64)
-    for n in range(N):
-        for b in range(nb):
-            out[n, 32 * b:32 * b + 32] = dequantize_block(fmt, blocks[n, b])
+    lib().orc_dequantize_matrix(fmt, _p(blocks, _u8p), N, nb, _p(out, _f64p))
     return out
 
 

@@ -358,6 +358,16 @@ void orc_dequantize_block(int fmt, const uint8_t *blk, double *w)
         w[t] = orc_weight_scale(fmt, blk, t) * (double)orc_codebook(fmt, codes[t]) + m;
 }
 
+/* Canonical blocks [rows][nb][block bytes] -> fp64 [rows][32 nb]: the
+ * block decoder above applied to every block in turn. */
+void orc_dequantize_matrix(int fmt, const uint8_t *blocks, int64_t rows, int64_t nb, double *w)
+{
+    const int bb = orc_block_bytes(fmt);
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++)
+            orc_dequantize_block(fmt, blocks + (r * nb + b) * bb, w + (r * nb + b) * 32);
+}
+
 /* ------------------------------------------------------------------ */
 /* Encoder (Reading: absmax scaling; the real model used an importance  */
 /* matrix [KK, mixed-precision section], which needs calibration data). */

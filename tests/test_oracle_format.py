@@ -692,3 +692,15 @@ def test_fp3e_nonfinite_rejected():
     w[9] = np.inf
     with pytest.raises(O.OracleError):
         O.quantize_block(FP3E, w)
+
+
+@pytest.mark.parametrize("fmt", (2, 3, 4, 12, 8, 16, 13))
+def test_dequantize_matrix_is_the_block_decoder_on_every_block(fmt):
+    """The matrix dequantizer is dequantize_block applied block by block, in
+    row-major block order (a swapped index or stride would misplace them)."""
+    W = inputgen.dense_weight(7, 96, seed=31, outliers=True)
+    blocks = O.quantize_matrix(fmt, W)
+    Wd = O.dequantize_matrix(fmt, blocks)
+    for n in range(7):
+        for b in range(3):
+            assert np.array_equal(Wd[n, 32 * b:32 * b + 32], O.dequantize_block(fmt, blocks[n, b]))
