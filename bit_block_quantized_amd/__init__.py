@@ -97,7 +97,8 @@ _SIGS = {
     "rfx_moe_workspace_bytes": ([_P, _I, _I], _SZ),
     "rfx_moe_route_topk": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_moe_ffn": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
-    "rfx_moe_debug_hidden": ([_P, _I, _I, _P, _P, _P, _P, _P], _I),
+    "rfx_moe_debug_hidden": ([_P, _I, _I, _P, _SZ, _P, _P, _P, _P], _I),
+    "rfx_moe_debug_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _P], _I),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -321,8 +322,18 @@ def moe_ffn(layer, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_of
 
 
 def moe_debug_hidden(layer, q, k, ws, h=None, hq=None, hs=None, stream=None):
-    _check(lib().rfx_moe_debug_hidden(layer.ref(), q, k, _dptr(ws), _dptr(h), _dptr(hq), _dptr(hs),
-                                      _stream(stream)))
+    _check(lib().rfx_moe_debug_hidden(layer.ref(), q, k, _dptr(ws), ws.numel() * ws.element_size(), _dptr(h),
+                                      _dptr(hq), _dptr(hs), _stream(stream)))
+
+
+def moe_debug_prefill(layer, q, k, xq, xs, topk_w, pairs_sorted, expert_off, ws, probe_expert, probe_first,
+                      h=None, dots_gate=None, dots_up=None, dots_down=None, stream=None):
+    """Test hook of the prefill path: reruns gate/up and down with the fp32 h
+    and one work item's block dots stored (see include/rfx.h)."""
+    _check(lib().rfx_moe_debug_prefill(layer.ref(), q, k, _dptr(xq), _dptr(xs), _dptr(topk_w), _dptr(pairs_sorted),
+                                       _dptr(expert_off), _dptr(ws), ws.numel() * ws.element_size(), probe_expert,
+                                       probe_first, _dptr(h), _dptr(dots_gate), _dptr(dots_up), _dptr(dots_down),
+                                       _stream(stream)))
 
 
 from .layer import DeviceMoeLayer, MoeBuffers  # noqa: E402,F401

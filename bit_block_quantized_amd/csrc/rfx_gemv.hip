@@ -423,15 +423,62 @@ __device__ __forceinline__ void gemv_body_mx(const GemvArgs &a, int p, int g, fl
         gemv_finish<Q>(a, p, g, W, red);
 }
 
+// Test hook on the block-scaled matrix core: the products gemv_body_mx
+// computes, each block's value 2^(E-128) D read before the activation scale
+// and multiplied back by 2^(128-E) (exact: a power of two). The stored dot
+// is that integer, or INT32_MIN when the value the matrix core produced is
+// not one (lost to the fp32 range), so an inexact product never passes.
+// Workgroup of W waves on row group g, no K split.
+template <int Q, bool FULL>
+__device__ __forceinline__ void gemv_dots_mx(const GemvArgs &a, int g)
+{
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    XCols<Q> xc;
+    xc.xq = a.xq;
+    xc.xs = nullptr;
+    xc.xsum = a.xsum;
+#pragma unroll
+    for (int j = 0; j < Q; j++) {
+        xc.xoff[j] = (uint32_t)j * (uint32_t)a.K;
+        xc.moff[j] = (uint32_t)j * (uint32_t)a.nb;
+    }
+    const MxLane<Q> ml = mx_lane<Q>(lane, xc);
+    constexpr int TB = TileFmt<RFX_FP4>::bytes;
+    const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * wave) / (unsigned)W));
+    const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(a.S * (wave + 1)) / (unsigned)W));
+    for (int s = s_begin; s < s_end; s++) {
+        const uint8_t *tile = a.W + ((size_t)g * a.S + s) * TB;
+        MxTile<Q> t;
+        t.x = load_mx_x<Q, FULL, false>(s, a.nb, xc, ml);
+        t.w = load_mx_w(tile, lane);
+        mx_block_values<Q>(t.w, t.x, ml, lane, [&](int col, int r, int tb, float v) {
+            const int row = g * 64 + r, blk = s * 8 + tb;
+            if (row < a.N && blk < a.nb) {
+                const int e = tile[8192 + r * 8 + tb];
+                const float dv = ldexpf(v, 128 - e);
+                int di = INT32_MIN;
+                if (fabsf(dv) < 2147483648.0f && (float)(int)dv == dv)
+                    di = (int)dv;
+                a.dots[((size_t)col * a.N + row) * a.nb + blk] = di;
+            }
+        });
+    }
+}
+
 // One GEMV; grid = (P, G).
 template <int FMT, int Q, bool DOTS, bool FULL>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 {
     __shared__ float red[16 * Q * 64];
-    if constexpr (use_mx<FMT, Q>() && !DOTS)
-        gemv_body_mx<Q, FULL, false>(a, blockIdx.x, blockIdx.y, red);
-    else
+    if constexpr (use_mx<FMT, Q>()) {
+        if constexpr (DOTS)
+            gemv_dots_mx<Q, FULL>(a, blockIdx.y);
+        else
+            gemv_body_mx<Q, FULL, false>(a, blockIdx.x, blockIdx.y, red);
+    } else {
         gemv_body<FMT, Q, DOTS, FULL>(a, blockIdx.x, blockIdx.y, red);
+    }
 }
 
 // Several independent GEMVs in one launch. The workgroups are the jobs'

@@ -1155,7 +1155,7 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
         return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
     if (resid && (st = check_ptr(resid, 16, "resid")))
         return st;
-    if (q > kMaxDecodeQ) // many tokens: grouped int8 MFMA path
+    if (q > kMaxDecodeQ) // many tokens: grouped matrix-core path
         return prefill_ffn(L, q, k, xq, xs, topk_w, pairs_sorted, expert_off, resid, y, w, (hipStream_t)stream);
     FfnArgs a{};
     a.gate = static_cast<const uint8_t *>(L->gate.data);
@@ -1216,8 +1216,8 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     return st;
 }
 
-int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, float *h, int8_t *hq, float *hs,
-                         void *stream)
+int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, size_t ws_bytes, float *h,
+                         int8_t *hq, float *hs, void *stream)
 {
     int st = check_layer(L);
     if (st)
@@ -1229,6 +1229,9 @@ int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, f
     if (h && q > kMaxDecodeQ)
         return fail(RFX_E_UNSUPPORTED, "rfx_moe_debug_hidden: h (fp32) is not kept for q > %d", kMaxDecodeQ);
     MoeWs w = carve(const_cast<void *>(ws), q, k, L->n_experts, L->hidden, L->inter);
+    if (ws_bytes < w.bytes)
+        return fail(RFX_E_WORKSPACE, "rfx_moe_debug_hidden: workspace %zu < %zu bytes for q=%d k=%d", ws_bytes,
+                    w.bytes, q, k);
     const size_t NP = (size_t)q * k + q;
     const hipStream_t s = (hipStream_t)stream;
     if (h && hipMemcpyAsync(h, w.h, NP * L->inter * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
@@ -1238,6 +1241,43 @@ int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, f
     if (hs && hipMemcpyAsync(hs, w.hs, NP * (L->inter / 32) * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
         return hip_status("debug copy hs");
     return RFX_OK;
+}
+
+int rfx_moe_debug_prefill(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
+                          const float *topk_w, const int32_t *pairs_sorted, const int32_t *expert_off, void *ws,
+                          size_t ws_bytes, int probe_expert, int probe_first, float *h, int32_t *dots_gate,
+                          int32_t *dots_up, int32_t *dots_down, void *stream)
+{
+    int st = check_layer(L);
+    if (st)
+        return st;
+    if (q <= kMaxDecodeQ || q > kMaxPrefillQ || k < 1 || k > kMaxK || k > L->n_experts)
+        return fail(RFX_E_INVAL, "rfx_moe_debug_prefill: q=%d k=%d (q must be %d..%d)", q, k, kMaxDecodeQ + 1,
+                    kMaxPrefillQ);
+    const bool has_shared = L->sh_gate.data != nullptr;
+    if (probe_expert < 0 || probe_expert > L->n_experts || (probe_expert == L->n_experts && !has_shared) ||
+        probe_first < 0 || probe_first % kPrefillChunk)
+        return fail(RFX_E_INVAL, "rfx_moe_debug_prefill: probe (expert %d, first %d)", probe_expert, probe_first);
+    if ((st = check_ptr(xq, 16, "xq")) || (st = check_ptr(xs, 4, "xs")) || (st = check_ptr(topk_w, 4, "topk_w")) ||
+        (st = check_ptr(pairs_sorted, 4, "pairs_sorted")) || (st = check_ptr(expert_off, 4, "expert_off")) ||
+        (st = check_ptr(ws, 256, "ws")))
+        return st;
+    if ((h && (st = check_ptr(h, 4, "h"))) || (dots_gate && (st = check_ptr(dots_gate, 4, "dots_gate"))) ||
+        (dots_up && (st = check_ptr(dots_up, 4, "dots_up"))) ||
+        (dots_down && (st = check_ptr(dots_down, 4, "dots_down"))))
+        return st;
+    MoeWs w = carve(ws, q, k, L->n_experts, L->hidden, L->inter);
+    if (ws_bytes < w.bytes)
+        return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    PrefillDebug dbg{};
+    dbg.h = h;
+    dbg.probe_expert = probe_expert;
+    dbg.probe_first = probe_first;
+    dbg.dots[0] = dots_gate;
+    dbg.dots[1] = dots_up;
+    dbg.dots[2] = dots_down;
+    return prefill_ffn(L, q, k, xq, xs, topk_w, pairs_sorted, expert_off, nullptr, nullptr, w, (hipStream_t)stream,
+                       &dbg);
 }
 
 } // extern "C"

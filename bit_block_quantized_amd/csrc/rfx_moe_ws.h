@@ -88,8 +88,19 @@ inline MoeWs carve(void *base, int q, int k, int E, int H, int I)
 int prefill_route(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx, float *topk_w,
                   int32_t *pairs_sorted, int32_t *expert_off, int8_t *xq, float *xs, int32_t *xsum,
                   const MoeWs &w, hipStream_t stream);
+// Test-hook stores of the prefill FFN kernels: the fp32 h of every row
+// ([q*k + q][I], or null) and, for the work item (probe_expert,
+// probe_first), the block dots of gate, up ([I][64][H/32]) and down
+// ([H][64][I/32]) (any may be null).
+struct PrefillDebug {
+    float *h;
+    int probe_expert, probe_first;
+    int32_t *dots[3];
+};
+// dbg non-null: the gate/up and down kernels with the test-hook stores,
+// no combine.
 int prefill_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid, float *y,
-                const MoeWs &w, hipStream_t stream);
+                const MoeWs &w, hipStream_t stream, const PrefillDebug *dbg = nullptr);
 
 } // namespace rfx

@@ -138,8 +138,9 @@ __device__ __forceinline__ MxW load_mx_w(const uint8_t *__restrict__ tile, int l
 }
 
 // Activation block of (h, lane): s * 8 + 2 bn + h, clamped into K (the
-// weights past K are zero).
-template <int Q, bool FULL>
+// weights past K are zero). SX = false leaves the scales out (the block-dot
+// test hook has none).
+template <int Q, bool FULL, bool SX = true>
 __device__ __forceinline__ MxX<Q> load_mx_x(int s, int nb, const XCols<Q> &xc, const MxLane<Q> &ml)
 {
     MxX<Q> x;
@@ -149,7 +150,7 @@ __device__ __forceinline__ MxX<Q> load_mx_x(int s, int nb, const XCols<Q> &xc, c
 #pragma unroll
         for (int p = 0; p < MxX<Q>::NP; p++) {
             x.xr[h][p] = *reinterpret_cast<const u32x4 *>(xc.xq + (ml.xo[p] + 32u * (uint32_t)blk));
-            const float sxv = xc.xs[ml.mo[p] + (uint32_t)blk];
+            const float sxv = SX ? xc.xs[ml.mo[p] + (uint32_t)blk] : 0.0f;
             x.sx[h][p] = ml.lo[p] ? sxv : 0.0f;
         }
     }
@@ -246,6 +247,40 @@ __device__ __forceinline__ void compute_mx(const MxW (&w)[M], const MxX<Q> &x, c
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The products of compute_mx for one weight matrix, stopped before the
+// activation scale: for every (half, pair, g) the low-part lanes hold
+// 2^(E-128) D, E the block exponent and D the block's integer dot, of their
+// (column, tile row, tile block), handed to store(col, row, blk, value).
+// Same operands, same products and the same high-into-low fold as the
+// product path; every lane takes part in the products and the fold.
+template <int Q, typename Store>
+__device__ __forceinline__ void mx_block_values(const MxW &w, const MxX<Q> &x, const MxLane<Q> &ml, int lane,
+                                                Store store)
+{
+    const int rq = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int p = 0; p < MxX<Q>::NP; p++) {
+            const i32x8 b = build_b<Q>(x.xr[h][p], ml, p);
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const f32x4 d = h == 0 ? mx_product<0>(w.a[2 * g], b, w.sa[g], ml.sb[p])
+                                       : mx_product<1>(w.a[2 * g + 1], b, w.sa[g], ml.sb[p]);
+                float blk[4];
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    blk[v] = d[v] + (p == 0 ? high_part<0>(d[v]) : high_part<1>(d[v]));
+                if (ml.lo[p]) {
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        store(2 * p + (n >> 3), 16 * g + 4 * rq + v, 2 * ml.bn + h, blk[v]);
+                }
+            }
         }
     }
 }

@@ -1,6 +1,6 @@
 // Prefill-sized MoE layer for gfx950: router over many tokens, stable
 // bucketing of the (token, slot) pairs by expert, and the expert FFN as
-// grouped int8 MFMA tiles with a per-block fp32 rescale.
+// grouped matrix-core tiles with a per-block fp32 rescale.
 //
 // Pages cited (title, site):
 //   [HM]  "DeepSeek V4 Flash hits 32 tok/s on AMD Ryzen AI MAX+ 395"
@@ -12,11 +12,14 @@
 // section): after the argsort every expert's tokens are contiguous, so with
 // thousands of tokens each expert's FFN is a small dense contraction
 // (tens of tokens x 2048 x 4096). There the packed FP2/FP3/FP4 blocks are
-// expanded through their codebooks into int8 operand tiles in LDS and fed to
-// v_mfma_i32_16x16x32_i8: one MFMA K step is exactly one 32-weight block, so
-// its int32 result is the exact block dot D, which is then scaled by the
-// weight and activation block scales in fp32 (the same sum as the decode
-// kernels, over the same blocks in the same order per output).
+// expanded through their codebooks into matrix-core operand fragments and
+// multiplied with the int8 activations one 32-weight block per instruction,
+// so each result is the exact integer block dot D, which is then scaled by
+// the weight and activation block scales in fp32 (the same sum as the
+// decode kernels, over the same blocks in the same order per output).
+// The operands are the codes' integer values held as f16 (exact: at most
+// 12 and 127 in magnitude) on v_mfma_f32_16x16x32_f16, whose fp32 result
+// needs no conversion before the rescale.
 //
 // Launches per layer: act quant, router logits (fp32 matrix core), softmax /
 // top-k, bucket (one workgroup), gate/up (+ SwiGLU + requantization), down,
@@ -310,8 +313,38 @@ __global__ __launch_bounds__(1024) void bucket_kernel(BucketArgs a)
 }
 
 // ------------------------------------------------------------------
-// Grouped FFN on MFMA.
+// Grouped FFN on the matrix core.
+//
+// Each work item is up to 64 tokens of one expert. A workgroup of eight
+// waves takes one item and a range of output rows; per 256-column K tile
+// the item's int8 activations are staged once into LDS as f16 operand
+// fragments, and every wave decodes the packed blocks of its own rows
+// straight from memory into f16 fragments through the codebook (byte
+// permutes of a table of f16 high bytes: every codebook value is a small
+// integer whose f16 low byte is zero). v_mfma_f32_16x16x32_f16 then takes
+// one 32-weight block per instruction: its operands are the int8 codes'
+// exact integer values and its fp32 sum of 32 products (each at most
+// 12 x 127, the sum below 2^24) is the exact block dot D, the integer dot
+// product of the method ([HM] para 3) carried in an fp32 register. D is
+// then scaled by the weight and activation block scales: one multiply and
+// one fused multiply-add per output and block.
+//
+// MFMA operands: A = activations (lane l: token l % 16 of the token tile,
+// K group l / 16 = values 8 (l / 16) .. +7 of the block), B = weights
+// (lane l: row l % 16 of the row tile, the same K group); output lane l,
+// register v: token 4 (l / 16) + v, row l % 16. A lane's eight weights are
+// taken from the packed words in the order the bit layout stores them,
+// which for every format is K order 8g .. 8g + 7.
 // ------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFfnWaves = 8;
+constexpr int kFfnThreads = 64 * kFfnWaves;
+constexpr int kGateRows = 16 * kFfnWaves;      // gate/up: one 16-row tile of each matrix per wave
+constexpr int kDownRT = 2;                     // down: row tiles per wave
+constexpr int kDownRows = 16 * kDownRT * kFfnWaves;
+
 struct FfnArgs {
     const uint8_t *gate, *up, *down; // routed stacks
     size_t gate_stride, up_stride, down_stride;
@@ -325,6 +358,11 @@ struct FfnArgs {
     const float *resid;
     float *y;
     MoeWs ws;
+    // test hook (DBG kernels only): fp32 h of every row, and the block dots
+    // of one work item, [row][slot][block] per matrix (gate, up, down)
+    float *dbg_h;
+    int probe_expert, probe_first;
+    int32_t *dots[3];
 };
 
 struct Item {
@@ -361,134 +399,147 @@ __device__ __forceinline__ void slot_rows(const FfnArgs &a, const Item &it, int 
     }
 }
 
-// Expand block b of row tr of one tile into 32 int8 codebook values (8
-// dwords, weights 4d..4d+3 in dword d) and its weight scale.
-template <int FMT>
-__device__ __forceinline__ void expand_block(const uint8_t *tile, int tr, int b, uint32_t (&v)[8], float &sw)
-{
-    if (FMT == RFX_FP4) {
-        const u32x4 c = *reinterpret_cast<const u32x4 *>(tile + b * 1024 + tr * 16);
-        const Sel8 sv = sel_fp4(c);
-#pragma unroll
-        for (int d = 0; d < 8; d++)
-            v[d] = (uint32_t)sv.v[d];
-        const uint32_t e = tile[8192 + tr * 8 + b];
-        sw = ldexpf(1.0f, (int)e - 128);
-    } else {
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(tile + (b >> 1) * 1024 + tr * 16 + (b & 1) * 8);
-        const uint32_t w[2] = {lo.x, lo.y};
-        uint32_t h = 0;
-        if (FMT == RFX_FP3)
-            h = *reinterpret_cast<const uint32_t *>(tile + (4 + (b >> 2)) * 1024 + tr * 16 + (b & 3) * 4);
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-            uint32_t sel = (w[d >> 2] >> (2 * (d & 3))) & 0x03030303u;
-            if (FMT == RFX_FP3) {
-                sel |= ((h >> d) & 0x01010101u) << 2;
-                // {-7 -5 -3 -1 | 1 3 5 7}
-                v[d] = __builtin_amdgcn_perm(0x07050301u, 0xFFFDFBF9u, sel);
-            } else {
-                // {-3 -1 1 3}
-                v[d] = __builtin_amdgcn_perm(0u, 0x0301FFFDu, sel);
-            }
-        }
-        const int sc = FMT == RFX_FP3 ? 6 : 4;
-        sw = half_bits_to_float(*reinterpret_cast<const uint16_t *>(tile + sc * 1024 + tr * 16 + b * 2));
-    }
-}
+// f16 high bytes of the codebook values (the low bytes are zero).
+// FP2 {-3, -1, 1, 3}; FP3 {-7, -5, ..., 7}; FP4 magnitudes {0, 1, 2, 3, 4,
+// 6, 8, 12} (2 x E2M1), the sign going to bit 7.
+constexpr uint32_t kH2 = 0x423CBCC2u;
+constexpr uint32_t kH3Lo = 0xBCC2C5C7u, kH3Hi = 0x4745423Cu;
+constexpr uint32_t kH4Lo = 0x42403C00u, kH4Hi = 0x4A484644u;
 
-// LDS operand fragments of v_mfma_i32_16x16x32_i8: lane l of a 16-row
-// (A) or 16-token (B) tile holds row / token l % 16, k = 8 (l / 16) .. +7
-// of one 32-k block. Fragment [tile][block][lane] = 8 bytes.
-__device__ __forceinline__ void put_frag(uint2 *frag_base, int r16, const uint32_t (&v)[8])
-{
-#pragma unroll
-    for (int kg = 0; kg < 4; kg++)
-        frag_base[r16 + 16 * kg] = make_uint2(v[2 * kg], v[2 * kg + 1]);
-}
+// One lane's packed words of one 256-column tile: per block, the word that
+// holds its K group (FP3: the low-bit word, then the high-bit word), and
+// its row's block scales.
+template <int F>
+struct WRow {
+    uint32_t c[F == RFX_FP3 ? 16 : 8];
+    uint32_t s[F == RFX_FP4 ? 2 : 4];
+};
 
-// Stage the activation slice of K tile s for up to 64 slots into LDS B
-// fragments (4 token tiles x 8 blocks x 64 lanes) and their block scales.
-// Thread (slot i = tid / 4, quarter qd = tid % 4) moves blocks 2qd, 2qd+1.
-// Slots past n and blocks past nb are zero.
-__device__ __forceinline__ void stage_b(const int8_t *rows, const float *scales, size_t row_stride,
-                                        size_t scale_stride, const int *slot_src, int n, int s, int nb,
-                                        uint2 *lB, float *lsx)
+// row r (0..63) of tile `tile`, lane K group g.
+template <int F>
+__device__ __forceinline__ WRow<F> load_wrow(const uint8_t *__restrict__ tile, int r, int g)
 {
-    const int tid = threadIdx.x;
-    const int i = tid >> 2, qd = tid & 3;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int b = 2 * qd + h;
-        const int blk = s * 8 + b;
-        uint32_t v[8];
-        float sx = 0.0f;
-        if (i < n && blk < nb) {
-            const int src = slot_src[i];
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
-            const u32x4 c0 = p[0], c1 = p[1];
-            v[0] = c0.x;
-            v[1] = c0.y;
-            v[2] = c0.z;
-            v[3] = c0.w;
-            v[4] = c1.x;
-            v[5] = c1.y;
-            v[6] = c1.z;
-            v[7] = c1.w;
-            sx = scales[(size_t)src * scale_stride + blk];
-        } else {
-#pragma unroll
-            for (int d = 0; d < 8; d++)
-                v[d] = 0u;
-        }
-        put_frag(lB + ((i >> 4) * 8 + b) * 64, i & 15, v);
-        lsx[b * 64 + i] = sx;
-    }
-}
-
-// One K tile of MFMA work for one wave: a 16-row A tile against up to 4
-// token tiles over 8 blocks. acc[tt][r] is row 4 (lane / 16) + r of the
-// tile, token 16 tt + lane % 16. lsw: the tile's row scales, block stride
-// sw_stride. Each MFMA is one block: its int32 result is the exact block
-// dot, scaled by (weight scale x activation scale) into fp32.
-__device__ __forceinline__ void mfma_tile(const uint2 *lA_tile, const float *lsw, int sw_stride, const uint2 *lB,
-                                          const float *lsx, int ntt, int lane, float (&acc)[4][4])
-{
+    WRow<F> w;
+    const uint8_t *rp = tile + r * 16;
 #pragma unroll
     for (int b = 0; b < 8; b++) {
-        const uint2 av = lA_tile[b * 64 + lane];
-        const long a8 = (long)(((unsigned long)av.y << 32) | av.x);
-        const float4 sw = *reinterpret_cast<const float4 *>(lsw + b * sw_stride + 4 * (lane >> 4));
-#pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            if (tt >= ntt)
-                break;
-            const uint2 bv = lB[(tt * 8 + b) * 64 + lane];
-            const long b8 = (long)(((unsigned long)bv.y << 32) | bv.x);
-            const i32x4 zero = {0, 0, 0, 0};
-            const i32x4 d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8, b8, zero, 0, 0, 0);
-            const float sx = lsx[b * 64 + 16 * tt + (lane & 15)];
-            acc[tt][0] += (float)d[0] * (sw.x * sx);
-            acc[tt][1] += (float)d[1] * (sw.y * sx);
-            acc[tt][2] += (float)d[2] * (sw.z * sx);
-            acc[tt][3] += (float)d[3] * (sw.w * sx);
+        if constexpr (F == RFX_FP4) {
+            w.c[b] = *reinterpret_cast<const uint32_t *>(rp + b * 1024 + g * 4);
+        } else {
+            const uint32_t lo = *reinterpret_cast<const uint32_t *>(rp + (b >> 1) * 1024 + (b & 1) * 8 + (g >> 1) * 4);
+            if constexpr (F == RFX_FP3) {
+                w.c[2 * b] = lo;
+                w.c[2 * b + 1] = *reinterpret_cast<const uint32_t *>(rp + (4 + (b >> 2)) * 1024 + (b & 3) * 4);
+            } else {
+                w.c[b] = lo;
+            }
         }
     }
+    if constexpr (F == RFX_FP4) {
+        const u32x2 s = *reinterpret_cast<const u32x2 *>(tile + 8192 + r * 8);
+        w.s[0] = s.x;
+        w.s[1] = s.y;
+    } else {
+        const u32x4 s = *reinterpret_cast<const u32x4 *>(rp + (F == RFX_FP3 ? 6 : 4) * 1024);
+        w.s[0] = s.x;
+        w.s[1] = s.y;
+        w.s[2] = s.z;
+        w.s[3] = s.w;
+    }
+    return w;
 }
 
-// LDS map of the FFN kernels (bytes): A fragments 16 KB, B fragments 16 KB,
-// row scales 2 KB, slot scales 2 KB, slot maps 512 B. The SwiGLU epilogue
-// reuses the fragment area for the [2][32][65] fp32 gate/up tile.
-constexpr int kLdsA = 0, kLdsB = 16384, kLdsSw = 32768, kLdsSx = 34816, kLdsRow = 36864, kLdsTok = 37120;
-constexpr int kLdsBytes = 37376;
-
-__device__ __forceinline__ void zero_acc(float (&acc)[4][4])
+// Weights 8g..8g+7 of block b as eight f16 values.
+template <int F>
+__device__ __forceinline__ f16x8 wfrag(const WRow<F> &w, int b, int g)
 {
+    uint32_t ha, hb; // f16 high bytes of weights 8g..8g+3 and 8g+4..8g+7
+    if (F == RFX_FP4) {
+        // word g: weight 8g + 4i + j at bits 8j + 4i
+        const uint32_t na = w.c[b] & 0x0F0F0F0Fu, nb = (w.c[b] >> 4) & 0x0F0F0F0Fu;
+        ha = __builtin_amdgcn_perm(kH4Hi, kH4Lo, na & 0x07070707u) | ((na << 4) & 0x80808080u);
+        hb = __builtin_amdgcn_perm(kH4Hi, kH4Lo, nb & 0x07070707u) | ((nb << 4) & 0x80808080u);
+    } else {
+        // word g / 2: weight 16m + 4i + j at bits 8j + 2i; the K group
+        // takes i = 2 (g % 2) and i + 1
+        const uint32_t word = F == RFX_FP3 ? w.c[2 * b] : w.c[b];
+        const uint32_t sh = 4u * (uint32_t)(g & 1);
+        uint32_t sa = (word >> sh) & 0x03030303u, sb = (word >> (sh + 2u)) & 0x03030303u;
+        if (F == RFX_FP3) {
+            // high bit of weight 4i + j at bit 8j + i, i = 2g and 2g + 1
+            const uint32_t h = w.c[2 * b + 1] >> (2u * (uint32_t)g);
+            sa |= (h & 0x01010101u) << 2;
+            sb |= ((h >> 1) & 0x01010101u) << 2;
+            ha = __builtin_amdgcn_perm(kH3Hi, kH3Lo, sa);
+            hb = __builtin_amdgcn_perm(kH3Hi, kH3Lo, sb);
+        } else {
+            ha = __builtin_amdgcn_perm(0u, kH2, sa);
+            hb = __builtin_amdgcn_perm(0u, kH2, sb);
+        }
+    }
+    const u32x4 v = {__builtin_amdgcn_perm(0u, ha, 0x010C000Cu), __builtin_amdgcn_perm(0u, ha, 0x030C020Cu),
+                     __builtin_amdgcn_perm(0u, hb, 0x010C000Cu), __builtin_amdgcn_perm(0u, hb, 0x030C020Cu)};
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// Weight scale of block b of the lane's row.
+template <int F>
+__device__ __forceinline__ float wscale(const WRow<F> &w, int b)
+{
+    if (F == RFX_FP4) {
+        const uint32_t e = (w.s[b >> 2] >> (8 * (b & 3))) & 0xffu;
+        return ldexpf(1.0f, (int)e - 128);
+    }
+    const uint32_t s2 = w.s[b >> 1];
+    return half_bits_to_float((b & 1) ? (s2 >> 16) : (s2 & 0xffffu));
+}
+
+// Four int8 codes -> two dwords of f16 (exact: f16 holds 1024 + u exactly
+// for u = x + 128 in 0..255).
+__device__ __forceinline__ void i8x4_to_f16(uint32_t x, uint32_t &p01, uint32_t &p23)
+{
+    const uint32_t u = x ^ 0x80808080u;
+    const f16x2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    p01 = __builtin_bit_cast(uint32_t,
+                             __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off);
+    p23 = __builtin_bit_cast(uint32_t,
+                             __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
+}
+
+// LDS map (bytes): activation fragments [4 token tiles][8 blocks][64
+// lanes] x 16 B = 32 KB; slot scales [8 blocks][64 slots] fp32 2 KB; slot
+// maps 2 x 256 B. The epilogues reuse the fragment area.
+constexpr int kLdsFrag = 0, kLdsSx = 32768, kLdsRow = 34816, kLdsTok = 35072;
+constexpr int kLdsBytes = 35328;
+
+// Stage K tile s of the item's activation rows (rows[src(i)], 32 int8 per
+// block, fp32 block scales) as f16 fragments. Wave w takes block w of the
+// tile, lane i the slot. Slots past n and blocks past nb are zero.
+__device__ __forceinline__ void stage_act(const int8_t *rows, const float *scales, size_t row_stride,
+                                          size_t scale_stride, const int *slot_src, int n, int s, int nb,
+                                          uint32_t *frag, float *lsx)
+{
+    const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
+    const int blk = s * 8 + b;
+    u32x4 c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
+    float sx = 0.0f;
+    if (i < n && blk < nb) {
+        const int src = slot_src[i];
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
+        c0 = p[0];
+        c1 = p[1];
+        sx = scales[(size_t)src * scale_stride + blk];
+    }
+    const uint32_t x[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    u32x4 *f = reinterpret_cast<u32x4 *>(frag) + ((i >> 4) * 8 + b) * 64 + (i & 15);
 #pragma unroll
-    for (int tt = 0; tt < 4; tt++)
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-            acc[tt][r] = 0.0f;
+    for (int g = 0; g < 4; g++) {
+        uint32_t p0, p1, p2, p3;
+        i8x4_to_f16(x[2 * g], p0, p1);
+        i8x4_to_f16(x[2 * g + 1], p2, p3);
+        f[16 * g] = u32x4{p0, p1, p2, p3};
+    }
+    lsx[b * 64 + i] = sx;
 }
 
 // Slot -> (h / o row, token) maps of an item, in LDS.
@@ -504,109 +555,163 @@ __device__ __forceinline__ void fill_slots(const FfnArgs &a, const Item &it, int
     }
 }
 
-// Gate/up: one workgroup = 32 intermediate rows of gate and of up x one
-// item. Wave w: matrix w >> 1 (gate, up), row tile w & 1. Epilogue:
-// h = silu(g) * u and the per-32 requantization of h, whose 32-row block
-// is exactly this workgroup's rows.
-template <int F>
-__device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm, const uint8_t *um, char *smem)
+// One K tile for one wave: M weight row tiles (w[m]) against the item's
+// ntt token tiles. acc[m][tt][v]: token 16 tt + 4 (l / 16) + v, row l % 16
+// of tile m. With DBG and `dots`, each block dot goes to dots[m] (rows of
+// the tile from row0[m], stride nbk blocks, 64 slots).
+template <int F, int M, bool DBG>
+__device__ __forceinline__ void ffn_tile(const WRow<F> (&w)[M], const uint32_t *frag, const float *lsx, int ntt,
+                                         int n, int s, int nb, float (&acc)[M][4][4], int32_t *const (&dots)[M],
+                                         const int (&row0)[M], int R)
 {
-    uint2 *lA = reinterpret_cast<uint2 *>(smem + kLdsA); // [2 mat][2 rt][8 b][64]
-    uint2 *lB = reinterpret_cast<uint2 *>(smem + kLdsB); // [4 tt][8 b][64]
-    float *lsw = reinterpret_cast<float *>(smem + kLdsSw); // [2 mat][8 b][32 rows]
-    float *lsx = reinterpret_cast<float *>(smem + kLdsSx); // [8 b][64 slots]
-    int *slot_row = reinterpret_cast<int *>(smem + kLdsRow);
-    int *slot_tok = reinterpret_cast<int *>(smem + kLdsTok);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r0 = blockIdx.x * 32, g = r0 >> 6, half = r0 & 63;
-    const int S = (a.H + 255) / 256, nbH = a.H / 32;
-    constexpr int TBYTES = TileFmt<F>::bytes;
-    fill_slots(a, it, slot_row, slot_tok);
-    __syncthreads();
-    const int ntt = (it.n + 15) >> 4;
-    float acc[4][4];
-    zero_acc(acc);
-    const int mat = wave >> 1, rt = wave & 1;
-    for (int s = 0; s < S; s++) {
-        {
-            // A: thread -> (row r, block b) of gate and of up
-            const int r = tid & 31, b = tid >> 5;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 2; m++) {
-                const uint8_t *tile = (m == 0 ? gm : um) + ((size_t)g * S + s) * TBYTES;
-                uint32_t v[8];
-                float sw = 0.0f;
-                if (s * 8 + b < nbH) {
-                    expand_block<F>(tile, half + r, b, v, sw);
-                } else {
+    for (int b = 0; b < 8; b++) {
+        if (s * 8 + b >= nb)
+            break;
+        f16x8 wv[M];
+        float sw[M];
 #pragma unroll
-                    for (int d = 0; d < 8; d++)
-                        v[d] = 0u;
+        for (int m = 0; m < M; m++) {
+            wv[m] = wfrag<F>(w[m], b, g);
+            sw[m] = wscale<F>(w[m], b);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++) {
+            if (tt >= ntt)
+                break;
+            const f16x8 av = __builtin_bit_cast(f16x8, reinterpret_cast<const u32x4 *>(frag)[(tt * 8 + b) * 64 + lane]);
+            const f32x4 sx = *reinterpret_cast<const f32x4 *>(lsx + b * 64 + 16 * tt + 4 * g);
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wv[m], zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    acc[m][tt][v] = fmaf(d[v], sw[m] * sx[v], acc[m][tt][v]);
+                if (DBG && dots[m]) {
+                    const int row = row0[m] + (lane & 15);
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        const int slot = 16 * tt + 4 * g + v;
+                        if (slot < n && row < R)
+                            dots[m][((size_t)row * 64 + slot) * nb + s * 8 + b] = (int)d[v];
+                    }
                 }
-                put_frag(lA + ((m * 2 + (r >> 4)) * 8 + b) * 64, r & 15, v);
-                lsw[(m * 8 + b) * 32 + r] = sw;
             }
         }
-        stage_b(a.xq, a.xs, (size_t)a.H, (size_t)nbH, slot_tok, it.n, s, nbH, lB, lsx);
-        __syncthreads();
-        mfma_tile(lA + (mat * 2 + rt) * 8 * 64, lsw + mat * 8 * 32 + 16 * rt, 32, lB, lsx, ntt, lane, acc);
-        __syncthreads();
     }
+}
 
-    // epilogue: gate and up tiles meet in LDS
-    float *hb = reinterpret_cast<float *>(smem + kLdsA); // [2][32][65]
+// Gate/up: one workgroup = 128 intermediate rows of gate and of up x one
+// item; wave w: row tile w of each. Epilogue: h = silu(g) * u and the
+// per-32 requantization of h (a 32-row block is two waves' tiles).
+template <int F, bool DBG>
+__device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm, const uint8_t *um, char *smem)
+{
+    uint32_t *frag = reinterpret_cast<uint32_t *>(smem + kLdsFrag);
+    float *lsx = reinterpret_cast<float *>(smem + kLdsSx);
+    int *slot_row = reinterpret_cast<int *>(smem + kLdsRow);
+    int *slot_tok = reinterpret_cast<int *>(smem + kLdsTok);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r0 = blockIdx.x * kGateRows + 16 * wave; // this wave's first row
+    const int grp = r0 >> 6, rin = (r0 & 63) + (lane & 15);
+    const int S = (a.H + 255) / 256, nbH = a.H / 32;
+    constexpr int TB = TileFmt<F>::bytes;
+    fill_slots(a, it, slot_row, slot_tok);
+    const int ntt = (it.n + 15) >> 4;
+    const bool probe = DBG && it.expert == a.probe_expert && it.first == a.probe_first;
+    int32_t *const dots[2] = {probe ? a.dots[0] : nullptr, probe ? a.dots[1] : nullptr};
+    const int row0[2] = {r0, r0};
+    float acc[2][4][4] = {};
+    const bool rows_ok = r0 < a.I; // waves past I only stage activations
+    for (int s = 0; s < S; s++) {
+        WRow<F> w[2];
+        if (rows_ok) {
+            const size_t toff = ((size_t)grp * S + s) * TB;
+            w[0] = load_wrow<F>(gm + toff, rin, g);
+            w[1] = load_wrow<F>(um + toff, rin, g);
+        }
+        __syncthreads(); // the previous tile's fragments are consumed (and the slot maps written)
+        stage_act(a.xq, a.xs, (size_t)a.H, (size_t)nbH, slot_tok, it.n, s, nbH, frag, lsx);
+        __syncthreads();
+        if (rows_ok)
+            ffn_tile<F, 2, DBG>(w, frag, lsx, ntt, it.n, s, nbH, acc, dots, row0, a.I);
+    }
+    __syncthreads();
+
+    // epilogue: h, amax over this wave's 16 rows per token, then over the
+    // 32-row block (waves 2j, 2j + 1) through LDS
+    float *amax_l = reinterpret_cast<float *>(smem + kLdsFrag);                   // [8 waves][64 slots]
+    int8_t *hq_l = reinterpret_cast<int8_t *>(smem + kLdsFrag + kFfnWaves * 256); // [64 slots][128 rows]
+    float h[4][4], am[4][4];
+    {
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int tt = 0; tt < 4; tt++) {
-        if (tt >= ntt)
-            break;
+        for (int tt = 0; tt < 4; tt++)
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            hb[(mat * 32 + 16 * rt + 4 * (lane >> 4) + r) * 65 + 16 * tt + (lane & 15)] = acc[tt][r];
+            for (int v = 0; v < 4; v++) {
+                const float gv = acc[0][tt][v], uv = acc[1][tt][v];
+                h[tt][v] = gv / (1.0f + expf(-gv)) * uv; // SwiGLU: silu(g) * u
+                float m = fabsf(h[tt][v]);
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1)
+                    m = fmaxf(m, __shfl_xor(m, o, 16));
+                am[tt][v] = m;
+            }
+    }
+    if (DBG && a.dbg_h && rows_ok) {
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int i = 16 * tt + 4 * g + v;
+                if (i < it.n)
+                    a.dbg_h[(size_t)slot_row[i] * a.I + r0 + (lane & 15)] = h[tt][v];
+            }
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                amax_l[wave * 64 + 16 * tt + 4 * g + v] = am[tt][v];
     }
     __syncthreads();
     {
 #pragma clang fp contract(off)
-        const int i = tid >> 2, rg = tid & 3;
-        float hv[8];
-        float amax = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float gv = hb[(8 * rg + j) * 65 + i], uv = hb[(32 + 8 * rg + j) * 65 + i];
-            hv[j] = gv / (1.0f + expf(-gv)) * uv; // SwiGLU: silu(g) * u
-            amax = fmaxf(amax, fabsf(hv[j]));
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-        const float sc = amax / 127.0f;
-        uint32_t packed[2] = {0u, 0u};
-        int sum = 0;
+        for (int tt = 0; tt < 4; tt++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            int qv = 0;
-            if (sc != 0.0f) {
-                float rr = rintf(hv[j] / sc);
-                rr = fminf(fmaxf(rr, -127.0f), 127.0f);
-                qv = (int)rr;
+            for (int v = 0; v < 4; v++) {
+                const int i = 16 * tt + 4 * g + v;
+                const float amax = fmaxf(am[tt][v], amax_l[(wave ^ 1) * 64 + i]);
+                const float sc = amax / 127.0f;
+                int qv = 0;
+                if (sc != 0.0f) {
+                    float rr = rintf(h[tt][v] / sc);
+                    rr = fminf(fmaxf(rr, -127.0f), 127.0f);
+                    qv = (int)rr;
+                }
+                hq_l[i * kGateRows + 16 * wave + (lane & 15)] = (int8_t)qv;
+                if ((wave & 1) == 0 && (lane & 15) == 0 && i < it.n && rows_ok)
+                    a.ws.hs[(size_t)slot_row[i] * (a.I / 32) + (r0 >> 5)] = sc;
             }
-            sum += qv;
-            packed[j >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (j & 3));
-        }
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 2, 64);
-        if (i < it.n) {
-            const size_t row = (size_t)slot_row[i];
-            *reinterpret_cast<uint2 *>(a.ws.hq + row * a.I + r0 + 8 * rg) = make_uint2(packed[0], packed[1]);
-            if (rg == 0) {
-                a.ws.hs[row * (a.I / 32) + blockIdx.x] = sc;
-                a.ws.hsum[row * (a.I / 32) + blockIdx.x] = sum;
-            }
-        }
+    }
+    __syncthreads();
+    {
+        // 64 slots x 128 rows of codes, 16 bytes per thread
+        const int i = tid >> 3, piece = tid & 7;
+        const int row = blockIdx.x * kGateRows + 16 * piece;
+        if (i < it.n && row < a.I)
+            *reinterpret_cast<u32x4 *>(a.ws.hq + (size_t)slot_row[i] * a.I + row) =
+                *reinterpret_cast<const u32x4 *>(hq_l + i * kGateRows + 16 * piece);
     }
 }
 
-template <int FG, int FS>
-__global__ __launch_bounds__(256) void prefill_gateup_kernel(FfnArgs a)
+template <int FG, int FS, bool DBG>
+__global__ __launch_bounds__(kFfnThreads, 4) void prefill_gateup_kernel(FfnArgs a)
 {
     __shared__ __align__(16) char smem[kLdsBytes];
     bool ok;
@@ -614,70 +719,70 @@ __global__ __launch_bounds__(256) void prefill_gateup_kernel(FfnArgs a)
     if (!ok)
         return;
     if (it.expert == a.E)
-        gateup_body<FS>(a, it, a.sh_gate, a.sh_up, smem);
+        gateup_body<FS, DBG>(a, it, a.sh_gate, a.sh_up, smem);
     else
-        gateup_body<FG>(a, it, a.gate + a.gate_stride * (size_t)it.expert, a.up + a.up_stride * (size_t)it.expert,
-                        smem);
+        gateup_body<FG, DBG>(a, it, a.gate + a.gate_stride * (size_t)it.expert,
+                             a.up + a.up_stride * (size_t)it.expert, smem);
 }
 
-// Down: one workgroup = 64 output rows x one item; wave w = row tile w.
-// o[row of slot][output row] in fp32 for the combine.
-template <int F>
+// Down: one workgroup = 256 output rows x one item; wave w: row tiles 2w,
+// 2w + 1. o[row of slot][output row] in fp32 for the combine.
+template <int F, bool DBG>
 __device__ void down_body(const FfnArgs &a, const Item &it, const uint8_t *dm, char *smem)
 {
-    uint2 *lA = reinterpret_cast<uint2 *>(smem + kLdsA); // [4 rt][8 b][64]
-    uint2 *lB = reinterpret_cast<uint2 *>(smem + kLdsB);
-    float *lsw = reinterpret_cast<float *>(smem + kLdsSw); // [8 b][64 rows]
+    uint32_t *frag = reinterpret_cast<uint32_t *>(smem + kLdsFrag);
     float *lsx = reinterpret_cast<float *>(smem + kLdsSx);
     int *slot_row = reinterpret_cast<int *>(smem + kLdsRow);
     int *slot_tok = reinterpret_cast<int *>(smem + kLdsTok);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = blockIdx.x;
     const int S = (a.I + 255) / 256, nbI = a.I / 32;
-    constexpr int TBYTES = TileFmt<F>::bytes;
+    constexpr int TB = TileFmt<F>::bytes;
     fill_slots(a, it, slot_row, slot_tok);
-    __syncthreads();
     const int ntt = (it.n + 15) >> 4;
-    float acc[4][4];
-    zero_acc(acc);
-    for (int s = 0; s < S; s++) {
-        const uint8_t *tile = dm + ((size_t)g * S + s) * TBYTES;
+    const bool probe = DBG && it.expert == a.probe_expert && it.first == a.probe_first;
+    int r0[kDownRT];
+    int32_t *dots[kDownRT];
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int u = tid + 256 * h;
-            const int r = u & 63, b = u >> 6;
-            uint32_t v[8];
-            float sw = 0.0f;
-            if (s * 8 + b < nbI) {
-                expand_block<F>(tile, r, b, v, sw);
-            } else {
-#pragma unroll
-                for (int d = 0; d < 8; d++)
-                    v[d] = 0u;
-            }
-            put_frag(lA + ((r >> 4) * 8 + b) * 64, r & 15, v);
-            lsw[b * 64 + r] = sw;
-        }
-        stage_b(a.ws.hq, a.ws.hs, (size_t)a.I, (size_t)nbI, slot_row, it.n, s, nbI, lB, lsx);
-        __syncthreads();
-        mfma_tile(lA + wave * 8 * 64, lsw + 16 * wave, 64, lB, lsx, ntt, lane, acc);
-        __syncthreads();
+    for (int m = 0; m < kDownRT; m++) {
+        r0[m] = blockIdx.x * kDownRows + 16 * (kDownRT * wave + m);
+        dots[m] = probe ? a.dots[2] : nullptr;
     }
-    const int orow = g * 64 + 16 * wave + 4 * (lane >> 4);
-    if (orow < a.H) {
+    const bool rows_ok = r0[0] < a.H;
+    float acc[kDownRT][4][4] = {};
+    for (int s = 0; s < S; s++) {
+        WRow<F> w[kDownRT];
+        if (rows_ok) {
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            const int i = 16 * tt + (lane & 15);
-            if (tt < ntt && i < it.n)
-                *reinterpret_cast<float4 *>(a.ws.o + (size_t)slot_row[i] * a.H + orow) =
-                    make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+            for (int m = 0; m < kDownRT; m++)
+                w[m] = load_wrow<F>(dm + ((size_t)(r0[m] >> 6) * S + s) * TB, (r0[m] & 63) + (lane & 15), g);
         }
+        __syncthreads();
+        stage_act(a.ws.hq, a.ws.hs, (size_t)a.I, (size_t)nbI, slot_row, it.n, s, nbI, frag, lsx);
+        __syncthreads();
+        if (rows_ok)
+            ffn_tile<F, kDownRT, DBG>(w, frag, lsx, ntt, it.n, s, nbI, acc, dots, r0, a.H);
+    }
+    if (!rows_ok)
+        return;
+#pragma unroll
+    for (int m = 0; m < kDownRT; m++) {
+        const int row = r0[m] + (lane & 15);
+        if (row >= a.H)
+            continue;
+#pragma unroll
+        for (int tt = 0; tt < 4; tt++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int i = 16 * tt + 4 * g + v;
+                if (i < it.n)
+                    a.ws.o[(size_t)slot_row[i] * a.H + row] = acc[m][tt][v];
+            }
     }
 }
 
-template <int FD, int FSD>
-__global__ __launch_bounds__(256) void prefill_down_kernel(FfnArgs a)
+template <int FD, int FSD, bool DBG>
+__global__ __launch_bounds__(kFfnThreads, 4) void prefill_down_kernel(FfnArgs a)
 {
     __shared__ __align__(16) char smem[kLdsBytes];
     bool ok;
@@ -685,9 +790,9 @@ __global__ __launch_bounds__(256) void prefill_down_kernel(FfnArgs a)
     if (!ok)
         return;
     if (it.expert == a.E)
-        down_body<FSD>(a, it, a.sh_down, smem);
+        down_body<FSD, DBG>(a, it, a.sh_down, smem);
     else
-        down_body<FD>(a, it, a.down + a.down_stride * (size_t)it.expert, smem);
+        down_body<FD, DBG>(a, it, a.down + a.down_stride * (size_t)it.expert, smem);
 }
 
 // y[t] = resid[t] + o_shared[t] + sum_j w[t][j] o[t*k + j], slot order.
@@ -714,26 +819,47 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(FfnArgs a, bool ha
     *reinterpret_cast<float4 *>(a.y + (size_t)t * a.H + h) = acc;
 }
 
-template <int FG>
+template <int FG, bool DBG>
 int launch_gateup(int fs, const FfnArgs &a, dim3 grid, hipStream_t st)
 {
     switch (fs) {
-    case RFX_FP2: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP2>), grid, dim3(256), 0, st, a); break;
-    case RFX_FP3: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP3>), grid, dim3(256), 0, st, a); break;
-    case RFX_FP4: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP4>), grid, dim3(256), 0, st, a); break;
+    case RFX_FP2: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP2, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP3, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((prefill_gateup_kernel<FG, RFX_FP4, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
     }
     return hip_status("prefill gate/up launch");
 }
 
-template <int FD>
+template <int FD, bool DBG>
 int launch_down(int fsd, const FfnArgs &a, dim3 grid, hipStream_t st)
 {
     switch (fsd) {
-    case RFX_FP2: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP2>), grid, dim3(256), 0, st, a); break;
-    case RFX_FP3: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP3>), grid, dim3(256), 0, st, a); break;
-    case RFX_FP4: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP4>), grid, dim3(256), 0, st, a); break;
+    case RFX_FP2: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP2, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
+    case RFX_FP3: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP3, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
+    case RFX_FP4: hipLaunchKernelGGL((prefill_down_kernel<FD, RFX_FP4, DBG>), grid, dim3(kFfnThreads), 0, st, a); break;
     }
     return hip_status("prefill down launch");
+}
+
+template <bool DBG>
+int launch_ffn(const rfx_moe_layer *L, const FfnArgs &a, int items, int fsg, int fsd, hipStream_t stream)
+{
+    int st = 0;
+    const dim3 ggrid((L->inter + kGateRows - 1) / kGateRows, items);
+    switch (L->gate.fmt) {
+    case RFX_FP2: st = launch_gateup<RFX_FP2, DBG>(fsg, a, ggrid, stream); break;
+    case RFX_FP3: st = launch_gateup<RFX_FP3, DBG>(fsg, a, ggrid, stream); break;
+    case RFX_FP4: st = launch_gateup<RFX_FP4, DBG>(fsg, a, ggrid, stream); break;
+    }
+    if (st)
+        return st;
+    const dim3 dgrid((L->hidden + kDownRows - 1) / kDownRows, items);
+    switch (L->down.fmt) {
+    case RFX_FP2: st = launch_down<RFX_FP2, DBG>(fsd, a, dgrid, stream); break;
+    case RFX_FP3: st = launch_down<RFX_FP3, DBG>(fsd, a, dgrid, stream); break;
+    case RFX_FP4: st = launch_down<RFX_FP4, DBG>(fsd, a, dgrid, stream); break;
+    }
+    return st;
 }
 
 } // namespace
@@ -784,7 +910,7 @@ int prefill_route(const rfx_moe_layer *L, const float *x, int q, int k, int32_t 
 
 int prefill_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid, float *y,
-                const MoeWs &w, hipStream_t stream)
+                const MoeWs &w, hipStream_t stream, const PrefillDebug *dbg)
 {
     FfnArgs a{};
     a.gate = static_cast<const uint8_t *>(L->gate.data);
@@ -810,30 +936,22 @@ int prefill_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.resid = resid;
     a.y = y;
     a.ws = w;
+    a.probe_expert = -1;
+    a.probe_first = -1;
     const int fsg = has_shared ? L->sh_gate.fmt : L->gate.fmt;
     const int fsd = has_shared ? L->sh_down.fmt : L->down.fmt;
     const int items = prefill_max_items(q, k, L->n_experts);
-    int st = 0;
-    {
-        const dim3 grid(L->inter / 32, items);
-        switch (L->gate.fmt) {
-        case RFX_FP2: st = launch_gateup<RFX_FP2>(fsg, a, grid, stream); break;
-        case RFX_FP3: st = launch_gateup<RFX_FP3>(fsg, a, grid, stream); break;
-        case RFX_FP4: st = launch_gateup<RFX_FP4>(fsg, a, grid, stream); break;
-        }
-        if (st)
-            return st;
+    if (dbg) {
+        a.dbg_h = dbg->h;
+        a.probe_expert = dbg->probe_expert;
+        a.probe_first = dbg->probe_first;
+        for (int m = 0; m < 3; m++)
+            a.dots[m] = dbg->dots[m];
+        return launch_ffn<true>(L, a, items, fsg, fsd, stream);
     }
-    {
-        const dim3 grid((L->hidden + 63) / 64, items);
-        switch (L->down.fmt) {
-        case RFX_FP2: st = launch_down<RFX_FP2>(fsd, a, grid, stream); break;
-        case RFX_FP3: st = launch_down<RFX_FP3>(fsd, a, grid, stream); break;
-        case RFX_FP4: st = launch_down<RFX_FP4>(fsd, a, grid, stream); break;
-        }
-        if (st)
-            return st;
-    }
+    int st = launch_ffn<false>(L, a, items, fsg, fsd, stream);
+    if (st)
+        return st;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((L->hidden / 4 + 255) / 256, q), dim3(256), 0, stream, a,
                        has_shared);
     return hip_status("prefill combine launch");

@@ -233,10 +233,15 @@ typedef struct rfx_gemv_job {
 size_t rfx_gemv_grouped_workspace_bytes(const rfx_gemv_job *jobs, int n_jobs);
 int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_bytes, void *stream);
 
-/* Test hook: the same decode path, storing every per-block integer dot
- * D[j][n][b] (int32 [q][N][K/32]) instead of the scaled sum: the dot of the
- * block's codebook values with the activation codes (FP2M: of the codes
- * 0..3; FP2S: over both halves, D0 + D1). */
+/* Test hook: the decode path rfx_gemv takes for the same format and q,
+ * storing every per-block integer dot D[j][n][b] (int32 [q][N][K/32])
+ * instead of the scaled sum: the dot of the block's codebook values with the
+ * activation codes (FP2M: of the codes 0..3; FP2S: over both halves,
+ * D0 + D1). FP4 with q <= 2 runs on the block-scaled matrix core, which
+ * applies the block exponent inside the product; there the hook reads each
+ * block's product 2^(E-128) D before the activation scale and multiplies it
+ * back by 2^(128-E), storing INT32_MIN for a block whose product is not an
+ * exact integer multiple (a value lost to the fp32 range). No xs is read. */
 int rfx_debug_block_dots(const rfx_qmat *W, const int8_t *xq, const int32_t *xsum, int q,
                          int32_t *dots, void *stream);
 
@@ -298,23 +303,44 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
  * [q][H]. ws: the workspace given to rfx_moe_route_topk may be reused.
  * q <= 4: block-dequant GEMV kernels, each active expert streamed once for
  * its tokens. q > 4 (prefill, needs the ws written by rfx_moe_route_topk):
- * per work item and 32 / 64 rows, the packed blocks are expanded through
- * their codebooks into int8 tiles and multiplied on v_mfma_i32_16x16x32_i8,
- * one MFMA K step per 32-weight block, so each int32 result is the exact
- * block dot, then scaled by the weight and activation block scales in
- * fp32 ([HM] para 3: integer dot products over the packed codes). */
+ * per work item (up to 64 tokens of one expert) and 128 / 256 rows, the
+ * packed blocks are expanded through their codebooks into matrix-core
+ * operands holding the codes' integer values (as f16, exact) and multiplied
+ * with the int8 activations (as f16, exact) on v_mfma_f32_16x16x32_f16, one
+ * instruction per 32-weight block, so each fp32 result is the exact integer
+ * block dot, then scaled by the weight and activation block scales in fp32
+ * ([HM] para 3: integer dot products over the packed codes). */
 int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
                 const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid,
                 float *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Test hook: after rfx_moe_ffn with the same workspace, copy out the
- * intermediate activations of the last call: h fp32 [(q*k)+q][I] (pairs in
- * pair order, then the shared expert per token), h~ int8 and its scales.
- * Any output pointer may be NULL. The prefill path (q > 4) does not keep
- * the fp32 h: h must be NULL there (RFX_E_UNSUPPORTED otherwise). */
-int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, float *h,
+/* Test hook: after rfx_moe_ffn with the same workspace (ws_bytes as given
+ * to it; RFX_E_WORKSPACE when smaller than rfx_moe_workspace_bytes(L, q,
+ * k)), copy out the intermediate activations of the last call: h fp32
+ * [(q*k)+q][I] (pairs in pair order, then the shared expert per token),
+ * h~ int8 and its scales. Any output pointer may be NULL. The prefill path
+ * (q > 4) does not keep the fp32 h: h must be NULL there
+ * (RFX_E_UNSUPPORTED otherwise); rfx_moe_debug_prefill gives it. */
+int rfx_moe_debug_hidden(const rfx_moe_layer *L, int q, int k, const void *ws, size_t ws_bytes, float *h,
                          int8_t *hq, float *hs, void *stream);
+
+/* Test hook of the prefill path (5 <= q <= 65536): after rfx_moe_route_topk
+ * with the same ws, q and k, runs the gate/up and down kernels of
+ * rfx_moe_ffn (not the combine) with extra stores: h fp32 [(q*k)+q][I] (the
+ * SwiGLU output each h~ row was requantized from), and for the one work
+ * item of expert probe_expert (n_experts = the shared expert) whose tokens
+ * start at position probe_first (a multiple of 64) of that expert's token
+ * list, every block dot the matrix core produced: dots_gate and dots_up
+ * int32 [I][64][H/32], dots_down int32 [H][64][I/32], indexed [output row]
+ * [token slot within the item][block]; slots past the item's tokens are
+ * left untouched. Any output pointer may be NULL. The workspace's h~, its
+ * scales and o are rewritten as rfx_moe_ffn writes them. Errors:
+ * RFX_E_INVAL (q, k, probe), RFX_E_ALIGN, RFX_E_WORKSPACE, RFX_E_HIP. */
+int rfx_moe_debug_prefill(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
+                          const float *topk_w, const int32_t *pairs_sorted, const int32_t *expert_off, void *ws,
+                          size_t ws_bytes, int probe_expert, int probe_first, float *h, int32_t *dots_gate,
+                          int32_t *dots_up, int32_t *dots_down, void *stream);
 
 #ifdef __cplusplus
 }

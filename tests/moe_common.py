@@ -58,6 +58,36 @@ class OracleMoe:
     def route(self, x, k):
         return O.route(x, self.s.router_w, self.s.router_b, k)
 
+    def down_abs(self, e):
+        """|dequantized down matrix| of expert e, fp64 [hidden][inter]."""
+        key = ("absdown", e)
+        if key not in self.cache:
+            fmt, blk = self.blocks(e, 2)
+            self.cache[key] = np.abs(O.dequantize_matrix(fmt, blk))
+        return self.cache[key]
+
+    def requant_bound(self, q, k, idx, w, hq_a, hs_a, hq_b, hs_b):
+        """Elementwise bound on |y_a - y_b| for two runs of the down +
+        combine stage that differ only in their requantized h (h~ = hs x hq
+        per 32-block): y = sum_p w_p . Wd_p . h~_p, so |y_a - y_b| <=
+        sum_p |w_p| . |Wd_p| . |h~_a,p - h~_b,p| (p over routed pairs, then
+        the shared expert per token with weight 1). Returns fp64 [q][hidden]
+        and the number of elements of h~ that differ."""
+        s = self.s
+        bound = np.zeros((q, s.hidden))
+        n_diff = 0
+        pairs = [(t * k + j, int(idx[t][j]), float(w[t][j]), t) for t in range(q) for j in range(k)]
+        if s.shared:
+            pairs += [(q * k + t, s.n_experts, 1.0, t) for t in range(q)]
+        for p, e, wp, t in pairs:
+            da = np.repeat(hs_a[p].astype(np.float64), 32) * hq_a[p].astype(np.float64)
+            db = np.repeat(hs_b[p].astype(np.float64), 32) * hq_b[p].astype(np.float64)
+            diff = np.abs(da - db)
+            if np.any(diff > 0):
+                bound[t] += abs(wp) * (self.down_abs(e) @ diff)
+                n_diff += int(np.count_nonzero(diff))
+        return bound, n_diff
+
     def expert_ffn(self, e, xq, xs, hq_override=None):
         fg, gb = self.blocks(e, 0)
         fu, ub = self.blocks(e, 1)

@@ -117,6 +117,78 @@ def test_gemv_7168_full(fmt, q):
     assert err <= TOL
 
 
+def test_gemv_7168_fp4_q2():
+    """FP4 with two columns also runs on the block-scaled matrix core (one
+    column pair): its block dots and y at the full 7168 x 7168 size."""
+    torch = need_gpu()
+    say("gemv 7168 fmt=4 q=2")
+    W, blocks = _big(4)
+    x = inputgen.activations(2, 7168, seed=1)
+    y, d, yo, do = _run(torch, 4, W, x, 2, split=True, blocks=blocks)
+    assert np.array_equal(d, do)
+    err = rel_err(y, yo)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+
+
+# exponent classes of the FP4 matrix-core dot test: products that are fp32
+# subnormals, ordinary ones, and the top of the e8m0 range
+_E_TINY = (0, 1, 2, 3, 5, 10)
+_E_NORMAL = (100, 115, 120, 124, 126, 127, 128, 130, 140, 200, 243)
+_E_HUGE = (245, 250, 252, 253, 254)
+
+
+@pytest.mark.parametrize("q", [1, 2])
+@pytest.mark.parametrize("shape", [(100, 544), (64, 512)])
+def test_fp4_matrix_core_dots_extreme_exponents(q, shape):
+    """FP4 with one or two columns runs on the block-scaled matrix core,
+    which applies each block's e8m0 exponent inside the product. Its block
+    dots must equal the oracle's exactly over the exponent range: blocks
+    whose products are fp32 subnormals (E near 0; row 0 holds only such
+    blocks), ordinary blocks, and E up to 254 with codes and activations
+    small enough that every partial product stays finite (one nonzero code
+    of magnitude 0.5 or 1, activations 0 or 1). The blocks are written as
+    canonical bytes: the encoder never emits E above 252 from fp32 weights.
+    Ragged N and K (a partial row group and a partial tile) and full tiles."""
+    torch = need_gpu()
+    N, K = shape
+    nb = K // 32
+    say(f"fp4 matrix-core dots, extreme exponents, q={q} N={N} K={K}")
+    rng = np.random.default_rng(7000 + 10 * q + N)
+    blocks = np.zeros((N, nb, 17), np.uint8)
+    cls = np.array([0 if n == 0 else b % 3 for n in range(N) for b in range(nb)]).reshape(N, nb)
+    xq = rng.integers(-127, 128, (q, K)).astype(np.int8)
+    for b in range(nb):
+        if b % 3 == 2:
+            xq[:, 32 * b:32 * b + 32] = rng.integers(0, 2, (q, 32))
+    for n in range(N):
+        for b in range(nb):
+            c = cls[n, b]
+            if c == 2:
+                codes = np.zeros(32, np.int64)
+                codes[rng.integers(32)] = rng.choice([1, 2, 9, 10])  # +-0.5, +-1 in E2M1
+                E = _E_HUGE[(n + b) % len(_E_HUGE)]
+            else:
+                codes = rng.integers(0, 16, 32)
+                table = _E_TINY if c == 0 else _E_NORMAL
+                E = table[(n + 3 * b) % len(table)]
+            blocks[n, b, :16] = O.pack_codes(4, codes)
+            blocks[n, b, 16] = E
+    dW = R.DeviceQMat.from_host(4, N, K, R.import_blocks(4, blocks))
+    xqd = torch.from_numpy(xq).cuda()
+    xsumd = torch.from_numpy(O.act_sums(xq)).cuda()
+    dots = torch.full((q, N, nb), -(2 ** 31), dtype=torch.int32, device="cuda")
+    R.debug_block_dots(dW, xqd, xsumd, q, dots)
+    _sync(torch)
+    _, do = O.gemv(4, blocks, xq, np.ones((q, nb), np.float32), want_dots=True)
+    d = dots.cpu().numpy()
+    bad = d != do
+    for c, name in enumerate(("tiny", "normal", "huge")):
+        m = np.broadcast_to(cls == c, bad.shape)
+        say(f"  {name} exponents: {int(bad[m].sum())} of {int(m.sum())} dots differ")
+    assert not bad.any()
+
+
 @pytest.mark.parametrize("fmt", GEMV_FMTS)
 def test_gemv_deterministic_and_columns_independent(fmt):
     torch = need_gpu()

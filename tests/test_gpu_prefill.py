@@ -1,19 +1,23 @@
 """GPU parity of the prefill-sized MoE layer (q > 4 tokens: fused router,
-one-workgroup stable bucketing, grouped int8-MFMA gate/up + SwiGLU +
+one-workgroup stable bucketing, grouped matrix-core gate/up + SwiGLU +
 requantization, down, combine) against the oracle, stage by stage:
 
 - the tokens' int8 activations bit-exact;
 - routing bit-exact except at near-ties;
 - bucketing = the oracle's stable bucketing of the GPU's indices, bit-exact;
-- every GPU code of h~ a valid rounding of the oracle's exact h (within half
-  a step plus fp32 noise) and the GPU's h~ scales within 1e-4 of the
-  oracle's;
+- the GPU's fp32 h (the prefill test hook keeps it) within 1e-4 of the
+  oracle's h, the GPU's h~ equal to the activation quantizer applied to the
+  GPU's h (codes and scales bit-exact), and every code a valid rounding of
+  the oracle's exact h within half a step plus 1e-4 (1 + |t|);
+- the block dots the matrix core produced for probed work items (a routed
+  expert's and the shared expert's; gate, up and down) equal to the
+  oracle's exact integer dots;
 - y within 1e-4 of the oracle fed the GPU's h~ (down, shared expert and
   combine).
 
 The small layers are checked on every token and pair; the 2048-token
-layer on every token's routing and on sampled experts and tokens (the
-oracle's FFN costs ~25 ms per (token, expert))."""
+layer on every token's routing and on sampled experts, tokens and work
+items (the oracle's FFN costs ~25 ms per (token, expert))."""
 
 import numpy as np
 import pytest
@@ -27,20 +31,49 @@ from moe_common import LayerSpec, OracleMoe, check_routing
 pytestmark = pytest.mark.gpu
 
 
-def _run(torch, spec, dev, x, k, resid=None):
+def _items(spec, gpu, q):
+    """The FFN work items the bucketing makes: (expert, first) per chunk of
+    up to 64 tokens of one expert, then the shared expert's chunks."""
+    counts = np.diff(gpu["expert_off"])
+    out = [(e, f) for e in range(spec.n_experts) for f in range(0, int(counts[e]), 64)]
+    if spec.shared:
+        out += [(spec.n_experts, f) for f in range(0, q, 64)]
+    return out
+
+
+def _run(torch, spec, dev, x, k, resid=None, probes=None):
+    """One prefill call, then the test hook: the fp32 h of every row and
+    the block dots of each probed work item (default: the first and the
+    last work item)."""
     q = x.shape[0]
     buf = R.MoeBuffers(dev, q, k)
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
     rd = None if resid is None else torch.from_numpy(np.ascontiguousarray(resid)).cuda()
     buf.run(dev, xd, resid=rd)
-    NP = q * k + q
-    hq = torch.empty((NP, spec.inter), dtype=torch.int8, device="cuda")
-    hs = torch.empty((NP, spec.inter // 32), dtype=torch.float32, device="cuda")
-    R.moe_debug_hidden(dev, q, k, buf.ws, None, hq, hs)
     torch.cuda.synchronize()
     out = {n: getattr(buf, n).cpu().numpy() for n in
            ("topk_idx", "topk_w", "pairs_sorted", "expert_off", "xq", "xs", "xsum", "y")}
-    out.update(hq=hq.cpu().numpy(), hs=hs.cpu().numpy())
+    NP = q * k + q
+    H, I = spec.hidden, spec.inter
+    if probes is None:
+        items = _items(spec, out, q)
+        probes = sorted({items[0], items[-1]})
+    h = torch.full((NP, I), float("nan"), dtype=torch.float32, device="cuda")
+    out["dots"] = {}
+    for i, (e, first) in enumerate(probes):
+        dg = torch.full((I, 64, H // 32), -(2 ** 31), dtype=torch.int32, device="cuda")
+        du = torch.full((I, 64, H // 32), -(2 ** 31), dtype=torch.int32, device="cuda")
+        dd = torch.full((H, 64, I // 32), -(2 ** 31), dtype=torch.int32, device="cuda")
+        R.moe_debug_prefill(dev, q, k, buf.xq, buf.xs, buf.topk_w, buf.pairs_sorted, buf.expert_off, buf.ws,
+                            e, first, h=h if i == 0 else None, dots_gate=dg, dots_up=du, dots_down=dd)
+        torch.cuda.synchronize()
+        out["dots"][(e, first)] = (dg.cpu().numpy(), du.cpu().numpy(), dd.cpu().numpy())
+        del dg, du, dd
+    hq = torch.empty((NP, I), dtype=torch.int8, device="cuda")
+    hs = torch.empty((NP, I // 32), dtype=torch.float32, device="cuda")
+    R.moe_debug_hidden(dev, q, k, buf.ws, None, hq, hs)
+    torch.cuda.synchronize()
+    out.update(h=h.cpu().numpy(), hq=hq.cpu().numpy(), hs=hs.cpu().numpy())
     return out
 
 
@@ -60,19 +93,53 @@ def _check_front(spec, gpu, x, k, orc):
     return near
 
 
-def _check_hidden_rows(gpu, rows, h_ref, hs_ref):
-    """GPU h~ rows against the oracle's exact h for the same rows."""
-    hq_g, hs_g = gpu["hq"][rows], gpu["hs"][rows]
-    assert rel_err(hs_g, hs_ref) <= TOL
-    s = np.repeat(hs_g.astype(np.float64), 32, axis=1)
+def _check_hidden_rows(gpu, rows, h_ref):
+    """GPU rows of h, h~ against the oracle's exact h of the same rows: h
+    within 1e-4; h~ the quantizer of the GPU's own h, bit-exact; every code
+    a valid rounding of the exact h (half a step plus 1e-4 (1 + |t|))."""
+    rows = np.asarray(rows)
+    h_g = gpu["h"][rows]
+    for i in range(len(rows)):
+        assert rel_err(h_g[i], h_ref[i]) <= TOL, rows[i]
+    qq, ss = O.quantize_act(h_g)
+    assert np.array_equal(gpu["hq"][rows], qq)
+    assert np.array_equal(gpu["hs"][rows].view(np.uint32), ss.view(np.uint32))
+    s = np.repeat(gpu["hs"][rows].astype(np.float64), 32, axis=1)
     t = np.divide(h_ref, s, out=np.zeros_like(h_ref), where=s > 0)
-    assert np.all(np.abs(t - hq_g) <= 0.5 + 1e-3 * (1 + np.abs(t)))
+    assert np.all(np.abs(t - gpu["hq"][rows]) <= 0.5 + 1e-4 * (1 + np.abs(t)))
 
 
 def _expert_h(orc, e, x_rows):
     oq, os_ = O.quantize_act(x_rows)
-    r = orc.expert_ffn(e, oq, os_)
-    return r["h"], r["hs"]
+    return orc.expert_ffn(e, oq, os_)["h"]
+
+
+def _item_rows(spec, gpu, q, k, e, first):
+    """(h / o rows, tokens) of work item (e, first)."""
+    if e == spec.n_experts:
+        tok = np.arange(first, min(first + 64, q))
+        return q * k + tok, tok
+    off, ps = gpu["expert_off"], gpu["pairs_sorted"]
+    pairs = ps[off[e] + first:min(off[e] + first + 64, off[e + 1])]
+    return pairs, pairs // k
+
+
+def _check_probe_dots(spec, orc, gpu, x, k, e, first):
+    """Block dots of one work item, gate / up / down, against the oracle's
+    exact integer dots on the same int8 inputs (down: the GPU's h~ rows)."""
+    q = x.shape[0]
+    rows, tok = _item_rows(spec, gpu, q, k, e, first)
+    n = len(rows)
+    dg, du, dd = gpu["dots"][(e, first)]
+    oq, os_ = O.quantize_act(x[tok])
+    for m, d in ((0, dg), (1, du)):
+        fmt, blk = orc.blocks(e, m)
+        _, do = O.gemv(fmt, blk, oq, os_, want_dots=True)       # [n][I][H/32]
+        assert np.array_equal(d[:, :n, :].transpose(1, 0, 2), do), (e, first, m)
+    fmt, blk = orc.blocks(e, 2)
+    _, do = O.gemv(fmt, blk, gpu["hq"][rows], gpu["hs"][rows], want_dots=True)  # [n][H][I/32]
+    assert np.array_equal(dd[:, :n, :].transpose(1, 0, 2), do), (e, first, "down")
+    say(f"  block dots of item (expert {e}, first {first}, {n} tokens) bit-exact")
 
 
 def _y_fed(spec, orc, gpu, x, k, t, resid=None):
@@ -100,16 +167,16 @@ def _y_fed(spec, orc, gpu, x, k, t, resid=None):
 def _check_all(spec, gpu, x, k, orc, resid=None):
     near = _check_front(spec, gpu, x, k, orc)
     q = x.shape[0]
-    idx, off, ps = gpu["topk_idx"], gpu["expert_off"], gpu["pairs_sorted"]
+    off, ps = gpu["expert_off"], gpu["pairs_sorted"]
     for e in range(spec.n_experts):
         pairs = ps[off[e]:off[e + 1]]
         if len(pairs) == 0:
             continue
-        h, hs = _expert_h(orc, e, x[pairs // k])
-        _check_hidden_rows(gpu, pairs, h, hs)
+        _check_hidden_rows(gpu, pairs, _expert_h(orc, e, x[pairs // k]))
     if spec.shared:
-        h, hs = _expert_h(orc, spec.n_experts, x)
-        _check_hidden_rows(gpu, np.arange(q * k, q * k + q), h, hs)
+        _check_hidden_rows(gpu, np.arange(q * k, q * k + q), _expert_h(orc, spec.n_experts, x))
+    for e, first in gpu["dots"]:
+        _check_probe_dots(spec, orc, gpu, x, k, e, first)
     y_ref = np.array([_y_fed(spec, orc, gpu, x, k, t, resid) for t in range(q)])
     err = rel_err(gpu["y"], y_ref)
     say(f"  near-ties {near}, y err (fed h~) {err:.2e}")
@@ -204,8 +271,10 @@ def test_prefill_deterministic():
 def test_prefill_full_2048_tokens_top6():
     """The prefill-sized layer: 2048 tokens, hidden 4096, 256 experts,
     intermediate 2048, top-6, shared FP4 expert. Routing and bucketing on
-    every token; h~ on three sampled experts (every token they got) and on
-    the shared expert for 16 tokens; y on 6 sampled tokens."""
+    every token; h and h~ on eight sampled experts (every token they got)
+    and on the shared expert for 64 tokens; the block dots of two work
+    items (the busiest expert's first, the shared expert's at token 1024);
+    y on 16 sampled tokens."""
     torch = need_gpu()
     say("prefill full: building 256 experts")
     spec = LayerSpec(layer=0, hidden=4096, inter=2048, n_experts=256, shared=True)
@@ -213,7 +282,12 @@ def test_prefill_full_2048_tokens_top6():
     orc = OracleMoe(spec)
     q, k = 2048, 6
     x = inputgen.tokens(0, 1000, q, spec.hidden)
-    gpu = _run(torch, spec, dev, x, k)
+    # the bucketing is checked bit-exact against the oracle's below, so the
+    # probed work items can be picked from the oracle's routing
+    ref = orc.route(x, k)
+    counts_ref = np.bincount(ref["idx"].reshape(-1), minlength=spec.n_experts)
+    busiest = int(np.argmax(counts_ref))
+    gpu = _run(torch, spec, dev, x, k, probes=[(busiest, 0), (spec.n_experts, 1024)])
     say("  checking routing")
     near = _check_front(spec, gpu, x, k, orc)
     off, ps = gpu["expert_off"], gpu["pairs_sorted"]
@@ -221,18 +295,19 @@ def test_prefill_full_2048_tokens_top6():
     say(f"  near-ties {near}; tokens per expert min {counts.min()} mean {counts.mean():.1f} max {counts.max()}")
     rng = np.random.default_rng(5)
     order = np.argsort(counts, kind="stable")
-    sample_e = sorted({int(order[-1]), int(order[len(order) // 2]), int(rng.integers(0, spec.n_experts))})
-    sample_t = sorted(rng.choice(q, 6, replace=False).tolist())
+    sample_e = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2]), busiest}
+                      | {int(e) for e in rng.choice(spec.n_experts, 5, replace=False)})
+    sample_t = sorted(rng.choice(q, 16, replace=False).tolist())
     need = set(sample_e) | {int(e) for t in sample_t for e in gpu["topk_idx"][t]} | {spec.n_experts}
     orc.prefetch(sorted(need), workers=16)
     for e in sample_e:
         pairs = ps[off[e]:off[e + 1]]
         say(f"  expert {e}: {len(pairs)} tokens")
-        h, hs = _expert_h(orc, e, x[pairs // k])
-        _check_hidden_rows(gpu, pairs, h, hs)
-    tok = np.arange(16) * 127 % q
-    h, hs = _expert_h(orc, spec.n_experts, x[tok])
-    _check_hidden_rows(gpu, q * k + tok, h, hs)
+        _check_hidden_rows(gpu, pairs, _expert_h(orc, e, x[pairs // k]))
+    tok = np.arange(1024, 1088)
+    _check_hidden_rows(gpu, q * k + tok, _expert_h(orc, spec.n_experts, x[tok]))
+    for e, first in gpu["dots"]:
+        _check_probe_dots(spec, orc, gpu, x, k, e, first)
     y_ref = np.array([_y_fed(spec, orc, gpu, x, k, t) for t in sample_t])
     err = rel_err(gpu["y"][sample_t], y_ref)
     say(f"  y err on tokens {sample_t} (fed h~): {err:.2e}")

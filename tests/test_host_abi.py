@@ -270,6 +270,36 @@ def test_moe_rejects_the_gemv_only_variant():
         assert st == -4 and b"FP3E" in L.rfx_last_error()
 
 
+def test_moe_debug_hooks_validation_without_gpu():
+    """The MoE test hooks check the workspace size against the q and k they
+    are given (and the prefill hook its q and probe) before any HIP call."""
+    L = R.lib()
+    good = 0x7f0000000000
+    f = _fake(good)
+    H, I, E = 256, 512, 4
+    z = R.QMat(0, 0, 0, 0, None)
+    lay = R.MoeLayerC(H, I, E, 0, R.QMat(2, I, H, E, good), R.QMat(2, I, H, E, good),
+                      R.QMat(3, H, I, E, good), z, z, z, good, None)
+    need = L.rfx_moe_workspace_bytes(ctypes.byref(lay), 4, 2)
+    assert need > 0
+    assert L.rfx_moe_debug_hidden(ctypes.byref(lay), 4, 2, f, need - 256, f, f, f, None) == -5
+    assert L.rfx_moe_debug_hidden(ctypes.byref(lay), 4, 3, f, need, None, f, f, None) == -5  # larger k
+    assert L.rfx_moe_debug_hidden(ctypes.byref(lay), 4, 2, None, need, None, f, f, None) == -1
+    need_p = L.rfx_moe_workspace_bytes(ctypes.byref(lay), 64, 2)
+
+    def pre(q, ws_bytes, pe, pf):
+        return L.rfx_moe_debug_prefill(ctypes.byref(lay), q, 2, f, f, f, f, f, f, ws_bytes, pe, pf,
+                                       f, f, f, f, None)
+
+    assert pre(4, need_p, 0, 0) == -1          # the decode sizes have no prefill kernels
+    assert pre(64, need_p - 256, 0, 0) == -5
+    assert pre(64, need_p, E, 0) == -1         # no shared expert in this layer
+    assert pre(64, need_p, -1, 0) == -1
+    assert pre(64, need_p, 0, 3) == -1         # a work item starts at a multiple of 64
+    assert L.rfx_moe_debug_prefill(ctypes.byref(lay), 64, 2, _fake(good + 4), f, f, f, f, f, need_p, 0, 0,
+                                   f, f, f, f, None) == -2
+
+
 def test_read_reference_validation_without_gpu():
     L = R.lib()
     good = 0x7f0000000000
