@@ -341,9 +341,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFfnWaves = 8;
 constexpr int kFfnThreads = 64 * kFfnWaves;
-constexpr int kGateRows = 16 * kFfnWaves;      // gate/up: one 16-row tile of each matrix per wave
-constexpr int kDownRT = 2;                     // down: row tiles per wave
-constexpr int kDownRows = 16 * kDownRT * kFfnWaves;
+constexpr int kGateRows = 16 * kFfnWaves;    // gate/up: one tile of gate and one of up per wave
+constexpr int kDownRows = 32 * kFfnWaves;    // down: two row tiles per wave
 
 struct FfnArgs {
     const uint8_t *gate, *up, *down; // routed stacks
@@ -406,68 +405,65 @@ constexpr uint32_t kH2 = 0x423CBCC2u;
 constexpr uint32_t kH3Lo = 0xBCC2C5C7u, kH3Hi = 0x4745423Cu;
 constexpr uint32_t kH4Lo = 0x42403C00u, kH4Hi = 0x4A484644u;
 
-// One lane's packed words of one 256-column tile: per block, the word that
-// holds its K group (FP3: the low-bit word, then the high-bit word), and
-// its row's block scales.
+// One lane's packed words of half a 256-column tile (4 blocks): per block,
+// the word that holds its K group (FP3: the low-bit word, then the
+// high-bit word), and its row's four block scales.
 template <int F>
-struct WRow {
-    uint32_t c[F == RFX_FP3 ? 16 : 8];
-    uint32_t s[F == RFX_FP4 ? 2 : 4];
+struct WHalf {
+    uint32_t c[F == RFX_FP3 ? 8 : 4];
+    uint32_t s[F == RFX_FP4 ? 1 : 2];
 };
 
-// row r (0..63) of tile `tile`, lane K group g.
+// Half hf of tile `tile`, row r (0..63), lane K group g.
 template <int F>
-__device__ __forceinline__ WRow<F> load_wrow(const uint8_t *__restrict__ tile, int r, int g)
+__device__ __forceinline__ WHalf<F> load_whalf(const uint8_t *__restrict__ tile, int r, int g, int hf)
 {
-    WRow<F> w;
+    WHalf<F> w;
     const uint8_t *rp = tile + r * 16;
 #pragma unroll
-    for (int b = 0; b < 8; b++) {
+    for (int j = 0; j < 4; j++) {
+        const int b = 4 * hf + j;
         if constexpr (F == RFX_FP4) {
-            w.c[b] = *reinterpret_cast<const uint32_t *>(rp + b * 1024 + g * 4);
+            w.c[j] = *reinterpret_cast<const uint32_t *>(rp + b * 1024 + g * 4);
         } else {
             const uint32_t lo = *reinterpret_cast<const uint32_t *>(rp + (b >> 1) * 1024 + (b & 1) * 8 + (g >> 1) * 4);
             if constexpr (F == RFX_FP3) {
-                w.c[2 * b] = lo;
-                w.c[2 * b + 1] = *reinterpret_cast<const uint32_t *>(rp + (4 + (b >> 2)) * 1024 + (b & 3) * 4);
+                w.c[2 * j] = lo;
+                w.c[2 * j + 1] = *reinterpret_cast<const uint32_t *>(rp + (4 + hf) * 1024 + j * 4);
             } else {
-                w.c[b] = lo;
+                w.c[j] = lo;
             }
         }
     }
     if constexpr (F == RFX_FP4) {
-        const u32x2 s = *reinterpret_cast<const u32x2 *>(tile + 8192 + r * 8);
-        w.s[0] = s.x;
-        w.s[1] = s.y;
+        w.s[0] = *reinterpret_cast<const uint32_t *>(tile + 8192 + r * 8 + 4 * hf);
     } else {
-        const u32x4 s = *reinterpret_cast<const u32x4 *>(rp + (F == RFX_FP3 ? 6 : 4) * 1024);
-        w.s[0] = s.x;
-        w.s[1] = s.y;
-        w.s[2] = s.z;
-        w.s[3] = s.w;
+        const u32x2 sc = *reinterpret_cast<const u32x2 *>(rp + (F == RFX_FP3 ? 6 : 4) * 1024 + 8 * hf);
+        w.s[0] = sc.x;
+        w.s[1] = sc.y;
     }
     return w;
 }
 
-// Weights 8g..8g+7 of block b as eight f16 values.
+// Weights 8g..8g+7 of block j of the half as eight f16 values.
 template <int F>
-__device__ __forceinline__ f16x8 wfrag(const WRow<F> &w, int b, int g)
+__device__ __forceinline__ f16x8 wfrag(const WHalf<F> &w, int j, int g)
 {
     uint32_t ha, hb; // f16 high bytes of weights 8g..8g+3 and 8g+4..8g+7
-    if (F == RFX_FP4) {
+    if constexpr (F == RFX_FP4) {
         // word g: weight 8g + 4i + j at bits 8j + 4i
-        const uint32_t na = w.c[b] & 0x0F0F0F0Fu, nb = (w.c[b] >> 4) & 0x0F0F0F0Fu;
+        const uint32_t na = w.c[j] & 0x0F0F0F0Fu, nb = (w.c[j] >> 4) & 0x0F0F0F0Fu;
         ha = __builtin_amdgcn_perm(kH4Hi, kH4Lo, na & 0x07070707u) | ((na << 4) & 0x80808080u);
         hb = __builtin_amdgcn_perm(kH4Hi, kH4Lo, nb & 0x07070707u) | ((nb << 4) & 0x80808080u);
     } else {
         // word g / 2: weight 16m + 4i + j at bits 8j + 2i; the K group
         // takes i = 2 (g % 2) and i + 1
-        const uint32_t word = F == RFX_FP3 ? w.c[2 * b] : w.c[b];
+        const uint32_t word = F == RFX_FP3 ? w.c[2 * j] : w.c[j];
         const uint32_t sh = 4u * (uint32_t)(g & 1);
         uint32_t sa = (word >> sh) & 0x03030303u, sb = (word >> (sh + 2u)) & 0x03030303u;
-        if (F == RFX_FP3) {
+        if constexpr (F == RFX_FP3) {
             // high bit of weight 4i + j at bit 8j + i, i = 2g and 2g + 1
-            const uint32_t h = w.c[2 * b + 1] >> (2u * (uint32_t)g);
+            const uint32_t h = w.c[2 * j + 1] >> (2u * (uint32_t)g);
             sa |= (h & 0x01010101u) << 2;
             sb |= ((h >> 1) & 0x01010101u) << 2;
             ha = __builtin_amdgcn_perm(kH3Hi, kH3Lo, sa);
@@ -482,16 +478,17 @@ __device__ __forceinline__ f16x8 wfrag(const WRow<F> &w, int b, int g)
     return __builtin_bit_cast(f16x8, v);
 }
 
-// Weight scale of block b of the lane's row.
+// Weight scale of block j of the half, for the lane's row.
 template <int F>
-__device__ __forceinline__ float wscale(const WRow<F> &w, int b)
+__device__ __forceinline__ float wscale(const WHalf<F> &w, int j)
 {
-    if (F == RFX_FP4) {
-        const uint32_t e = (w.s[b >> 2] >> (8 * (b & 3))) & 0xffu;
+    if constexpr (F == RFX_FP4) {
+        const uint32_t e = (w.s[0] >> (8 * j)) & 0xffu;
         return ldexpf(1.0f, (int)e - 128);
+    } else {
+        const uint32_t s2 = w.s[j >> 1];
+        return half_bits_to_float((j & 1) ? (s2 >> 16) : (s2 & 0xffffu));
     }
-    const uint32_t s2 = w.s[b >> 1];
-    return half_bits_to_float((b & 1) ? (s2 >> 16) : (s2 & 0xffffu));
 }
 
 // Four int8 codes -> two dwords of f16 (exact: f16 holds 1024 + u exactly
@@ -506,31 +503,45 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t x, uint32_t &p01, uint32_t 
                              __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off);
 }
 
-// LDS map (bytes): activation fragments [4 token tiles][8 blocks][64
-// lanes] x 16 B = 32 KB; slot scales [8 blocks][64 slots] fp32 2 KB; slot
-// maps 2 x 256 B. The epilogues reuse the fragment area.
-constexpr int kLdsFrag = 0, kLdsSx = 32768, kLdsRow = 34816, kLdsTok = 35072;
-constexpr int kLdsBytes = 35328;
+// LDS map (bytes): two buffers of activation fragments [4 token tiles][8
+// blocks][64 lanes] x 16 B (32 KB each) and of slot scales [8 blocks][64
+// slots] fp32 (2 KB each); slot maps 2 x 256 B. The epilogue reuses the
+// fragment area.
+constexpr int kLdsFrag = 0, kLdsSx = 65536, kLdsRow = 69632, kLdsTok = 69888;
+constexpr int kLdsBytes = 70144;
 
-// Stage K tile s of the item's activation rows (rows[src(i)], 32 int8 per
-// block, fp32 block scales) as f16 fragments. Wave w takes block w of the
-// tile, lane i the slot. Slots past n and blocks past nb are zero.
-__device__ __forceinline__ void stage_act(const int8_t *rows, const float *scales, size_t row_stride,
-                                          size_t scale_stride, const int *slot_src, int n, int s, int nb,
-                                          uint32_t *frag, float *lsx)
+// One thread's share of a K tile of the item's activation rows: slot t % 64,
+// block t / 64 (32 int8), and the block's fp32 scale. Slots past n and
+// blocks past nb are zero.
+struct ActStage {
+    u32x4 x0, x1;
+    float sx;
+};
+
+__device__ __forceinline__ ActStage act_load(const int8_t *rows, const float *scales, size_t row_stride,
+                                             size_t scale_stride, const int *slot_src, int n, int s, int nb)
 {
     const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
     const int blk = s * 8 + b;
-    u32x4 c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
-    float sx = 0.0f;
+    ActStage a;
+    a.x0 = u32x4{0u, 0u, 0u, 0u};
+    a.x1 = a.x0;
+    a.sx = 0.0f;
     if (i < n && blk < nb) {
         const int src = slot_src[i];
         const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
-        c0 = p[0];
-        c1 = p[1];
-        sx = scales[(size_t)src * scale_stride + blk];
+        a.x0 = p[0];
+        a.x1 = p[1];
+        a.sx = scales[(size_t)src * scale_stride + blk];
     }
-    const uint32_t x[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    return a;
+}
+
+// ... converted to f16 fragments (values 8g .. 8g + 7 are K group g).
+__device__ __forceinline__ void act_store(const ActStage &a, uint32_t *frag, float *lsx)
+{
+    const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
+    const uint32_t x[8] = {a.x0.x, a.x0.y, a.x0.z, a.x0.w, a.x1.x, a.x1.y, a.x1.z, a.x1.w};
     u32x4 *f = reinterpret_cast<u32x4 *>(frag) + ((i >> 4) * 8 + b) * 64 + (i & 15);
 #pragma unroll
     for (int g = 0; g < 4; g++) {
@@ -539,7 +550,7 @@ __device__ __forceinline__ void stage_act(const int8_t *rows, const float *scale
         i8x4_to_f16(x[2 * g + 1], p2, p3);
         f[16 * g] = u32x4{p0, p1, p2, p3};
     }
-    lsx[b * 64 + i] = sx;
+    lsx[b * 64 + i] = a.sx;
 }
 
 // Slot -> (h / o row, token) maps of an item, in LDS.
@@ -555,101 +566,176 @@ __device__ __forceinline__ void fill_slots(const FfnArgs &a, const Item &it, int
     }
 }
 
-// One K tile for one wave: M weight row tiles (w[m]) against the item's
-// ntt token tiles. acc[m][tt][v]: token 16 tt + 4 (l / 16) + v, row l % 16
-// of tile m. With DBG and `dots`, each block dot goes to dots[m] (rows of
-// the tile from row0[m], stride nbk blocks, 64 slots).
-template <int F, int M, bool DBG>
-__device__ __forceinline__ void ffn_tile(const WRow<F> (&w)[M], const uint32_t *frag, const float *lsx, int ntt,
-                                         int n, int s, int nb, float (&acc)[M][4][4], int32_t *const (&dots)[M],
-                                         const int (&row0)[M], int R)
+// Blocks 4 hf .. 4 hf + 3 of K tile s for one wave: its M 16-row weight
+// tiles w[m] (rows r0[m] .. + 15) against the item's NT token tiles.
+// acc[m][tt][v]: token 16 tt + 4 (l / 16) + v, row r0[m] + l % 16. The
+// token tiles run as a pipeline: tile tt's products are issued before tile
+// tt - 1's results are scaled, and tile tt + 1's operands are read from LDS
+// meanwhile. With DBG and dots[m] set, each block dot is also stored,
+// [row][slot][block].
+template <int F, int M, int NT, bool DBG>
+__device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t *frag, const float *lsx, int n,
+                                         int s, int hf, int nb, float (&acc)[M][NT][4], int32_t *const (&dots)[M],
+                                         const int (&r0)[M], int R)
 {
     const int lane = threadIdx.x & 63, g = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 *fr = reinterpret_cast<const u32x4 *>(frag) + lane;
+    const float *sxp = lsx + 4 * g;
 #pragma unroll
-    for (int b = 0; b < 8; b++) {
+    for (int j = 0; j < 4; j++) {
+        const int b = 4 * hf + j;
         if (s * 8 + b >= nb)
             break;
+        f16x8 av = __builtin_bit_cast(f16x8, fr[b * 64]);
+        f32x4 sx = *reinterpret_cast<const f32x4 *>(sxp + b * 64);
         f16x8 wv[M];
         float sw[M];
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            wv[m] = wfrag<F>(w[m], b, g);
-            sw[m] = wscale<F>(w[m], b);
+            wv[m] = wfrag<F>(w[m], j, g);
+            sw[m] = wscale<F>(w[m], j);
         }
+        f32x4 dp[M], sx_prev = sx;
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++) {
-            if (tt >= ntt)
-                break;
-            const f16x8 av = __builtin_bit_cast(f16x8, reinterpret_cast<const u32x4 *>(frag)[(tt * 8 + b) * 64 + lane]);
-            const f32x4 sx = *reinterpret_cast<const f32x4 *>(lsx + b * 64 + 16 * tt + 4 * g);
+        for (int tt = 0; tt < NT; tt++) {
+            f16x8 av_n = av;
+            f32x4 sx_n = sx;
+            if (tt + 1 < NT) {
+                av_n = __builtin_bit_cast(f16x8, fr[((tt + 1) * 8 + b) * 64]);
+                sx_n = *reinterpret_cast<const f32x4 *>(sxp + b * 64 + 16 * (tt + 1));
+            }
+            f32x4 dc[M];
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wv[m], zero, 0, 0, 0);
+            for (int m = 0; m < M; m++)
+                dc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wv[m], zero, 0, 0, 0);
+            if (tt > 0) {
 #pragma unroll
-                for (int v = 0; v < 4; v++)
-                    acc[m][tt][v] = fmaf(d[v], sw[m] * sx[v], acc[m][tt][v]);
-                if (DBG && dots[m]) {
-                    const int row = row0[m] + (lane & 15);
+                for (int m = 0; m < M; m++)
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        acc[m][tt - 1][v] = fmaf(dp[m][v], sw[m] * sx_prev[v], acc[m][tt - 1][v]);
+            }
+            if (DBG) {
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    if (!dots[m])
+                        continue;
+                    const int row = r0[m] + (lane & 15);
 #pragma unroll
                     for (int v = 0; v < 4; v++) {
                         const int slot = 16 * tt + 4 * g + v;
                         if (slot < n && row < R)
-                            dots[m][((size_t)row * 64 + slot) * nb + s * 8 + b] = (int)d[v];
+                            dots[m][((size_t)row * 64 + slot) * nb + s * 8 + b] = (int)dc[m][v];
                     }
                 }
             }
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                dp[m] = dc[m];
+            sx_prev = sx;
+            av = av_n;
+            sx = sx_n;
         }
+#pragma unroll
+        for (int m = 0; m < M; m++)
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                acc[m][NT - 1][v] = fmaf(dp[m][v], sw[m] * sx_prev[v], acc[m][NT - 1][v]);
     }
 }
 
+// The K loop of one workgroup, software-pipelined. Activations: while K
+// tile s is computed from one LDS buffer, tile s + 1's rows load into
+// staging registers and go to the other buffer after the compute (one
+// barrier per tile). Weights: half tiles in two register sets used in
+// turn, the next half loading while the current one is computed. The wave's
+// M row tiles start at r0[m] in mat[m] (a wave whose rows are past R only
+// stages activations).
+template <int F, int M, int NT, bool DBG>
+__device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const int (&r0)[M], int R, int S, int nb,
+                                         const int8_t *act, const float *act_s, size_t act_stride,
+                                         size_t act_sstride, const int *slot_src, int n, char *smem,
+                                         float (&acc)[M][NT][4], int32_t *const (&dots)[M])
+{
+    constexpr int TB = TileFmt<F>::bytes;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const bool rows_ok = r0[0] < R;
+    const uint8_t *tb[M];
+    int rin[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        tb[m] = mat[m] + (size_t)(r0[m] >> 6) * S * TB;
+        rin[m] = (r0[m] & 63) + (lane & 15);
+    }
+    WHalf<F> wa[M], wb[M];
+    if (rows_ok) {
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            wa[m] = load_whalf<F>(tb[m], rin[m], g, 0);
+    }
+    act_store(act_load(act, act_s, act_stride, act_sstride, slot_src, n, 0, nb),
+              reinterpret_cast<uint32_t *>(smem + kLdsFrag), reinterpret_cast<float *>(smem + kLdsSx));
+    __syncthreads();
+    for (int s = 0; s < S; s++) {
+        const uint32_t *frag = reinterpret_cast<const uint32_t *>(smem + kLdsFrag + (s & 1) * 32768);
+        const float *lsx = reinterpret_cast<const float *>(smem + kLdsSx + (s & 1) * 2048);
+        if (rows_ok) {
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                wb[m] = load_whalf<F>(tb[m] + (size_t)s * TB, rin[m], g, 1);
+        }
+        ActStage st{};
+        if (s + 1 < S)
+            st = act_load(act, act_s, act_stride, act_sstride, slot_src, n, s + 1, nb);
+        if (rows_ok)
+            ffn_half<F, M, NT, DBG>(wa, frag, lsx, n, s, 0, nb, acc, dots, r0, R);
+        if (rows_ok && s + 1 < S) {
+#pragma unroll
+            for (int m = 0; m < M; m++)
+                wa[m] = load_whalf<F>(tb[m] + (size_t)(s + 1) * TB, rin[m], g, 0);
+        }
+        if (rows_ok)
+            ffn_half<F, M, NT, DBG>(wb, frag, lsx, n, s, 1, nb, acc, dots, r0, R);
+        if (s + 1 < S) {
+            act_store(st, reinterpret_cast<uint32_t *>(smem + kLdsFrag + ((s + 1) & 1) * 32768),
+                      reinterpret_cast<float *>(smem + kLdsSx + ((s + 1) & 1) * 2048));
+            __syncthreads();
+        }
+    }
+    __syncthreads(); // every wave done with the fragments (the epilogue reuses them)
+}
+
 // Gate/up: one workgroup = 128 intermediate rows of gate and of up x one
-// item; wave w: row tile w of each. Epilogue: h = silu(g) * u and the
-// per-32 requantization of h (a 32-row block is two waves' tiles).
-template <int F, bool DBG>
+// item; wave w: rows 16w..16w+15 of both. Epilogue: h = silu(g) * u and
+// the per-32 requantization of h (a 32-row block is two waves' rows).
+template <int F, int NT, bool DBG>
 __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm, const uint8_t *um, char *smem)
 {
-    uint32_t *frag = reinterpret_cast<uint32_t *>(smem + kLdsFrag);
-    float *lsx = reinterpret_cast<float *>(smem + kLdsSx);
-    int *slot_row = reinterpret_cast<int *>(smem + kLdsRow);
-    int *slot_tok = reinterpret_cast<int *>(smem + kLdsTok);
+    const int *slot_row = reinterpret_cast<const int *>(smem + kLdsRow);
+    const int *slot_tok = reinterpret_cast<const int *>(smem + kLdsTok);
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r0 = blockIdx.x * kGateRows + 16 * wave; // this wave's first row
-    const int grp = r0 >> 6, rin = (r0 & 63) + (lane & 15);
+    const int rw = blockIdx.x * kGateRows + 16 * wave; // this wave's first row
     const int S = (a.H + 255) / 256, nbH = a.H / 32;
-    constexpr int TB = TileFmt<F>::bytes;
-    fill_slots(a, it, slot_row, slot_tok);
-    const int ntt = (it.n + 15) >> 4;
     const bool probe = DBG && it.expert == a.probe_expert && it.first == a.probe_first;
     int32_t *const dots[2] = {probe ? a.dots[0] : nullptr, probe ? a.dots[1] : nullptr};
-    const int row0[2] = {r0, r0};
-    float acc[2][4][4] = {};
-    const bool rows_ok = r0 < a.I; // waves past I only stage activations
-    for (int s = 0; s < S; s++) {
-        WRow<F> w[2];
-        if (rows_ok) {
-            const size_t toff = ((size_t)grp * S + s) * TB;
-            w[0] = load_wrow<F>(gm + toff, rin, g);
-            w[1] = load_wrow<F>(um + toff, rin, g);
-        }
-        __syncthreads(); // the previous tile's fragments are consumed (and the slot maps written)
-        stage_act(a.xq, a.xs, (size_t)a.H, (size_t)nbH, slot_tok, it.n, s, nbH, frag, lsx);
-        __syncthreads();
-        if (rows_ok)
-            ffn_tile<F, 2, DBG>(w, frag, lsx, ntt, it.n, s, nbH, acc, dots, row0, a.I);
-    }
-    __syncthreads();
+    const uint8_t *const mats[2] = {gm, um};
+    const int r0[2] = {rw, rw};
+    float acc[2][NT][4] = {};
+    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.I, S, nbH, a.xq, a.xs, (size_t)a.H, (size_t)nbH, slot_tok, it.n, smem, acc,
+                            dots);
+    const bool rows_ok = rw < a.I;
 
     // epilogue: h, amax over this wave's 16 rows per token, then over the
     // 32-row block (waves 2j, 2j + 1) through LDS
     float *amax_l = reinterpret_cast<float *>(smem + kLdsFrag);                   // [8 waves][64 slots]
     int8_t *hq_l = reinterpret_cast<int8_t *>(smem + kLdsFrag + kFfnWaves * 256); // [64 slots][128 rows]
-    float h[4][4], am[4][4];
+    float h[NT][4], am[NT][4];
     {
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int tt = 0; tt < NT; tt++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const float gv = acc[0][tt][v], uv = acc[1][tt][v];
@@ -663,17 +749,17 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
     }
     if (DBG && a.dbg_h && rows_ok) {
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int tt = 0; tt < NT; tt++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int i = 16 * tt + 4 * g + v;
                 if (i < it.n)
-                    a.dbg_h[(size_t)slot_row[i] * a.I + r0 + (lane & 15)] = h[tt][v];
+                    a.dbg_h[(size_t)slot_row[i] * a.I + rw + (lane & 15)] = h[tt][v];
             }
     }
     if ((lane & 15) == 0) {
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int tt = 0; tt < NT; tt++)
 #pragma unroll
             for (int v = 0; v < 4; v++)
                 amax_l[wave * 64 + 16 * tt + 4 * g + v] = am[tt][v];
@@ -682,7 +768,7 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
     {
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int tt = 0; tt < NT; tt++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int i = 16 * tt + 4 * g + v;
@@ -696,7 +782,7 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
                 }
                 hq_l[i * kGateRows + 16 * wave + (lane & 15)] = (int8_t)qv;
                 if ((wave & 1) == 0 && (lane & 15) == 0 && i < it.n && rows_ok)
-                    a.ws.hs[(size_t)slot_row[i] * (a.I / 32) + (r0 >> 5)] = sc;
+                    a.ws.hs[(size_t)slot_row[i] * (a.I / 32) + (rw >> 5)] = sc;
             }
     }
     __syncthreads();
@@ -710,6 +796,17 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
     }
 }
 
+template <int F, bool DBG>
+__device__ void gateup_dispatch(const FfnArgs &a, const Item &it, const uint8_t *gm, const uint8_t *um, char *smem)
+{
+    switch ((it.n + 15) >> 4) {
+    case 1: gateup_body<F, 1, DBG>(a, it, gm, um, smem); break;
+    case 2: gateup_body<F, 2, DBG>(a, it, gm, um, smem); break;
+    case 3: gateup_body<F, 3, DBG>(a, it, gm, um, smem); break;
+    default: gateup_body<F, 4, DBG>(a, it, gm, um, smem); break;
+    }
+}
+
 template <int FG, int FS, bool DBG>
 __global__ __launch_bounds__(kFfnThreads, 4) void prefill_gateup_kernel(FfnArgs a)
 {
@@ -718,60 +815,42 @@ __global__ __launch_bounds__(kFfnThreads, 4) void prefill_gateup_kernel(FfnArgs 
     const Item it = load_item(a, blockIdx.y, ok);
     if (!ok)
         return;
+    fill_slots(a, it, reinterpret_cast<int *>(smem + kLdsRow), reinterpret_cast<int *>(smem + kLdsTok));
+    __syncthreads();
     if (it.expert == a.E)
-        gateup_body<FS, DBG>(a, it, a.sh_gate, a.sh_up, smem);
+        gateup_dispatch<FS, DBG>(a, it, a.sh_gate, a.sh_up, smem);
     else
-        gateup_body<FG, DBG>(a, it, a.gate + a.gate_stride * (size_t)it.expert,
-                             a.up + a.up_stride * (size_t)it.expert, smem);
+        gateup_dispatch<FG, DBG>(a, it, a.gate + a.gate_stride * (size_t)it.expert,
+                                 a.up + a.up_stride * (size_t)it.expert, smem);
 }
 
-// Down: one workgroup = 256 output rows x one item; wave w: row tiles 2w,
-// 2w + 1. o[row of slot][output row] in fp32 for the combine.
-template <int F, bool DBG>
+// Down: one workgroup = 256 output rows x one item; wave w: rows
+// 32w..32w+31 (two row tiles). o[row of slot][output row] in fp32 for the
+// combine.
+template <int F, int NT, bool DBG>
 __device__ void down_body(const FfnArgs &a, const Item &it, const uint8_t *dm, char *smem)
 {
-    uint32_t *frag = reinterpret_cast<uint32_t *>(smem + kLdsFrag);
-    float *lsx = reinterpret_cast<float *>(smem + kLdsSx);
-    int *slot_row = reinterpret_cast<int *>(smem + kLdsRow);
-    int *slot_tok = reinterpret_cast<int *>(smem + kLdsTok);
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int *slot_row = reinterpret_cast<const int *>(smem + kLdsRow);
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rw = blockIdx.x * kDownRows + 32 * wave;
     const int S = (a.I + 255) / 256, nbI = a.I / 32;
-    constexpr int TB = TileFmt<F>::bytes;
-    fill_slots(a, it, slot_row, slot_tok);
-    const int ntt = (it.n + 15) >> 4;
     const bool probe = DBG && it.expert == a.probe_expert && it.first == a.probe_first;
-    int r0[kDownRT];
-    int32_t *dots[kDownRT];
-#pragma unroll
-    for (int m = 0; m < kDownRT; m++) {
-        r0[m] = blockIdx.x * kDownRows + 16 * (kDownRT * wave + m);
-        dots[m] = probe ? a.dots[2] : nullptr;
-    }
-    const bool rows_ok = r0[0] < a.H;
-    float acc[kDownRT][4][4] = {};
-    for (int s = 0; s < S; s++) {
-        WRow<F> w[kDownRT];
-        if (rows_ok) {
-#pragma unroll
-            for (int m = 0; m < kDownRT; m++)
-                w[m] = load_wrow<F>(dm + ((size_t)(r0[m] >> 6) * S + s) * TB, (r0[m] & 63) + (lane & 15), g);
-        }
-        __syncthreads();
-        stage_act(a.ws.hq, a.ws.hs, (size_t)a.I, (size_t)nbI, slot_row, it.n, s, nbI, frag, lsx);
-        __syncthreads();
-        if (rows_ok)
-            ffn_tile<F, kDownRT, DBG>(w, frag, lsx, ntt, it.n, s, nbI, acc, dots, r0, a.H);
-    }
-    if (!rows_ok)
+    int32_t *const dots[2] = {probe ? a.dots[2] : nullptr, probe ? a.dots[2] : nullptr};
+    const uint8_t *const mats[2] = {dm, dm};
+    const int r0[2] = {rw, rw + 16};
+    float acc[2][NT][4] = {};
+    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.H, S, nbI, a.ws.hq, a.ws.hs, (size_t)a.I, (size_t)nbI, slot_row, it.n, smem,
+                            acc, dots);
+    if (rw >= a.H)
         return;
 #pragma unroll
-    for (int m = 0; m < kDownRT; m++) {
+    for (int m = 0; m < 2; m++) {
         const int row = r0[m] + (lane & 15);
         if (row >= a.H)
             continue;
 #pragma unroll
-        for (int tt = 0; tt < 4; tt++)
+        for (int tt = 0; tt < NT; tt++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int i = 16 * tt + 4 * g + v;
@@ -781,18 +860,34 @@ __device__ void down_body(const FfnArgs &a, const Item &it, const uint8_t *dm, c
     }
 }
 
+template <int F, bool DBG>
+__device__ void down_dispatch(const FfnArgs &a, const Item &it, const uint8_t *dm, char *smem)
+{
+    switch ((it.n + 15) >> 4) {
+    case 1: down_body<F, 1, DBG>(a, it, dm, smem); break;
+    case 2: down_body<F, 2, DBG>(a, it, dm, smem); break;
+    case 3: down_body<F, 3, DBG>(a, it, dm, smem); break;
+    default: down_body<F, 4, DBG>(a, it, dm, smem); break;
+    }
+}
+
+// Three waves per SIMD for down (152 registers with FP3 weights, none
+// spilled), four for gate/up (128, where the wider occupancy paid more
+// than the few spilled registers cost, measured).
 template <int FD, int FSD, bool DBG>
-__global__ __launch_bounds__(kFfnThreads, 4) void prefill_down_kernel(FfnArgs a)
+__global__ __launch_bounds__(kFfnThreads, 3) void prefill_down_kernel(FfnArgs a)
 {
     __shared__ __align__(16) char smem[kLdsBytes];
     bool ok;
     const Item it = load_item(a, blockIdx.y, ok);
     if (!ok)
         return;
+    fill_slots(a, it, reinterpret_cast<int *>(smem + kLdsRow), reinterpret_cast<int *>(smem + kLdsTok));
+    __syncthreads();
     if (it.expert == a.E)
-        down_body<FSD, DBG>(a, it, a.sh_down, smem);
+        down_dispatch<FSD, DBG>(a, it, a.sh_down, smem);
     else
-        down_body<FD, DBG>(a, it, a.down + a.down_stride * (size_t)it.expert, smem);
+        down_dispatch<FD, DBG>(a, it, a.down + a.down_stride * (size_t)it.expert, smem);
 }
 
 // y[t] = resid[t] + o_shared[t] + sum_j w[t][j] o[t*k + j], slot order.
