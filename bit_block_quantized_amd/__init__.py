@@ -88,6 +88,7 @@ _SIGS = {
     "rfx_quantize_act": ([_P, _I, _I, _P, _P, _P, _P], _I),
     "rfx_gemv_workspace_bytes": ([_P, _I], _SZ),
     "rfx_gemv": ([_P, _P, _P, _P, _I, _P, _P, _SZ, _P], _I),
+    "rfx_gemv_noalloc": ([_P, _P, _P, _P, _I, _P, _P], _I),
     "rfx_gemv_q1": ([_P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_gemv_q4": ([_P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_gemv_grouped_workspace_bytes": ([_P, _I], _SZ),
@@ -253,6 +254,11 @@ def gemv(W: DeviceQMat, xq, xs, xsum, q, y, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().rfx_gemv(W.ref(), _dptr(xq), _dptr(xs), _dptr(xsum), q, _dptr(y), _dptr(ws),
                           ws_bytes, _stream(stream)))
+
+
+def gemv_noalloc(W: DeviceQMat, xq, xs, xsum, q, y, stream=None):
+    """rfx_gemv with the library's own per-GPU scratch (no workspace)."""
+    _check(lib().rfx_gemv_noalloc(W.ref(), _dptr(xq), _dptr(xs), _dptr(xsum), q, _dptr(y), _stream(stream)))
 
 
 def gemv_q1(W: DeviceQMat, xq, xs, xsum, y, ws=None, stream=None):

@@ -46,6 +46,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "rfx_decode.h"
 #include "rfx_mx4.h"
@@ -628,6 +629,62 @@ int check_act(const int8_t *xq, const float *xs, const int32_t *xsum, bool need_
     return st;
 }
 
+// ------------------------------------------------------------------
+// rfx_gemv_noalloc: rfx_gemv with its split-K exchange slots in a
+// file-scope device array instead of a caller workspace, for callers that
+// cannot allocate. The largest split choose_shape picks (row groups x
+// (P - 1) below 192, q <= 4) needs under 192 KiB of slots.
+// ------------------------------------------------------------------
+constexpr size_t kNoAllocBytes = 256u << 10;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices]; // device address of `scratch`, per device
+
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned *p, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+} // namespace
+
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends. In host code the name is only a stand-in: kernels and
+// copies take the address hipGetSymbolAddress returns for the current
+// device.
+static __device__ __align__(256) unsigned scratch[kNoAllocBytes / sizeof(unsigned)];
+
+namespace {
+
+// The current device's address of `scratch`: looked up once per device and
+// cleared then (a fill kernel on the caller's stream, ahead of the call's
+// own kernels); every completed GEMV leaves its slots zero again.
+int scratch_address(void **out, hipStream_t st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return hip_status("hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(RFX_E_UNSUPPORTED, "rfx_gemv_noalloc: device %d (at most %d devices)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(RFX_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        const size_t n = kNoAllocBytes / sizeof(unsigned);
+        hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<unsigned *>(p), n);
+        if (int rc = hip_status("rfx_gemv_noalloc scratch clear"))
+            return rc;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RFX_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -697,6 +754,27 @@ int rfx_gemv(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t
     a.y = y;
     a.slots = static_cast<unsigned *>(ws);
     return launch<false>(W->fmt, a, q, G, sh.W, (hipStream_t)stream);
+}
+
+int rfx_gemv_noalloc(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum, int q, float *y,
+                     void *stream)
+{
+    int st = check_qmat(W, "W", false);
+    if (st)
+        return st;
+    if (q < 1 || q > 4)
+        return fail(RFX_E_INVAL, "rfx_gemv_noalloc: q=%d (must be 1..4)", q);
+    if ((st = check_act(xq, xs, xsum, true)) || (st = check_ptr(y, 4, "y")))
+        return st;
+    const size_t need = rfx_gemv_workspace_bytes(W, q);
+    if (need > kNoAllocBytes)
+        return fail(RFX_E_WORKSPACE, "rfx_gemv_noalloc: this shape needs %zu bytes of scratch, more than its %zu",
+                    need, kNoAllocBytes);
+    void *ws = nullptr;
+    if (need && (st = scratch_address(&ws, (hipStream_t)stream)))
+        return st;
+    // the same launch as rfx_gemv with a workspace: same shape, same kernels
+    return rfx_gemv(W, xq, xs, xsum, q, y, ws, ws ? kNoAllocBytes : 0, stream);
 }
 
 int rfx_gemv_q1(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum, float *y,

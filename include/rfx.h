@@ -199,6 +199,21 @@ int rfx_quantize_act(const float *x, int q, int K, int8_t *xq, float *xs, int32_
 size_t rfx_gemv_workspace_bytes(const rfx_qmat *W, int q);
 int rfx_gemv(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum, int q,
              float *y, void *ws, size_t ws_bytes, void *stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): rfx_gemv
+ * with the split-K exchange slots in a 256 KiB array the library holds on
+ * each GPU it runs on (from the first call on that GPU until the process
+ * ends) instead of a workspace argument. Same arguments otherwise, same
+ * kernels, launch shape and results as rfx_gemv with a workspace. It calls
+ * no hipMalloc / hipFree; the first call on a device looks the array up and
+ * clears it with a fill kernel on `stream`, and every completed call leaves
+ * it clear. All calls on one GPU share the array: calls that can overlap
+ * on one GPU (other streams, other threads) race and must not be issued.
+ * Errors: those of rfx_gemv; RFX_E_WORKSPACE if a shape would need more
+ * than the array holds (no valid shape does: the largest split needs under
+ * 192 KiB); RFX_E_HIP if the array's address cannot be obtained. */
+int rfx_gemv_noalloc(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum, int q,
+                     float *y, void *stream);
 int rfx_gemv_q1(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum,
                 float *y, void *ws, size_t ws_bytes, void *stream);
 int rfx_gemv_q4(const rfx_qmat *W, const int8_t *xq, const float *xs, const int32_t *xsum,

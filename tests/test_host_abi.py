@@ -247,6 +247,11 @@ def test_device_entry_validation_without_gpu():
     assert L.rfx_quantize_act(_fake(good), 1, 64, _fake(good + 8), _fake(good), _fake(good), null) == -2
     assert L.rfx_debug_block_dots(ctypes.byref(W), _fake(good), _fake(good), 0, _fake(good), null) == -1
     assert b"q" in L.rfx_last_error()
+    # the no-workspace GEMV validates the same way, before looking up its scratch
+    assert L.rfx_gemv_noalloc(None, _fake(good), _fake(good), _fake(good), 1, _fake(good), null) == -1
+    assert L.rfx_gemv_noalloc(ctypes.byref(W), _fake(good), _fake(good), _fake(good), 5, _fake(good), null) == -1
+    assert L.rfx_gemv_noalloc(ctypes.byref(W), _fake(good + 1), _fake(good), _fake(good), 1, _fake(good), null) == -2
+    assert L.rfx_gemv_noalloc(ctypes.byref(stack), _fake(good), _fake(good), _fake(good), 1, _fake(good), null) == -1
 
 
 def test_moe_rejects_the_gemv_only_variant():
