@@ -64,7 +64,8 @@ class MoeLayerC(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("gate", QMat), ("up", QMat), ("down", QMat),
                 ("sh_gate", QMat), ("sh_up", QMat), ("sh_down", QMat),
-                ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p)]
+                ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("expert_data", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -342,4 +343,5 @@ def moe_debug_prefill(layer, q, k, xq, xs, topk_w, pairs_sorted, expert_off, ws,
                                        _stream(stream)))
 
 
-from .layer import DeviceMoeLayer, MoeBuffers  # noqa: E402,F401
+from .layer import DeviceMoeLayer, MoeBuffers, PlacedMoeLayer, hot_experts_by_frequency  # noqa: E402,F401
+from . import layer  # noqa: E402,F401

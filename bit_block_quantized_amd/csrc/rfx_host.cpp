@@ -45,7 +45,7 @@ int check_ptr(const void *p, size_t align, const char *what)
     return RFX_OK;
 }
 
-int check_qmat(const rfx_qmat *W, const char *what, bool allow_stack)
+int check_qmat(const rfx_qmat *W, const char *what, bool allow_stack, bool data_optional)
 {
     if (!W)
         return fail(RFX_E_INVAL, "%s descriptor is NULL", what);
@@ -56,6 +56,8 @@ int check_qmat(const rfx_qmat *W, const char *what, bool allow_stack)
                     what, W->rows, W->cols);
     if (W->count < 1 || (!allow_stack && W->count != 1))
         return fail(RFX_E_INVAL, "%s: bad count %d", what, W->count);
+    if (data_optional && !W->data)
+        return RFX_OK;
     return check_ptr(W->data, 256, what);
 }
 

@@ -36,7 +36,9 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int fail(int status, const char *fmt, ...);
 
 // Validation helpers (host only, no HIP calls).
-int check_qmat(const rfx_qmat *W, const char *what, bool allow_stack);
+// data_optional: a NULL data pointer is accepted (the MoE stacks when a
+// per-expert placement table is given).
+int check_qmat(const rfx_qmat *W, const char *what, bool allow_stack, bool data_optional = false);
 int check_ptr(const void *p, size_t align, const char *what);
 
 // Last HIP error as an RFX status (RFX_OK if none).

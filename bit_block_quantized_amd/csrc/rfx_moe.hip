@@ -450,7 +450,18 @@ struct FfnArgs {
     const float *resid; // [q][H] or null
     float *y;           // [q][H]
     MoeWs ws;
+    const void *const *expert_data; // placement table [3][E] or null
 };
+
+// Matrix m (0 gate, 1 up, 2 down) of routed expert e: from the placement
+// table when there is one, else from the stack.
+__device__ __forceinline__ const uint8_t *expert_mat(const FfnArgs &a, int m, int e)
+{
+    if (a.expert_data)
+        return static_cast<const uint8_t *>(a.expert_data[m * a.E + e]);
+    return m == 0 ? a.gate + a.gate_stride * (size_t)e
+         : m == 1 ? a.up + a.up_stride * (size_t)e : a.down + a.down_stride * (size_t)e;
+}
 
 // Column j of a slot: its h / output row index and its activation token.
 template <int NE>
@@ -572,8 +583,8 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
         gm = a.sh_gate;
         um = a.sh_up;
     } else {
-        gm = a.gate + a.gate_stride * (size_t)si.expert;
-        um = a.up + a.up_stride * (size_t)si.expert;
+        gm = expert_mat(a, 0, si.expert);
+        um = expert_mat(a, 1, si.expert);
     }
     gm += (size_t)g * S * TileFmt<FG>::bytes;
     um += (size_t)g * S * TileFmt<FU>::bytes;
@@ -644,8 +655,8 @@ __device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int 
         gm = a.sh_gate;
         um = a.sh_up;
     } else {
-        gm = a.gate + a.gate_stride * (size_t)si.expert;
-        um = a.up + a.up_stride * (size_t)si.expert;
+        gm = expert_mat(a, 0, si.expert);
+        um = expert_mat(a, 1, si.expert);
     }
     gm += (size_t)g * S * TB;
     um += (size_t)g * S * TB;
@@ -831,7 +842,7 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
         xc.moff[j] = moff[j];
     }
     const int S = (a.I + 255) / 256;
-    const uint8_t *dm = si.kind == 2 ? a.sh_down : a.down + a.down_stride * (size_t)si.expert;
+    const uint8_t *dm = si.kind == 2 ? a.sh_down : expert_mat(a, 2, si.expert);
     dm += (size_t)g * S * TileFmt<FD>::bytes;
     float ao[NE];
 #pragma unroll
@@ -879,7 +890,7 @@ __device__ void down_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int la
         xc.moff[j] = (uint32_t)cols.out_idx[j] * (uint32_t)nbI;
     }
     const int S = (a.I + 255) / 256;
-    const uint8_t *dm = si.kind == 2 ? a.sh_down : a.down + a.down_stride * (size_t)si.expert;
+    const uint8_t *dm = si.kind == 2 ? a.sh_down : expert_mat(a, 2, si.expert);
     dm += (size_t)g * S * TB;
     const MxLane<NE> ml = mx_lane<NE>(lane, xc);
     float acc[4][4];
@@ -1013,8 +1024,11 @@ int check_layer(const rfx_moe_layer *L)
     if (L->hidden < 32 || L->hidden % 32 || L->inter < 32 || L->inter % 32)
         return fail(RFX_E_INVAL, "hidden=%d inter=%d must be positive multiples of 32", L->hidden, L->inter);
     int st;
-    if ((st = check_qmat(&L->gate, "gate", true)) || (st = check_qmat(&L->up, "up", true)) ||
-        (st = check_qmat(&L->down, "down", true)))
+    const bool placed = L->expert_data != nullptr;
+    if ((st = check_qmat(&L->gate, "gate", true, placed)) || (st = check_qmat(&L->up, "up", true, placed)) ||
+        (st = check_qmat(&L->down, "down", true, placed)))
+        return st;
+    if (placed && (st = check_ptr(L->expert_data, 8, "expert_data")))
         return st;
     if (L->gate.rows != L->inter || L->gate.cols != L->hidden || L->up.rows != L->inter ||
         L->up.cols != L->hidden || L->down.rows != L->hidden || L->down.cols != L->inter)
@@ -1189,6 +1203,7 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.resid = resid;
     a.y = y;
     a.ws = w;
+    a.expert_data = L->expert_data;
     const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
     const hipStream_t s = (hipStream_t)stream;
     const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);

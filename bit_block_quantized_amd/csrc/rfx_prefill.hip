@@ -362,7 +362,18 @@ struct FfnArgs {
     float *dbg_h;
     int probe_expert, probe_first;
     int32_t *dots[3];
+    const void *const *expert_data; // placement table [3][E] or null
 };
+
+// Matrix m (0 gate, 1 up, 2 down) of routed expert e: from the placement
+// table when there is one, else from the stack.
+__device__ __forceinline__ const uint8_t *expert_mat(const FfnArgs &a, int m, int e)
+{
+    if (a.expert_data)
+        return static_cast<const uint8_t *>(a.expert_data[m * a.E + e]);
+    return m == 0 ? a.gate + a.gate_stride * (size_t)e
+         : m == 1 ? a.up + a.up_stride * (size_t)e : a.down + a.down_stride * (size_t)e;
+}
 
 struct Item {
     int expert; // E = the shared expert
@@ -820,8 +831,7 @@ __global__ __launch_bounds__(kFfnThreads, 4) void prefill_gateup_kernel(FfnArgs 
     if (it.expert == a.E)
         gateup_dispatch<FS, DBG>(a, it, a.sh_gate, a.sh_up, smem);
     else
-        gateup_dispatch<FG, DBG>(a, it, a.gate + a.gate_stride * (size_t)it.expert,
-                                 a.up + a.up_stride * (size_t)it.expert, smem);
+        gateup_dispatch<FG, DBG>(a, it, expert_mat(a, 0, it.expert), expert_mat(a, 1, it.expert), smem);
 }
 
 // Down: one workgroup = 256 output rows x one item; wave w: rows
@@ -887,7 +897,7 @@ __global__ __launch_bounds__(kFfnThreads, 3) void prefill_down_kernel(FfnArgs a)
     if (it.expert == a.E)
         down_dispatch<FSD, DBG>(a, it, a.sh_down, smem);
     else
-        down_dispatch<FD, DBG>(a, it, a.down + a.down_stride * (size_t)it.expert, smem);
+        down_dispatch<FD, DBG>(a, it, expert_mat(a, 2, it.expert), smem);
 }
 
 // y[t] = resid[t] + o_shared[t] + sum_j w[t][j] o[t*k + j], slot order.
@@ -1033,6 +1043,7 @@ int prefill_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.ws = w;
     a.probe_expert = -1;
     a.probe_first = -1;
+    a.expert_data = L->expert_data;
     const int fsg = has_shared ? L->sh_gate.fmt : L->gate.fmt;
     const int fsd = has_shared ? L->sh_down.fmt : L->down.fmt;
     const int items = prefill_max_items(q, k, L->n_experts);

@@ -91,6 +91,57 @@ class DeviceMoeLayer:
         return n
 
 
+def hot_experts_by_frequency(counts, n_hot):
+    """The n_hot experts picked most often (ties to the lower id): the
+    placement policy for a fixed budget of expert slots in HBM. counts: picks
+    per expert from a warm-up run or the router's known bias."""
+    counts = np.asarray(counts)
+    order = np.lexsort((np.arange(len(counts)), -counts))
+    return sorted(int(e) for e in order[:n_hot])
+
+
+class PlacedMoeLayer(DeviceMoeLayer):
+    """The experts of a DeviceMoeLayer placed by temperature: routed experts
+    in `hot` stay in device memory (HBM), the others move to pinned host
+    memory, which the kernels read directly over the host link; a device
+    table of per-expert pointers ([gate e][up e][down e]) tells the kernels
+    where each is (rfx_moe_layer.expert_data). The shared expert and the
+    router stay in device memory."""
+
+    def __init__(self, layer: DeviceMoeLayer, hot, device="cuda"):
+        import torch
+        E = layer.n_experts
+        self.hot = sorted(set(int(e) for e in hot))
+        hot_set = set(self.hot)
+        self.cold = [e for e in range(E) if e not in hot_set]
+        mats = (layer.gate, layer.up, layer.down)
+        table = np.zeros((3, E), np.uint64)
+        self.hot_data, self.cold_data = [], []
+        for m, qm in enumerate(mats):
+            nb = qmat_bytes(qm.fmt, qm.rows, qm.cols)
+            hot_t = torch.empty(max(1, len(self.hot)) * nb, dtype=torch.uint8, device=device)
+            cold_t = torch.empty(max(1, len(self.cold)) * nb, dtype=torch.uint8, pin_memory=True)
+            for i, e in enumerate(self.hot):
+                hot_t[i * nb:(i + 1) * nb].copy_(qm.data[e * nb:(e + 1) * nb])
+                table[m, e] = hot_t.data_ptr() + i * nb
+            for i, e in enumerate(self.cold):
+                cold_t[i * nb:(i + 1) * nb].copy_(qm.data[e * nb:(e + 1) * nb])
+                table[m, e] = cold_t.data_ptr() + i * nb
+            self.hot_data.append(hot_t)
+            self.cold_data.append(cold_t)
+        torch.cuda.synchronize()
+        self.table = torch.from_numpy(table.view(np.int64)).to(device)
+        z = [DeviceQMat(qm.fmt, qm.rows, qm.cols, None, qm.count) for qm in mats]
+        super().__init__(layer.hidden, layer.inter, E, z[0], z[1], z[2], layer.sh, layer.router_w, layer.router_b)
+        self.c.expert_data = self.table.data_ptr()
+        self.source = layer
+
+    def hbm_bytes(self):
+        """Packed routed-expert bytes held in device memory and in host memory."""
+        per = sum(qmat_bytes(qm.fmt, qm.rows, qm.cols) for qm in (self.gate, self.up, self.down))
+        return per * len(self.hot), per * len(self.cold)
+
+
 class MoeBuffers:
     """Device buffers for one MoE decode call with q tokens, top-k."""
 

@@ -287,6 +287,16 @@ typedef struct rfx_moe_layer {
     rfx_qmat sh_gate, sh_up, sh_down;
     const float *router_w; /* device fp32 [E][H] */
     const float *router_b; /* device fp32 [E], or NULL */
+    /* Expert placement (optional). NULL: routed expert e of gate / up / down
+     * is matrix e of that stack. Otherwise a device-readable table of 3 * E
+     * pointers, [gate e = 0..E-1][up e][down e], each to one expert matrix in
+     * the tiled layout (256-B aligned), which may sit in device memory or in
+     * mapped pinned host memory (hipHostMalloc): the kernels read either
+     * directly, so hot experts can stay in HBM and cold ones in host memory
+     * ([AIN] dual-GPU section: experts are independent and can be split
+     * across devices by how often they are used). The stacks then give only
+     * format, shape and count; their data may be NULL. */
+    const void *const *expert_data;
 } rfx_moe_layer;
 
 size_t rfx_moe_workspace_bytes(const rfx_moe_layer *L, int q, int k);

@@ -321,3 +321,29 @@ def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5, -6):
         assert L.rfx_status_str(st)
     assert L.rfx_status_str(-99) == b"unknown status"
+
+
+def test_hot_expert_policy():
+    """The n most picked experts, ties to the lower id."""
+    from bit_block_quantized_amd.layer import hot_experts_by_frequency
+    counts = np.array([5, 9, 9, 0, 7, 9, 1])
+    assert hot_experts_by_frequency(counts, 3) == [1, 2, 5]
+    assert hot_experts_by_frequency(counts, 4) == [1, 2, 4, 5]
+    assert hot_experts_by_frequency(counts, 0) == []
+    assert hot_experts_by_frequency(counts, 10) == list(range(7))
+
+
+def test_placement_table_validation_without_gpu():
+    """With a per-expert pointer table the routed stacks need no data
+    pointer; the table itself must be present and 8-byte aligned."""
+    L = R.lib()
+    good = 0x7f0000000000
+    f = _fake(good)
+    H, I, E = 256, 512, 4
+    z = R.QMat(0, 0, 0, 0, None)
+    lay = R.MoeLayerC(H, I, E, 0, R.QMat(2, I, H, E, None), R.QMat(2, I, H, E, None),
+                      R.QMat(3, H, I, E, None), z, z, z, good, None, None)
+    need = L.rfx_moe_workspace_bytes(ctypes.byref(lay), 1, 2)
+    assert L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, need, None) == -1  # stacks NULL, no table
+    lay.expert_data = good + 4
+    assert L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, need, None) == -2
