@@ -243,6 +243,65 @@ def bench_moe(torch, R, inputgen, layers, reps):
             "distinct_experts_per_layer": hist,
             "steps_per_s": round(1e3 / ms, 1)}
         log(f"moe stack q={q}: {ms * 1e3:.1f} us/step, {nb / (ms * 1e-3) / 1e9:.0f} GB/s")
+    f = profile_summary("moe_decode_pmc", MOE_SOURCES)
+    out["traffic"] = ({k: int(v.split()[0]) for k, v in f.items() if k.endswith("_bytes")}
+                      if f else None)
+    return out
+
+
+def bench_placement(torch, R, inputgen, layers, n_hot=64, steps=16, n_layers=2):
+    """Expert placement on one GPU: the first n_layers of the Zipf(1.1)
+    stack at q = 1, top-4, decoding `steps` fresh tokens; per layer the
+    n_hot experts the router bias ranks highest stay in HBM and the others
+    sit in pinned host memory, read by the kernels over the host link. The
+    same steps with every expert in HBM for comparison. Reports us per step,
+    the share of routed picks that hit host memory and the host bytes read
+    per step."""
+    from bit_block_quantized_amd.layer import hot_experts_by_frequency
+    sel = [lay[1] for lay in layers[:n_layers]]
+    placed = [R.PlacedMoeLayer(z, hot_experts_by_frequency(np.exp(z.router_b.cpu().numpy().astype(np.float64)),
+                                                            n_hot)) for z in sel]
+    xs = [torch.from_numpy(inputgen.tokens(100, s, 1, MOE_H)).cuda() for s in range(steps)]
+    per_expert = placed[0].hbm_bytes()[0] // max(1, len(placed[0].hot))
+
+    def measure(lays, cold_sets):
+        bufs = [R.MoeBuffers(l, 1, 4) for l in lays]
+        xb = [torch.empty((1, MOE_H), dtype=torch.float32, device="cuda") for _ in lays]
+
+        def step(s):
+            x = xs[s]
+            for l, lay in enumerate(lays):
+                bufs[l].run(lay, x, resid=x, out=xb[l])
+                x = xb[l]
+
+        cold = picks = 0
+        for s in range(steps):
+            step(s)
+            torch.cuda.synchronize()
+            for l in range(len(lays)):
+                idx = bufs[l].topk_idx.cpu().numpy().reshape(-1)
+                picks += idx.size
+                cold += int(np.isin(idx, cold_sets[l]).sum())
+        g = graph_of(torch, step, steps)
+        ms = time_graph(torch, g, 3) / steps
+        del g
+        return ms, cold, picks
+
+    ms_hbm, _, _ = measure(sel, [[] for _ in sel])
+    ms_pl, cold, picks = measure(placed, [p.cold for p in placed])
+    hb, cb = placed[0].hbm_bytes()
+    host_bytes = cold * per_expert / steps
+    out = {"workload": f"first {n_layers} layers of the Zipf(1.1) stack, q=1, top-4, {steps} fresh tokens; "
+                       f"{n_hot} of {MOE_E} routed experts per layer in HBM, the rest in pinned host memory",
+           "us_per_step_all_hbm": round(ms_hbm * 1e3, 2), "us_per_step_placed": round(ms_pl * 1e3, 2),
+           "cold_pick_share": round(cold / max(1, picks), 4),
+           "hbm_GiB_per_layer": round(hb / 2**30, 2), "host_GiB_per_layer": round(cb / 2**30, 2),
+           "host_bytes_per_step": int(host_bytes),
+           "host_link_GBps": round(host_bytes / max(1e-9, (ms_pl - ms_hbm) * 1e-3) / 1e9, 1) if ms_pl > ms_hbm
+           else None}
+    del placed
+    torch.cuda.empty_cache()
+    log(f"placement: {out}")
     return out
 
 
@@ -267,7 +326,13 @@ def bench_prefill(torch, R, inputgen, layer, reps, tokens=2048, k=6):
     wbytes = layer.weight_bytes(idx.reshape(-1).tolist())
     counts = np.bincount(idx.reshape(-1), minlength=MOE_E)
     log(f"prefill {tokens} tokens top-{k}: {ms * 1e3:.1f} us, {2 * macs / (ms * 1e-3) / 1e12:.1f} int8 TOP/s")
-    return {"us": round(ms * 1e3, 1), "tokens": tokens, "k": k,
+    counters = {}
+    f = profile_summary("moe_prefill_2048_pmc", PREFILL_SOURCES)
+    if f:
+        for key in ("MfmaUtil_pct", "VALUBusy_pct", "gateup_read_bytes", "down_read_bytes", "traffic_bytes_per_layer"):
+            if key in f:
+                counters[key] = float(f[key].split()[0])
+    return {"counters": counters or None, "us": round(ms * 1e3, 1), "tokens": tokens, "k": k,
             "tokens_per_s": round(tokens / (ms * 1e-3), 1),
             "int8_ops": 2 * macs, "int8_TOPs": round(2 * macs / (ms * 1e-3) / 1e12, 2),
             "frac_int8_mfma_peak": round(2 * macs / (ms * 1e-3) / 5.0e15, 4),
@@ -372,25 +437,206 @@ def bench_config1(torch, R, inputgen, reps):
             "bytes_per_call": w + a}
 
 
-def cpu_baseline(R, work, rows=N, repeats=8):
-    """The CPU oracle on a bounded sample: the first `rows` rows of every
-    matrix, all six (format, q) products, `repeats` times, one thread."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(R, work, rows=N, repeats=4):
+    """The CPU oracle as it stands on a bounded sample: every row of each
+    7168 x 7168 matrix, all six (format, q) products, `repeats` times; once
+    on one thread and once over all host threads (the rows split into one
+    contiguous chunk per thread, each chunk one call of the unchanged oracle
+    GEMV; ctypes releases the GIL). Reported in GB/s of the same algorithmic
+    bytes as the GPU step."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import inputgen
     import oracle as O
     blocks = {fmt: O.quantize_matrix(fmt, work[fmt]["W"][:rows]) for fmt in FORMATS}
     xq = {q: O.quantize_act(inputgen.activations(q, K, seed=1)) for q in (1, 4)}
-    t0 = time.perf_counter()
-    nbytes = 0
-    for _ in range(repeats):
-        for fmt in FORMATS:
-            for q in (1, 4):
-                O.gemv(fmt, blocks[fmt], xq[q][0], xq[q][1])
-                w, a, _ = algorithmic_bytes(R, fmt, q, n=rows)
-                nbytes += w + a
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of each 7168x7168 matrix, FP2/FP3/FP4 x q=1,4, "
-                      f"{repeats} repeats, one thread, {dt:.1f} s"}
+    nbytes = repeats * sum(sum(algorithmic_bytes(R, fmt, q, n=rows)[:2]) for fmt in FORMATS for q in (1, 4))
+
+    def run(threads):
+        chunks = [(r * rows // threads, (r + 1) * rows // threads) for r in range(threads)]
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            for _ in range(repeats):
+                for fmt in FORMATS:
+                    for q in (1, 4):
+                        list(ex.map(lambda c: O.gemv(fmt, blocks[fmt][c[0]:c[1]], xq[q][0], xq[q][1]), chunks))
+        return time.perf_counter() - t0
+
+    dt1 = run(1)
+    nth = host_threads()
+    dtn = run(nth)
+    return {"value": round(nbytes / dtn / 1e9, 4), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of each 7168x7168 matrix, FP2/FP3/FP4 x q=1,4, {repeats} repeats, "
+                      f"{nth} threads over row chunks, {dtn:.1f} s",
+            "single_thread": {"value": round(nbytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(dt1, 1)},
+            "cpu_model": cpu_model()}
+
+
+def cpu_moe_layer(R, inputgen, layer=0, q=4, k=6):
+    """The oracle's MoE layer (routing, every pair's and the shared expert's
+    FFN in fp64, combine) for the q = 4, top-6 decode workload of `layer`,
+    on one thread and over all host threads (one task per (token, expert)
+    pair). The experts the tokens pick are encoded by the oracle first,
+    outside the timed region."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle as O
+    x = inputgen.tokens(layer, 7, q, MOE_H)
+    wr = inputgen.router_weight(layer, MOE_E, MOE_H)
+    ref = O.route(x, wr, None, k)
+    idx, w = ref["idx"], ref["w"]
+    experts = sorted(set(idx.reshape(-1).tolist())) + [MOE_E]
+    nth = host_threads()
+    mats = {}
+
+    def enc(em):
+        e, m = em
+        rows, cols = (MOE_I, MOE_H) if m < 2 else (MOE_H, MOE_I)
+        fmt = 4 if e == MOE_E else (2 if m < 2 else 3)
+        return em, (fmt, O.quantize_matrix(fmt, inputgen.expert_weight(layer, e, m, rows, cols)))
+
+    with ThreadPoolExecutor(nth) as ex:
+        mats.update(ex.map(enc, [(e, m) for e in experts for m in range(3)]))
+    xq, xs = O.quantize_act(x)
+    jobs = [(t, int(idx[t][j])) for t in range(q) for j in range(k)] + [(t, MOE_E) for t in range(q)]
+
+    def ffn(job):
+        t, e = job
+        (fg, gb), (fu, ub), (fd, db) = mats[(e, 0)], mats[(e, 1)], mats[(e, 2)]
+        return O.ffn(fg, gb, fu, ub, fd, db, xq[t:t + 1], xs[t:t + 1])["o"][0]
+
+    def layer_once(threads):
+        t0 = time.perf_counter()
+        O.route(x, wr, None, k)
+        with ThreadPoolExecutor(threads) as ex:
+            o = list(ex.map(ffn, jobs))
+        o_pairs = np.array(o[:q * k]).reshape(q, k, MOE_H)
+        O.combine(np.array(o[q * k:]), o_pairs, w)
+        return time.perf_counter() - t0
+
+    t1 = layer_once(1)
+    tn = layer_once(nth)
+    wbytes = sum(R.qmat_bytes(mats[(e, m)][0], *((MOE_I, MOE_H) if m < 2 else (MOE_H, MOE_I)))
+                 for e in experts for m in range(3)) + MOE_E * MOE_H * 4
+    return {"workload": f"one MoE decode layer, q={q}, top-{k}, 256 experts (layer {layer}), "
+                        f"{len(experts) - 1} distinct experts + shared",
+            "seconds_1_thread": round(t1, 3), "seconds_all_threads": round(tn, 3), "threads": nth,
+            "GBps_all_threads": round(wbytes / tn / 1e9, 4)}
+
+
+def profile_summary(name, sources):
+    """Fields of a committed rocprofv3 summary (profiles/<name>.txt), or
+    None when it is missing or the listed kernel sources changed since it
+    was taken (its kernel_sources_sha256 no longer matches)."""
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != sources_sha256(sources):
+        return None
+    return fields
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(names):
+        with open(os.path.join(ROOT, "bit_block_quantized_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+MOE_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_ws.h", "rfx_mx4.h",
+               "rfx_xtile.h")
+PREFILL_SOURCES = ("rfx_decode.h", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_ws.h", "rfx_prefill.hip")
+
+
+def profile_only(args, torch, R, inputgen):
+    """--only moe / prefill: the workload launched eagerly a few times, for
+    a profiler (no graphs, no timing of record)."""
+    if args.only == "prefill":
+        layers = build_moe_layers(torch, R, inputgen, 1)
+        layer = layers[0][0]
+        buf = R.MoeBuffers(layer, 2048, 6)
+        x = torch.from_numpy(inputgen.tokens(0, 1000, 2048, MOE_H)).cuda()
+        n = max(1, args.steps)
+        ms = time_eager(torch, lambda i: buf.run(layer, x), n)
+        out = {"only": "prefill", "layers_run": n + 10, "us": round(ms * 1e3, 1)}
+    else:
+        layers = build_moe_layers(torch, R, inputgen, max(1, args.moe_layers))
+        q, k = 4, 6
+        bufs = [R.MoeBuffers(lay[0], q, k) for lay in layers]
+        xs = [torch.from_numpy(inputgen.tokens(l, 7, q, MOE_H)).cuda() for l in range(len(layers))]
+        n = max(1, args.steps) * len(layers)
+        ms4 = time_eager(torch, lambda i: bufs[i % len(layers)].run(layers[i % len(layers)][0], xs[i % len(layers)]),
+                         n)
+        sb = [R.MoeBuffers(lay[1], 1, 4) for lay in layers]
+        x0 = torch.from_numpy(inputgen.tokens(100, 0, 1, MOE_H)).cuda()
+        xbuf = [x0] + [torch.empty((1, MOE_H), dtype=torch.float32, device="cuda") for _ in layers]
+
+        def step(i):
+            for l, lay in enumerate(layers):
+                sb[l].run(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
+
+        ms1 = time_eager(torch, step, max(1, args.steps))
+        out = {"only": "moe", "layer_q4_top6_us": round(ms4 * 1e3, 1), "stack_q1_us_per_step": round(ms1 * 1e3, 1),
+               "layers": len(layers)}
+    if args.copy_ref_mib:
+        nb = args.copy_ref_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_ref_bytes"] = nb
+    print(json.dumps(out), flush=True)
+
+
+def per_config(out):
+    """Each workload's fraction of the 8 TB/s peak (the target is judged per
+    workload), in one place."""
+    pc = {}
+    if "config1" in out:
+        c1 = out["config1"]
+        pc["config1_fp4_1024_q1"] = {"us_per_call": c1["us_per_call"],
+                                     "rotated_GBps": c1["rotated_1024_copies"]["GBps"],
+                                     "note": "0.56 MB stays in L2: launch-latency-bound"}
+    pk = {f"{p['fmt']}_q{p['q']}": p["frac_hbm"] for p in out.get("per_kernel", []) if p["fmt"] in ("FP2", "FP3", "FP4")}
+    pc["config2_gemv_7168"] = {"grouped_step_frac": out["frac_hbm_peak"], "single_launch_frac": pk}
+    if "moe" in out:
+        m = out["moe"]
+        pc["config3_moe_layer_q4_top6_frac"] = m["layer_q4_top6"]["frac_hbm"]
+        pc["config4_stack8_frac"] = {"q1": m["stack8_q1_top4_zipf"]["frac_hbm"],
+                                     "q4": m["stack8_q4_top4_zipf"]["frac_hbm"]}
+    if "prefill" in out:
+        p = out["prefill"]
+        pc["config5_prefill"] = {"us": p["us"], "frac_hbm": round(p["weight_GBps"] / HBM_PEAK_GBPS, 4),
+                                 "mfma_util_pct": (p.get("counters") or {}).get("MfmaUtil_pct")}
+    return pc
 
 
 def main():
@@ -405,12 +651,14 @@ def main():
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="with --only: then run 3 plain device copies of this many MiB (counter scaling)")
     ap.add_argument("--only", default=None,
-                    help="fmt,q (or 'grouped': the grouped step): launch only this, eagerly, "
-                         "--steps x copies times (profiling)")
+                    help="fmt,q | grouped | moe | prefill: launch only this, eagerly, for a profiler")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the decode path has no multi-GPU part); "
               "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        print("bench.py: --steps must be at least 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -420,6 +668,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     R.lib()
+    if args.only in ("moe", "prefill"):
+        profile_only(args, torch, R, inputgen)
+        return
     if args.moe_only:
         layers = build_moe_layers(torch, R, inputgen, max(1, args.moe_layers))
         print(json.dumps({"moe": bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5)),
@@ -472,8 +723,7 @@ def main():
             del g
 
     # whole step: the six GEMVs as one grouped launch (the headline) and,
-    # for comparison, as six launches back to back; one graph holds `rot`
-    # steps
+    # for comparison, as six launches back to back
     assert step_bytes == sum(p["weight_bytes"] + p["act_bytes"] for p in per if p["fmt"] in ("FP2", "FP3", "FP4"))
     rot = len(garrs)
 
@@ -485,11 +735,13 @@ def main():
     g = graph_of(torch, step_six, rot)
     ms_six = time_graph(torch, g, max(1, -(-args.steps // rot))) / rot
     del g
-    g = graph_of(torch, lambda i: R.gemv_grouped(garrs[i], gws), rot)
+    # the timed region: exactly --steps steps (step i: rotation i mod R),
+    # one graph of that many grouped launches, replayed --warmup times
+    # untimed first
+    g = graph_of(torch, lambda i: R.gemv_grouped(garrs[i % rot], gws), args.steps)
     for _ in range(args.warmup):
         g.replay()
-    reps = max(1, -(-args.steps // rot))
-    ms = time_graph(torch, g, reps) / rot
+    ms = time_graph(torch, g, 1) / args.steps
     value = step_bytes / (ms * 1e-3) / 1e9
     del g
     log(f"step: grouped {ms * 1e3:.2f} us ({value:.0f} GB/s), six launches {ms_six * 1e3:.2f} us")
@@ -500,7 +752,7 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": reps * rot,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -508,18 +760,19 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "dense GEMV 7168x7168, FP2/FP3/FP4 x q=1,4 per step, rotated copies",
+        "config": {"workload": "dense GEMV 7168x7168: six independent GEMVs (FP2/FP3/FP4 x q=1,4) in one grouped "
+                               "launch per step, rotated weight copies",
                    "rows": N, "cols": K, "formats": ["FP2", "FP3", "FP4"], "q": [1, 4],
                    "copies": {FMT_NAME[f]: len(work[f]["mats"]) for f in FORMATS},
-                   "timing": "HIP graph replay, one grouped launch per step"},
+                   "timing": "one HIP graph of --steps grouped launches after --warmup untimed replays"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gemv_grouped_kernel (FP2/FP3/FP4 x q=1,4, 7168x7168)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("grouped"),
-                     "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy "
-                                     "(read 1.009 x the algorithmic bytes): "
-                                     "profiles/gemv_grouped_7168_pmc.txt",
+                     "traffic_note": "FETCH_SIZE+WRITE_SIZE per launch, scaled by a 256 MiB copy: "
+                                     "profiles/gemv_grouped_7168_pmc.txt (null when the kernel sources changed "
+                                     "since the counters were taken)",
                      "bytes_per_launch": step_bytes,
                      "avg_launch_us": round(ms * 1e3, 3)},
         "step_six_launches": {"us": round(ms_six * 1e3, 3),
@@ -538,6 +791,7 @@ def main():
     if args.moe_layers > 0:
         layers = build_moe_layers(torch, R, inputgen, args.moe_layers)
         out["moe"] = bench_moe(torch, R, inputgen, layers, reps=max(5, args.steps // 5))
+        out["moe"]["placement"] = bench_placement(torch, R, inputgen, layers)
         out["prefill"] = bench_prefill(torch, R, inputgen, layers[0][0], reps=5)
         del layers
         torch.cuda.empty_cache()
@@ -546,10 +800,13 @@ def main():
         out["hbm_read_GBps"] = round(hbm_read_reference(torch, R), 1)
     except Exception as e:  # pragma: no cover
         out["hbm_copy_GBps"] = f"failed: {e}"
+    out["per_config"] = per_config(out)
     if not args.no_cpu_baseline:
         import inputgen as ig
         wk = {f: {"W": ig.dense_weight(N, K, seed=SEEDS[f], outliers=True)} for f in FORMATS}
         out["cpu_baseline"] = cpu_baseline(R, wk)
+        if args.moe_layers > 0:
+            out["cpu_baseline"]["moe_layer"] = cpu_moe_layer(R, ig)
     print(json.dumps(out), flush=True)
 
 
