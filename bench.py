@@ -243,6 +243,28 @@ def bench_moe(torch, R, inputgen, layers, reps):
             "distinct_experts_per_layer": hist,
             "steps_per_s": round(1e3 / ms, 1)}
         log(f"moe stack q={q}: {ms * 1e3:.1f} us/step, {nb / (ms * 1e-3) / 1e9:.0f} GB/s")
+    # the same workloads through the single-launch layer kernel
+    # (rfx_moe_forward with RFX_FORWARD_ONE_LAUNCH): same results, timed
+    # beside the three launches
+    one = {}
+    for q, k, zipf in ((1, 4, True), (4, 4, True), (4, 6, False)):
+        sel = [lay[1] if zipf else lay[0] for lay in layers]
+        fb = [R.MoeBuffers(d, q, k) for d in sel]
+        x0 = torch.from_numpy(inputgen.tokens(100, 0, q, MOE_H) if zipf else inputgen.tokens(0, 7, q, MOE_H)).cuda()
+        xb = [x0] + [torch.empty((q, MOE_H), dtype=torch.float32, device="cuda") for _ in sel]
+
+        def fwd_step(i, sel=sel, fb=fb, xb=xb, zipf=zipf):
+            for l, d in enumerate(sel):
+                fb[l].forward(d, xb[l], resid=xb[l] if zipf else None, out=xb[l + 1], one_launch=True)
+
+        fwd_step(0)
+        torch.cuda.synchronize()
+        ms = time_graph(torch, graph_of(torch, fwd_step, 1), reps) / len(sel)
+        for l, d in enumerate(sel):
+            R.moe_forward_status(d, q, k, fb[l].ws)
+        one[f"q{q}_top{k}{'_zipf' if zipf else ''}_us_per_layer"] = round(ms * 1e3, 2)
+        log(f"moe one launch q={q} top-{k}: {ms * 1e3:.1f} us per layer")
+    out["one_launch"] = one
     f = profile_summary("moe_decode_pmc", MOE_SOURCES)
     out["traffic"] = ({k: int(v.split()[0]) for k, v in f.items() if k.endswith("_bytes")}
                       if f else None)

@@ -32,8 +32,9 @@ FP3E = 13
 VARIANT_FORMATS = (FP2M, Q8, FP2S, FP3E)
 
 RFX_OK = 0
+RFX_E_TIMEOUT = -7
 _STATUS = {-1: "RFX_E_INVAL", -2: "RFX_E_ALIGN", -3: "RFX_E_RANGE", -4: "RFX_E_UNSUPPORTED",
-           -5: "RFX_E_WORKSPACE", -6: "RFX_E_HIP"}
+           -5: "RFX_E_WORKSPACE", -6: "RFX_E_HIP", -7: "RFX_E_TIMEOUT"}
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBPATH = os.path.join(HERE, "librfx.so")
@@ -99,6 +100,9 @@ _SIGS = {
     "rfx_moe_workspace_bytes": ([_P, _I, _I], _SZ),
     "rfx_moe_route_topk": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "rfx_moe_ffn": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "rfx_moe_forward": ([_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, ctypes.c_uint, _P], _I),
+    "rfx_moe_forward_single_launch": ([_P, _I, _I], _I),
+    "rfx_moe_forward_status": ([_P, _I, _I, _P, _SZ, _P], _I),
     "rfx_moe_debug_hidden": ([_P, _I, _I, _P, _SZ, _P, _P, _P, _P], _I),
     "rfx_moe_debug_prefill": ([_P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _P, _P, _P, _P, _P], _I),
 }
@@ -128,6 +132,12 @@ def _check(st: int):
     if st != RFX_OK:
         raise RfxError(st, lib().rfx_last_error().decode())
     return st
+
+
+def _check_nonneg(v: int):
+    if v < 0:
+        raise RfxError(v, lib().rfx_last_error().decode())
+    return v
 
 
 def _np_ptr(a: np.ndarray):
@@ -326,6 +336,30 @@ def moe_ffn(layer, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_of
     _check(lib().rfx_moe_ffn(layer.ref(), q, k, _dptr(xq), _dptr(xs), _dptr(xsum), _dptr(topk_idx),
                              _dptr(topk_w), _dptr(pairs_sorted), _dptr(expert_off), _dptr(resid),
                              _dptr(y), _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+FORWARD_ONE_LAUNCH = 1
+
+
+def moe_forward(layer, x, q, k, y, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, ws,
+                resid=None, one_launch=False, stream=None):
+    """moe_route_topk then moe_ffn in one call; one_launch: the single-launch
+    layer kernel where moe_forward_single_launch says it can take the call."""
+    _check(lib().rfx_moe_forward(layer.ref(), _dptr(x), q, k, _dptr(resid), _dptr(y), _dptr(topk_idx),
+                                 _dptr(topk_w), _dptr(pairs_sorted), _dptr(expert_off), _dptr(xq), _dptr(xs),
+                                 _dptr(xsum), _dptr(ws), ws.numel() * ws.element_size(),
+                                 FORWARD_ONE_LAUNCH if one_launch else 0, _stream(stream)))
+
+
+def moe_forward_single_launch(layer, q: int, k: int) -> bool:
+    return bool(_check_nonneg(lib().rfx_moe_forward_single_launch(layer.ref(), q, k)))
+
+
+def moe_forward_status(layer, q, k, ws, stream=None):
+    """Raises RfxError(RFX_E_TIMEOUT) if a bounded wait of the one-launch
+    layer kernel ran out since the last check (synchronizes the stream)."""
+    _check(lib().rfx_moe_forward_status(layer.ref(), q, k, _dptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)))
 
 
 def moe_debug_hidden(layer, q, k, ws, h=None, hq=None, hs=None, stream=None):

@@ -77,6 +77,7 @@ const char *rfx_status_str(int st)
     case RFX_E_UNSUPPORTED: return "unsupported";
     case RFX_E_WORKSPACE: return "workspace missing or too small";
     case RFX_E_HIP: return "HIP runtime error";
+    case RFX_E_TIMEOUT: return "a bounded device-side wait ran out";
     }
     return "unknown status";
 }

@@ -22,6 +22,22 @@ constexpr int kRouteGroup = 16;
 constexpr int kRouteMaxGroups = kMaxE / kRouteGroup;
 constexpr int kRouteCntStride = 32; // 32-bit words between counters
 
+// Counters of the single-launch decode layer kernel (rfx_moe_layer.hip),
+// each on its own 128-byte line: activation quantization done, abort (a
+// bounded wait ran out), the sticky timeout word, the exit count over the
+// groups; then per slot the gate/up row groups done (h~ of the slot
+// complete) and the slot's routing word (published bit, token count,
+// expert, pair ids); then the exit count per group of kExitGroup
+// workgroups.
+constexpr int kSyncLine = 32; // 32-bit words per counter line
+constexpr int kSyncXq = 0, kSyncAbort = 1, kSyncErr = 2, kSyncExitTop = 3, kSyncH = 4;
+constexpr int kMaxSlots = kMaxDecodeQ * kMaxK + 1;
+constexpr int kSyncSlot = kSyncH + kMaxSlots;
+constexpr int kSyncExit = kSyncSlot + kMaxSlots;
+constexpr int kExitGroup = 64;
+constexpr int kMaxExitGroups = 128; // at most 8192 workgroups per launch
+constexpr int kSyncWords = (kSyncExit + kMaxExitGroups) * kSyncLine;
+
 // Work items of the prefill FFN: (expert, first token) per chunk of up to
 // kPrefillChunk tokens of one expert, then the shared expert's chunks.
 inline int prefill_max_items(int q, int k, int E)
@@ -43,6 +59,7 @@ struct MoeWs {
     float *o;           // [NP][H]
     unsigned *comb_cnt; // [H/64 + 1]
     int32_t *items;     // [0] = count, then (expert, first token) pairs (prefill)
+    unsigned *sync;     // [kSyncWords] counters of the single-launch decode kernel
     size_t bytes;
 };
 
@@ -67,6 +84,7 @@ inline MoeWs carve(void *base, int q, int k, int E, int H, int I)
     const size_t o_o = take(NP * H * 4);
     const size_t o_cc = take((size_t)(H / 64 + 1) * 4);
     const size_t o_it = take((size_t)(1 + 2 * prefill_max_items(q, k, E)) * 4);
+    const size_t o_sy = take((size_t)kSyncWords * 4);
     w.bytes = off;
     char *b = static_cast<char *>(base);
     if (b) {
@@ -79,6 +97,7 @@ inline MoeWs carve(void *base, int q, int k, int E, int H, int I)
         w.o = reinterpret_cast<float *>(b + o_o);
         w.comb_cnt = reinterpret_cast<unsigned *>(b + o_cc);
         w.items = reinterpret_cast<int32_t *>(b + o_it);
+        w.sync = reinterpret_cast<unsigned *>(b + o_sy);
     }
     return w;
 }

@@ -46,7 +46,8 @@ enum {
     RFX_E_RANGE = -3,      /* non-finite weight, or fp16 scale overflow */
     RFX_E_UNSUPPORTED = -4,/* valid request this build does not implement */
     RFX_E_WORKSPACE = -5,  /* workspace missing or too small */
-    RFX_E_HIP = -6         /* a HIP runtime call or launch failed */
+    RFX_E_HIP = -6,        /* a HIP runtime call or launch failed */
+    RFX_E_TIMEOUT = -7     /* a bounded device-side wait ran out (rfx_moe_forward_status) */
 };
 
 /* Block formats. A block is 32 consecutive weights of one row along the
@@ -339,6 +340,41 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
                 const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid,
                 float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* The whole layer, rfx_moe_route_topk then rfx_moe_ffn, in one call with
+ * the same arguments, outputs and results (bit for bit). flags = 0: the
+ * two calls (three kernel launches). flags = RFX_FORWARD_ONE_LAUNCH: for
+ * q <= 4 with routed gate/up in RFX_FP2, down in RFX_FP3 and the shared
+ * expert (if any) in RFX_FP4 ([HM] para 2 and [KK] ROCmFPX section), one
+ * kernel launch ([HM] para 3: several positions verified in one fused
+ * pass; [KK] DSpark section: the decode step as one fused graph):
+ * workgroups with the token-quantization, router, gate/up and down roles
+ * run together, the shared expert's gate/up streams while the router
+ * runs, the router publishes one word per expert slot, and each down
+ * workgroup fetches its weights before its slot's h~ is complete; they
+ * synchronize through counters in ws with time-bounded waits. It is not
+ * faster than the three launches on MI355X at these sizes (both are bound
+ * by the same chain of dependent memory round trips), so it is not the
+ * default. Other formats and q > 4 take the two calls either way;
+ * rfx_moe_forward_single_launch(L, q, k) says whether the one-launch kernel
+ * can take a call (1 / 0; < 0: a bad layer). x fp32 [q][H], 16-B aligned;
+ * resid fp32 [q][H] or NULL, and may be x itself; y must alias none of x,
+ * resid and ws. ws: rfx_moe_workspace_bytes(L, q, k) bytes, zero-filled
+ * before its first use (the counters return to zero at the end of every
+ * call); calls that share a ws must not overlap. Errors: those of the two
+ * calls; RFX_E_INVAL for unknown flags. */
+#define RFX_FORWARD_ONE_LAUNCH 1u
+int rfx_moe_forward(const rfx_moe_layer *L, const float *x, int q, int k, const float *resid, float *y,
+                    int32_t *topk_idx, float *topk_w, int32_t *pairs_sorted, int32_t *expert_off,
+                    int8_t *xq, float *xs, int32_t *xsum, void *ws, size_t ws_bytes, unsigned flags,
+                    void *stream);
+int rfx_moe_forward_single_launch(const rfx_moe_layer *L, int q, int k);
+
+/* After rfx_moe_forward calls on ws (synchronizes the stream): RFX_OK, or
+ * RFX_E_TIMEOUT if a wait of the one-launch kernel ran out of its time
+ * bound since the last status call (the outputs of that call are
+ * undefined; the word is cleared). */
+int rfx_moe_forward_status(const rfx_moe_layer *L, int q, int k, void *ws, size_t ws_bytes, void *stream);
 
 /* Test hook: after rfx_moe_ffn with the same workspace (ws_bytes as given
  * to it; RFX_E_WORKSPACE when smaller than rfx_moe_workspace_bytes(L, q,

@@ -305,6 +305,53 @@ def test_moe_debug_hooks_validation_without_gpu():
                                    f, f, f, f, None) == -2
 
 
+def test_moe_forward_validation_without_gpu():
+    """rfx_moe_forward checks what both of its calls check before any HIP
+    call; rfx_moe_forward_single_launch is host logic: one launch for q <= 4
+    with FP2 gate/up, FP3 down and an FP4 shared expert (or none), two calls
+    otherwise."""
+    L = R.lib()
+    good = 0x7f0000000000
+    f = _fake(good)
+    H, I, E = 512, 256, 16
+    z = R.QMat(0, 0, 0, 0, None)
+
+    def layer(fg, fd, fs):
+        sh = [R.QMat(fs, I, H, 1, good), R.QMat(fs, I, H, 1, good), R.QMat(fs, H, I, 1, good)] if fs else [z, z, z]
+        return R.MoeLayerC(H, I, E, 0, R.QMat(fg, I, H, E, good), R.QMat(fg, I, H, E, good),
+                           R.QMat(fd, H, I, E, good), *sh, good, None, None)
+
+    lay = layer(2, 3, 4)
+    for q in (1, 2, 3, 4):
+        assert L.rfx_moe_forward_single_launch(ctypes.byref(lay), q, 4) == 1
+    assert L.rfx_moe_forward_single_launch(ctypes.byref(lay), 5, 4) == 0   # prefill sizes: two calls
+    assert L.rfx_moe_forward_single_launch(ctypes.byref(layer(2, 3, 0)), 1, 8) == 1  # no shared expert
+    for fmts in ((4, 3, 4), (2, 2, 4), (2, 3, 2), (3, 3, 4)):
+        assert L.rfx_moe_forward_single_launch(ctypes.byref(layer(*fmts)), 1, 4) == 0
+    assert L.rfx_moe_forward_single_launch(None, 1, 4) == -1
+    assert L.rfx_moe_forward_single_launch(ctypes.byref(lay), 1, 9) == -1
+
+    need = L.rfx_moe_workspace_bytes(ctypes.byref(lay), 2, 4)
+    assert need > 0
+
+    def fwd(lp, q, k, x=f, resid=None, ws=f, ws_bytes=need, flags=1):
+        return L.rfx_moe_forward(lp, x, q, k, resid, f, f, f, f, f, f, f, f, ws, ws_bytes, flags, None)
+
+    assert fwd(None, 2, 4) == -1
+    assert fwd(ctypes.byref(lay), 2, 0) == -1
+    assert fwd(ctypes.byref(lay), 0, 4) == -1
+    assert fwd(ctypes.byref(lay), 2, 4, x=None) == -1
+    assert fwd(ctypes.byref(lay), 2, 4, x=_fake(good + 4)) == -2
+    assert fwd(ctypes.byref(lay), 2, 4, resid=_fake(good + 4)) == -2
+    assert fwd(ctypes.byref(lay), 2, 4, ws=None) == -1
+    assert fwd(ctypes.byref(lay), 2, 4, ws_bytes=need - 256) == -5
+    assert fwd(ctypes.byref(lay), 3, 4) == -5   # sized for q = 2
+    assert fwd(ctypes.byref(lay), 2, 4, flags=2) == -1
+    assert fwd(ctypes.byref(lay), 2, 4, ws_bytes=need - 256, flags=0) == -5
+    assert L.rfx_moe_forward_status(ctypes.byref(lay), 2, 4, f, need - 256, None) == -5
+    assert L.rfx_moe_forward_status(ctypes.byref(lay), 2, 4, None, need, None) == -1
+
+
 def test_read_reference_validation_without_gpu():
     L = R.lib()
     good = 0x7f0000000000
@@ -318,7 +365,7 @@ def test_read_reference_validation_without_gpu():
 
 def test_status_strings():
     L = R.lib()
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.rfx_status_str(st)
     assert L.rfx_status_str(-99) == b"unknown status"
 
