@@ -592,9 +592,9 @@ def sources_sha256(names):
     return h.hexdigest()
 
 
-MOE_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_ws.h", "rfx_mx4.h",
-               "rfx_xtile.h")
-PREFILL_SOURCES = ("rfx_decode.h", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_ws.h", "rfx_prefill.hip")
+MOE_SOURCES = ("rfx_decode.h", "rfx_gemv.hip", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_dev.h", "rfx_moe_ws.h",
+               "rfx_mx4.h", "rfx_xtile.h")
+PREFILL_SOURCES = ("rfx_decode.h", "rfx_internal.h", "rfx_moe.hip", "rfx_moe_dev.h", "rfx_moe_ws.h", "rfx_prefill.hip")
 
 
 def profile_only(args, torch, R, inputgen):

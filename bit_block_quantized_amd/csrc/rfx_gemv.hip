@@ -44,9 +44,13 @@
 //     so one matrix's last workgroups overlap the next one's weight stream.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
+#include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "rfx_decode.h"
 #include "rfx_mx4.h"
@@ -483,11 +487,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 }
 
 // Several independent GEMVs in one launch. The workgroups are the jobs'
-// (row group, K split) pairs, numbered job by job with the longest work
-// first, so the heavy jobs' workgroups are placed first and the light
-// ones fill in after them; one job's last workgroups run while the next
-// job's weights stream, and only the launch's end is a tail.
+// (row group, K split) pairs. When every workgroup of the launch is
+// resident at once, the dispatcher places workgroup b on CU b mod n_cu (in
+// round b / n_cu; measured on MI355X), so each CU's share is fixed by the
+// order, and the launch ends with its most loaded CU: the host orders the
+// workgroups so that the CUs' shares cost about the same (balanced_order),
+// else they run job by job, the longest work first.
 constexpr int kMaxJobs = RFX_MAX_GEMV_JOBS;
+constexpr int kMaxOrder = 1024; // workgroups a balanced order covers
 
 // Every job runs W waves per workgroup (one block size per launch), each
 // wave a contiguous run of tiles with the next tile in flight. K is split
@@ -502,6 +509,8 @@ struct GroupArgs {
     int kind[kMaxJobs];         // 8 * fmt + q
     int wg_begin[kMaxJobs + 1]; // job j: workgroups [wg_begin[j], wg_begin[j + 1])
     int n;
+    int n_order;                // 0: workgroups job by job; else workgroup b is
+    uint16_t order[kMaxOrder];  // order[b] = (job << 12) | index within the job
 };
 
 template <bool FULL>
@@ -509,12 +518,25 @@ __global__ __launch_bounds__(64 * kGroupW) void gemv_grouped_kernel(GroupArgs ga
 {
     __shared__ float red[kGroupW * 4 * 64];
     const int bid = blockIdx.x;
-    int j = 0;
-    while (j + 1 < ga.n && bid >= ga.wg_begin[j + 1])
-        j++;
+    int j = 0, local;
+    if (ga.n_order) {
+        // read straight from the kernel-argument segment (ga is its only
+        // argument, at offset 0): indexing the by-value struct with bid makes
+        // the compiler copy the whole struct to private memory first
+        typedef const __attribute__((address_space(4))) uint16_t *korder_t;
+        typedef const __attribute__((address_space(4))) char *kbytes_t;
+        const unsigned e =
+            ((korder_t)((kbytes_t)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(GroupArgs, order)))[bid];
+        j = (int)(e >> 12);
+        local = (int)(e & 4095u);
+    } else {
+        while (j + 1 < ga.n && bid >= ga.wg_begin[j + 1])
+            j++;
+        local = bid - ga.wg_begin[j];
+    }
     j = __builtin_amdgcn_readfirstlane(j);
+    local = __builtin_amdgcn_readfirstlane(local);
     const GemvArgs &a = ga.job[j];
-    const int local = bid - ga.wg_begin[j];
     const int p = local & (a.P - 1), g = local / a.P;
 #define RFX_JOB(F, QQ)                                                                                        \
     case 8 * F + QQ:                                                                                          \
@@ -627,6 +649,131 @@ int check_act(const int8_t *xq, const float *xs, const int32_t *xsum, bool need_
     if (!st)
         st = check_ptr(xsum, 4, "xsum");
     return st;
+}
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static int n_cu[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!n_cu[dev]) {
+        int v = 0;
+        n_cu[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                        ? v
+                        : 256;
+    }
+    return n_cu[dev];
+}
+
+// Balanced workgroup order of a grouped launch whose workgroups are all
+// resident at once (at most three per CU: a workgroup of four waves at the
+// kernel's ~140 registers). Cost of a workgroup: its tiles x (tile bytes +
+// 1700 per activation column beyond the first), a fit of per-CU finishing
+// times of the six-GEMV 7168 x 7168 step on MI355X (a q = 4 tile's decode
+// and dots cost about as much as 5 KB more weights). Largest cost first,
+// each to the CU with the least cost that has a position left (CU c holds
+// positions c, c + n_cu, ...), then swaps between the most loaded CU and
+// the others while they lower its cost. Deterministic; results do not
+// depend on the order (each workgroup computes the same values wherever
+// it runs). Orders are cached per launch signature.
+bool balanced_order(GroupArgs &ga, int wgs)
+{
+    const int n_cu = cu_count();
+    if (wgs > kMaxOrder || wgs > 3 * n_cu || n_cu > 1024 || wgs < 2)
+        return false;
+    struct Key {
+        int n, wgs, n_cu, sig[kMaxJobs][3];
+        bool operator==(const Key &o) const { return std::memcmp(this, &o, sizeof(Key)) == 0; }
+    };
+    Key key;
+    std::memset(&key, 0, sizeof key);
+    key.n = ga.n;
+    key.wgs = wgs;
+    key.n_cu = n_cu;
+    for (int j = 0; j < ga.n; j++) {
+        key.sig[j][0] = ga.kind[j];
+        key.sig[j][1] = ga.wg_begin[j + 1] - ga.wg_begin[j];
+        key.sig[j][2] = (int)ceil_div(ga.job[j].S, ga.job[j].P);
+    }
+    static std::mutex mu;
+    static std::vector<std::pair<Key, std::vector<uint16_t>>> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &e : cache)
+        if (e.first == key) {
+            std::copy(e.second.begin(), e.second.end(), ga.order);
+            ga.n_order = wgs;
+            return true;
+        }
+    struct Item {
+        long cost;
+        int job, local;
+    };
+    std::vector<Item> items;
+    for (int j = 0; j < ga.n; j++) {
+        const int fmt = ga.kind[j] >> 3, q = ga.kind[j] & 7;
+        const long cost = (long)key.sig[j][2] * (tile_bytes(fmt) + 1700L * (q - 1));
+        for (int l = 0; l < key.sig[j][1]; l++)
+            items.push_back(Item{cost, j, l});
+    }
+    std::stable_sort(items.begin(), items.end(), [](const Item &a, const Item &b) { return a.cost > b.cost; });
+    std::vector<long> load(n_cu, 0);
+    std::vector<std::vector<int>> held(n_cu); // item indices per CU
+    std::vector<int> cap(n_cu);
+    for (int c = 0; c < n_cu; c++)
+        cap[c] = c < wgs ? (wgs - 1 - c) / n_cu + 1 : 0;
+    for (int i = 0; i < (int)items.size(); i++) {
+        int best = -1;
+        for (int c = 0; c < n_cu; c++)
+            if ((int)held[c].size() < cap[c] && (best < 0 || load[c] < load[best]))
+                best = c;
+        held[best].push_back(i);
+        load[best] += items[i].cost;
+    }
+    for (int it = 0; it < 4 * wgs; it++) {
+        int a = 0;
+        for (int c = 1; c < n_cu; c++)
+            if (load[c] > load[a])
+                a = c;
+        long gain = 0;
+        int bb = -1, ia = -1, ib = -1;
+        for (int b = 0; b < n_cu; b++) {
+            if (b == a)
+                continue;
+            for (int x = 0; x < (int)held[a].size(); x++)
+                for (int y = 0; y < (int)held[b].size(); y++) {
+                    const long d = items[held[a][x]].cost - items[held[b][y]].cost;
+                    if (d <= 0 || load[b] + d >= load[a])
+                        continue;
+                    const long g = load[a] - std::max(load[a] - d, load[b] + d);
+                    if (g > gain) {
+                        gain = g;
+                        bb = b;
+                        ia = x;
+                        ib = y;
+                    }
+                }
+        }
+        if (bb < 0)
+            break;
+        const long d = items[held[a][ia]].cost - items[held[bb][ib]].cost;
+        std::swap(held[a][ia], held[bb][ib]);
+        load[a] -= d;
+        load[bb] += d;
+    }
+    std::vector<uint16_t> ord(wgs);
+    for (int c = 0; c < n_cu; c++)
+        for (int k = 0; k < (int)held[c].size(); k++) {
+            const Item &t = items[held[c][k]];
+            ord[c + k * n_cu] = (uint16_t)((t.job << 12) | t.local);
+        }
+    if (cache.size() >= 16)
+        cache.erase(cache.begin());
+    cache.emplace_back(key, ord);
+    std::copy(ord.begin(), ord.end(), ga.order);
+    ga.n_order = wgs;
+    return true;
 }
 
 // ------------------------------------------------------------------
@@ -872,6 +1019,7 @@ int rfx_gemv_grouped(const rfx_gemv_job *jobs, int n_jobs, void *ws, size_t ws_b
         full = full && jb.W.cols % kTileCols == 0;
     }
     ga.wg_begin[n_jobs] = wgs;
+    balanced_order(ga, wgs);
     if (ws_off) {
         if (!ws || ws_bytes < ws_off)
             return fail(RFX_E_WORKSPACE, "rfx_gemv_grouped: workspace %zu < %zu bytes", ws ? ws_bytes : (size_t)0,
