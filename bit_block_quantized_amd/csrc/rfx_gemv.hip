@@ -670,9 +670,11 @@ int cu_count()
 // Balanced workgroup order of a grouped launch whose workgroups are all
 // resident at once (at most three per CU: a workgroup of four waves at the
 // kernel's ~140 registers). Cost of a workgroup: its tiles x (tile bytes +
-// 1700 per activation column beyond the first), a fit of per-CU finishing
-// times of the six-GEMV 7168 x 7168 step on MI355X (a q = 4 tile's decode
-// and dots cost about as much as 5 KB more weights). Largest cost first,
+// an amount per activation column beyond the first), a fit of per-CU
+// finishing times of the six-GEMV 7168 x 7168 step on MI355X: a column's
+// decode share and int8 matrix ops cost about as much as 1450 more weight
+// bytes per tile, and about 330 for FP4 on the f16 matrix op (q >= 3; at
+// q = 2 FP4 runs on the block-scaled matrix core). Largest cost first,
 // each to the CU with the least cost that has a position left (CU c holds
 // positions c, c + n_cu, ...), then swaps between the most loaded CU and
 // the others while they lower its cost. Deterministic; results do not
@@ -713,7 +715,8 @@ bool balanced_order(GroupArgs &ga, int wgs)
     std::vector<Item> items;
     for (int j = 0; j < ga.n; j++) {
         const int fmt = ga.kind[j] >> 3, q = ga.kind[j] & 7;
-        const long cost = (long)key.sig[j][2] * (tile_bytes(fmt) + 1700L * (q - 1));
+        const long per_col = fmt == RFX_FP4 ? 330L : 1450L;
+        const long cost = (long)key.sig[j][2] * (tile_bytes(fmt) + per_col * (q - 1));
         for (int l = 0; l < key.sig[j][1]; l++)
             items.push_back(Item{cost, j, l});
     }

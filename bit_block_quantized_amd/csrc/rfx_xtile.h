@@ -13,6 +13,10 @@
 // and every use waits for all of them), and a v_mfma_i32_4x4x4_16b_i8 per
 // K step takes the decoded weights of each lane's row as one operand and
 // the activations, broadcast from one 4-lane group, as the other.
+// FP4 (E2M1 codes, [HM] para 2) takes the f16 form of the same matrix op:
+// the hardware FP4 -> f16 conversion expands two codes per instruction and
+// the lane's activations are turned into f16 once per tile, which needs a
+// third of the vector instructions of the byte-permute expansion.
 #pragma once
 
 #include "rfx_decode.h"
@@ -110,6 +114,9 @@ __device__ __forceinline__ int bcast_row(int v)
 // tile feeds every column, and each lane ends with its own row's q dots.
 // ------------------------------------------------------------------
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Per-lane part of one tile's activations: code holds bytes
 // [16 (l / 4), 16 (l / 4) + 16) of column min(l % 4, Q - 1)'s 256-byte
@@ -184,18 +191,134 @@ __device__ __forceinline__ void block_half_dots_mfma(const Sel8 &sel, const XTil
     d1 = mfma_step<BI, 7>(d1, xt.code, sel.v[7]);
 }
 
+// Exact block dots of block BI as one accumulation chain (a dependent
+// matrix op of the same kind reads the previous result after two wait
+// states), started at -off * sum(x) for FP2 / FP3.
 template <int FMT, int Q, int BI>
 __device__ __forceinline__ i32x4 block_dots_mfma(const Sel8 &sel, const XTileM<Q> &xt)
 {
-    i32x4 d0, d1;
-    block_half_dots_mfma<FMT, Q, BI>(sel, xt, d0, d1);
-    return d0 + d1;
+    i32x4 d = {0, 0, 0, 0};
+    if (FMT == RFX_FP2 || FMT == RFX_FP3 || FMT == RFX_FP3E) {
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            d[j] = bcast_row<BI>(xt.nsum[j]);
+    }
+    d = mfma_step<BI, 0>(d, xt.code, sel.v[0]);
+    d = mfma_step<BI, 1>(d, xt.code, sel.v[1]);
+    d = mfma_step<BI, 2>(d, xt.code, sel.v[2]);
+    d = mfma_step<BI, 3>(d, xt.code, sel.v[3]);
+    d = mfma_step<BI, 4>(d, xt.code, sel.v[4]);
+    d = mfma_step<BI, 5>(d, xt.code, sel.v[5]);
+    d = mfma_step<BI, 6>(d, xt.code, sel.v[6]);
+    d = mfma_step<BI, 7>(d, xt.code, sel.v[7]);
+    return d;
+}
+
+// FP4 on v_mfma_f32_4x4x4_16b_f16. v_cvt_scalef32_pk_f16_fp4 with scale 2
+// turns byte b of a code word into two f16 values, 2 x E2M1 of its low and
+// of its high nibble (measured on gfx950, all 256 byte values): in word m
+// of a block those are weights 8m + b and 8m + 4 + b. K step (m, p) takes
+// bytes 2p and 2p + 1, i.e. weights (8m + 2p, 8m + 2p + 4, 8m + 2p + 1,
+// 8m + 2p + 5), and the activations must come in that order. Products and
+// sums are integers below 2^24, so the f32 accumulation is exact and the
+// result equals the int8 path's.
+struct XHalf {
+    u32x4 h[2]; // h[m % 2]: the lane's A operands of word m, step p in dwords 2p, 2p + 1
+};
+
+// The lane's 16 activations (bytes of code) in f16, in the step order
+// above: gather the two bytes of each pair, bias them to unsigned
+// (x + 128), put each under the f16 exponent byte 0x64 (the value
+// 1024 + x + 128) and subtract 1152 (exact: all values are integers below
+// 2048).
+__device__ __forceinline__ XHalf act_f16_fp4(const u32x4 &code)
+{
+    const uint32_t w[4] = {code.x, code.y, code.z, code.w};
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    uint32_t o[8];
+#pragma unroll
+    for (int mp = 0; mp < 2; mp++) {
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            const uint32_t sel = (uint32_t)(2 * p) | (uint32_t)(2 * p + 1) << 8 | (uint32_t)(2 * p + 4) << 16 |
+                                 (uint32_t)(2 * p + 5) << 24;
+            const uint32_t t = __builtin_amdgcn_perm(w[2 * mp + 1], w[2 * mp], sel) ^ 0x80808080u;
+            const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u)) - bias;
+            const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u)) - bias;
+            o[4 * mp + 2 * p] = __builtin_bit_cast(uint32_t, lo);
+            o[4 * mp + 2 * p + 1] = __builtin_bit_cast(uint32_t, hi);
+        }
+    }
+    XHalf x;
+    x.h[0] = u32x4{o[0], o[1], o[2], o[3]};
+    x.h[1] = u32x4{o[4], o[5], o[6], o[7]};
+    return x;
+}
+
+// The two K steps of code word M of block BI.
+template <int BI, int M>
+__device__ __forceinline__ f32x4 fp4_word_steps(f32x4 d, uint32_t w, const XHalf &xh)
+{
+    const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 0);
+    const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 1);
+    const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 2);
+    const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 2.0f, 3);
+    const u32x4 &xa = xh.h[M & 1];
+    const f16x4 a0 = __builtin_bit_cast(f16x4, u32x2{xa.x, xa.y});
+    const f16x4 a1 = __builtin_bit_cast(f16x4, u32x2{xa.z, xa.w});
+    const f16x4 b0 = {h0[0], h0[1], h1[0], h1[1]};
+    const f16x4 b1 = {h2[0], h2[1], h3[0], h3[1]};
+    d = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, b0, d, 4, 2 * BI + (M >> 1), 0);
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a1, b1, d, 4, 2 * BI + (M >> 1), 0);
+}
+
+// Exact dots of FP4 block BI (its four code words in c) for the four
+// column slots, as f32 integers.
+template <int BI>
+__device__ __forceinline__ f32x4 fp4_block_dots(const u32x4 &c, const XHalf &xh)
+{
+    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+    d = fp4_word_steps<BI, 0>(d, c.x, xh);
+    d = fp4_word_steps<BI, 1>(d, c.y, xh);
+    d = fp4_word_steps<BI, 2>(d, c.z, xh);
+    return fp4_word_steps<BI, 3>(d, c.w, xh);
+}
+
+// Weight scale of FP4 block BI for the 2 x E2M1 values: 2^(e - 128).
+template <int BI>
+__device__ __forceinline__ float fp4_scale(const TileRegs<RFX_FP4> &t)
+{
+    const uint32_t e = ((BI < 4 ? t.sc8.x : t.sc8.y) >> (8 * (BI & 3))) & 0xffu;
+    return ldexpf(1.0f, (int)e - 128);
+}
+
+// The f16 activations of a tile for FP4 (nothing for the other formats).
+template <int FMT>
+__device__ __forceinline__ XHalf tile_xhalf(const u32x4 &code)
+{
+    if constexpr (FMT == RFX_FP4)
+        return act_f16_fp4(code);
+    else
+        return XHalf{};
 }
 
 template <int FMT, int Q, int BI, bool FULL>
-__device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
-                                                float (&acc)[Q])
+__device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, const XHalf &xh,
+                                                int b0, int nb, float (&acc)[Q])
 {
+    if constexpr (FMT == RFX_FP4) {
+        float sw = fp4_scale<BI>(t);
+        if (!FULL)
+            sw = b0 + BI < nb ? sw : 0.0f;
+        const f32x4 d = fp4_block_dots<BI>(t.c[BI], xh);
+#pragma unroll
+        for (int j = 0; j < Q; j++) {
+            const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+            acc[j] += (sw * sxb) * d[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
     Sel8 sel;
     float sw;
     decode_block2<FMT, BI>(t, sel, sw);
@@ -228,10 +351,10 @@ __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XT
 }
 
 template <int FMT, int Q, bool FULL, int... BI>
-__device__ __forceinline__ void tile_blocks_mfma_seq(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
-                                                     float (&acc)[Q], std::integer_sequence<int, BI...>)
+__device__ __forceinline__ void tile_blocks_mfma_seq(const TileRegs<FMT> &t, const XTileM<Q> &xt, const XHalf &xh,
+                                                     int b0, int nb, float (&acc)[Q], std::integer_sequence<int, BI...>)
 {
-    (tile_block_mfma<FMT, Q, BI, FULL>(t, xt, b0, nb, acc), ...);
+    (tile_block_mfma<FMT, Q, BI, FULL>(t, xt, xh, b0, nb, acc), ...);
 }
 
 // All 8 blocks of one tile on the matrix core. Every lane must be active
@@ -240,19 +363,37 @@ template <int FMT, int Q, bool FULL>
 __device__ __forceinline__ void tile_blocks_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, int b0, int nb,
                                                  float (&acc)[Q])
 {
-    tile_blocks_mfma_seq<FMT, Q, FULL>(t, xt, b0, nb, acc, std::make_integer_sequence<int, 8>{});
+    const XHalf xh = tile_xhalf<FMT>(xt.code);
+    tile_blocks_mfma_seq<FMT, Q, FULL>(t, xt, xh, b0, nb, acc, std::make_integer_sequence<int, 8>{});
 }
 
 // A gate tile and the matching up tile (same format) against one
 // activation slice: block BI of both.
 template <int F, int Q, int BI, bool FULL>
 __device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const TileRegs<F> &tu, const XTileM<Q> &xt,
-                                                 int b0, int nb, float (&ag)[Q], float (&au)[Q])
+                                                 const XHalf &xh, int b0, int nb, float (&ag)[Q], float (&au)[Q])
 {
     float sxb[Q];
 #pragma unroll
     for (int j = 0; j < Q; j++)
         sxb[j] = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+    if constexpr (F == RFX_FP4) {
+        float sg = fp4_scale<BI>(tg), su = fp4_scale<BI>(tu);
+        if (!FULL) {
+            sg = b0 + BI < nb ? sg : 0.0f;
+            su = b0 + BI < nb ? su : 0.0f;
+        }
+        const f32x4 dg = fp4_block_dots<BI>(tg.c[BI], xh);
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            ag[j] += (sg * sxb[j]) * dg[j];
+        const f32x4 du = fp4_block_dots<BI>(tu.c[BI], xh);
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            au[j] += (su * sxb[j]) * du[j];
+        __builtin_amdgcn_sched_barrier(0);
+        return;
+    }
     Sel8 sel;
     float sw;
     decode_block2<F, BI>(tg, sel, sw);
@@ -274,23 +415,28 @@ __device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const Ti
 
 template <int F, int Q, bool FULL, int... BI>
 __device__ __forceinline__ void tile_blocks2_mfma_seq(const TileRegs<F> &tg, const TileRegs<F> &tu,
-                                                      const XTileM<Q> &xt, int b0, int nb, float (&ag)[Q],
-                                                      float (&au)[Q], std::integer_sequence<int, BI...>)
+                                                      const XTileM<Q> &xt, const XHalf &xh, int b0, int nb,
+                                                      float (&ag)[Q], float (&au)[Q], std::integer_sequence<int, BI...>)
 {
-    (tile_block2_mfma<F, Q, BI, FULL>(tg, tu, xt, b0, nb, ag, au), ...);
+    (tile_block2_mfma<F, Q, BI, FULL>(tg, tu, xt, xh, b0, nb, ag, au), ...);
 }
 
 template <int F, int Q, bool FULL>
 __device__ __forceinline__ void tile_blocks2_mfma(const TileRegs<F> &tg, const TileRegs<F> &tu, const XTileM<Q> &xt,
                                                   int b0, int nb, float (&ag)[Q], float (&au)[Q])
 {
-    tile_blocks2_mfma_seq<F, Q, FULL>(tg, tu, xt, b0, nb, ag, au, std::make_integer_sequence<int, 8>{});
+    const XHalf xh = tile_xhalf<F>(xt.code);
+    tile_blocks2_mfma_seq<F, Q, FULL>(tg, tu, xt, xh, b0, nb, ag, au, std::make_integer_sequence<int, 8>{});
 }
 
 // The per-block dots themselves (debug path), block BI.
 template <int FMT, int Q, int BI>
 __device__ __forceinline__ i32x4 tile_block_dots_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt)
 {
+    if constexpr (FMT == RFX_FP4) {
+        const f32x4 d = fp4_block_dots<BI>(t.c[BI], act_f16_fp4(xt.code));
+        return i32x4{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+    }
     Sel8 sel;
     float sw;
     decode_block2<FMT, BI>(t, sel, sw);
