@@ -196,6 +196,8 @@ def moe_bytes(R, layer, topk_idx, q):
 
 def bench_moe(torch, R, inputgen, layers, reps):
     out = {}
+    # every layer through rfx_moe_forward (at q = 1 the gate/up workgroups
+    # route themselves; at q = 4 the router launch and the FFN launches)
     # single layer, q = 4, top-6, rotated over the distinct layers
     q, k = 4, 6
     bufs = [R.MoeBuffers(lay[0], q, k) for lay in layers]
@@ -203,7 +205,7 @@ def bench_moe(torch, R, inputgen, layers, reps):
 
     def one(i):
         l = i % len(layers)
-        bufs[l].run(layers[l][0], xs[l])
+        bufs[l].forward(layers[l][0], xs[l])
 
     for l in range(len(layers)):
         one(l)
@@ -228,7 +230,7 @@ def bench_moe(torch, R, inputgen, layers, reps):
 
         def step(i):
             for l, lay in enumerate(layers):
-                sb[l].run(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
+                sb[l].forward(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
 
         step(0)
         torch.cuda.synchronize()

@@ -43,6 +43,9 @@ namespace {
 // one counter over the groups), since atomics on one address serialize;
 // the last workgroup to arrive picks the top k per token and buckets the
 // pairs.
+// ARRIVE = false: logits and quantization only; the top k is picked by
+// every gate/up workgroup of the next launch (wg_route).
+template <bool ARRIVE>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
 {
     __shared__ int s_last;
@@ -94,6 +97,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a)
         const float l = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
         __hip_atomic_store(a.logits + (size_t)tid * a.E + e, a.wb ? l + a.wb[e] : l, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!ARRIVE) {
+        route_quant(a, blockIdx.x, gridDim.x, 4, wave, lane);
+        return;
     }
     // (2) arrival. Every workgroup but the last then quantizes its share
     //     of the tokens (late, so that no logit waits for it) and leaves;
@@ -156,10 +163,10 @@ __device__ __forceinline__ void gateup_tile(const GUTile<FG, NE> &t, int s, int 
 
 template <int FG, int NE>
 __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W,
-                            float *red)
+                            float *red, const int *pairs_lds)
 {
     constexpr int FU = FG;
-    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const SlotCols<NE> cols = slot_cols<NE>(si, a, pairs_lds);
     const int nbH = a.H / 32;
     uint32_t goff[NE], moff[NE];
 #pragma unroll
@@ -234,10 +241,11 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
 // operand, built once per (half, column pair). Same tile split, reduction and
 // epilogue as gateup_body. SINGLE: one tile buffer (see gateup_body).
 template <int NE, bool SINGLE = true>
-__device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
+__device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red,
+                               const int *pairs_lds)
 {
     constexpr int TB = TileFmt<RFX_FP4>::bytes;
-    const SlotCols<NE> cols = slot_cols<NE>(si, a);
+    const SlotCols<NE> cols = slot_cols<NE>(si, a, pairs_lds);
     const int nbH = a.H / 32;
     XCols<NE> xc;
     xc.xq = a.xq;
@@ -311,13 +319,29 @@ __device__ void gateup_body_mx(const FfnArgs &a, const SlotInfo &si, int g, int 
         gateup_finish<NE>(a, cols, g, lane, W, red);
 }
 
-template <int FG, int FS>
-__global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
+// ROUTE: the workgroups of routed slots pick the top k from the router
+// logits themselves (wg_route) and row group 0 of slot 1 writes the
+// routing outputs; the shared expert's workgroups (slot 0) need no routing
+// and start on their weights at once.
+template <int FG, int FS, bool ROUTE>
+__global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a, RouteOut ro)
 {
     __shared__ float red[8 * 2 * kMaxDecodeQ * 64];
+    __shared__ RouteLds s_route;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int W = blockDim.x >> 6;
-    const SlotInfo si = find_slot(blockIdx.y, a.expert_off, a.E, a.has_shared);
+    const int *pl = nullptr;
+    const int slot = blockIdx.y;
+    SlotInfo si;
+    if (ROUTE && a.has_shared && slot == 0) {
+        si = SlotInfo{2, -1, 0, 0, 0};
+    } else {
+        if (ROUTE) {
+            wg_route(ro, a.q, a.k, a.E, blockIdx.x == 0 && slot == (a.has_shared ? 1 : 0), s_route);
+            pl = s_route.pairs;
+        }
+        si = find_slot(slot, ROUTE ? s_route.eoff : a.expert_off, a.E, a.has_shared);
+    }
     if (si.kind == 0)
         return;
     const int ne = si.kind == 2 ? a.q : si.pe - si.pb;
@@ -328,27 +352,27 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
         switch (ne) {
         case 1:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FS, 1>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FS, 1>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
         case 2:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FS, 2>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FS, 2>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
         case 3:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<3>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<3>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FS, 3>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FS, 3>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
         case 4:
             if constexpr (FS == RFX_FP4)
-                gateup_body_mx<4>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<4>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FS, 4>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FS, 4>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
         default: break;
         }
@@ -356,18 +380,18 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a)
         switch (ne) {
         case 1:
             if constexpr (FG == RFX_FP4)
-                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<1>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FG, 1>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FG, 1>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
         case 2:
             if constexpr (FG == RFX_FP4)
-                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body_mx<2>(a, si, blockIdx.x, lane, wave, W, red, pl);
             else
-                gateup_body<FG, 2>(a, si, blockIdx.x, lane, wave, W, red);
+                gateup_body<FG, 2>(a, si, blockIdx.x, lane, wave, W, red, pl);
             break;
-        case 3: gateup_body<FG, 3>(a, si, blockIdx.x, lane, wave, W, red); break;
-        case 4: gateup_body<FG, 4>(a, si, blockIdx.x, lane, wave, W, red); break;
+        case 3: gateup_body<FG, 3>(a, si, blockIdx.x, lane, wave, W, red, pl); break;
+        case 4: gateup_body<FG, 4>(a, si, blockIdx.x, lane, wave, W, red, pl); break;
         default: break;
         }
     }
@@ -602,14 +626,14 @@ int check_layer(const rfx_moe_layer *L)
     return check_ptr(L->router_w, 16, "router_w");
 }
 
-template <int FG>
-int launch_gateup(int fs, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st)
+template <int FG, bool ROUTE>
+int launch_gateup(int fs, const FfnArgs &a, const RouteOut &ro, dim3 grid, dim3 block, hipStream_t st)
 {
     const size_t lds = 0;
     switch (fs) {
-    case RFX_FP2: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP2>), grid, block, lds, st, a); break;
-    case RFX_FP3: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP3>), grid, block, lds, st, a); break;
-    case RFX_FP4: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP4>), grid, block, lds, st, a); break;
+    case RFX_FP2: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP2, ROUTE>), grid, block, lds, st, a, ro); break;
+    case RFX_FP3: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP3, ROUTE>), grid, block, lds, st, a, ro); break;
+    case RFX_FP4: hipLaunchKernelGGL((gateup_kernel<FG, RFX_FP4, ROUTE>), grid, block, lds, st, a, ro); break;
     }
     return hip_status("gate/up launch");
 }
@@ -624,6 +648,65 @@ int launch_down(int fsd, const FfnArgs &a, dim3 grid, dim3 block, hipStream_t st
     case RFX_FP4: hipLaunchKernelGGL((down_kernel<FD, RFX_FP4>), grid, block, lds, st, a); break;
     }
     return hip_status("down launch");
+}
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int n_cu[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (!n_cu[dev]) {
+        int v = 0;
+        n_cu[dev] = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                        ? v
+                        : 256;
+    }
+    return n_cu[dev];
+}
+
+// The decode FFN (q <= 4): gate/up then down. ro: the gate/up workgroups
+// route from these logits themselves (and write the routing outputs), else
+// the routing comes in a's inputs.
+int decode_ffn(const rfx_moe_layer *L, const FfnArgs &a, const RouteOut *ro, hipStream_t s)
+{
+    int st = RFX_OK;
+    const int q = a.q, k = a.k;
+    const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
+    const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);
+    const int SH = (int)ceil_div(L->hidden, 256), SI = (int)ceil_div(L->inter, 256);
+    {
+        const int W = waves_for(max_slots * GI, SH, kMaxFfnWaves);
+        dim3 grid(GI, max_slots), block(64 * W);
+        const RouteOut r = ro ? *ro : RouteOut{};
+        switch (a.fmt_g) {
+        case RFX_FP2:
+            st = ro ? launch_gateup<RFX_FP2, true>(a.fmt_sg, a, r, grid, block, s)
+                    : launch_gateup<RFX_FP2, false>(a.fmt_sg, a, r, grid, block, s);
+            break;
+        case RFX_FP3:
+            st = ro ? launch_gateup<RFX_FP3, true>(a.fmt_sg, a, r, grid, block, s)
+                    : launch_gateup<RFX_FP3, false>(a.fmt_sg, a, r, grid, block, s);
+            break;
+        case RFX_FP4:
+            st = ro ? launch_gateup<RFX_FP4, true>(a.fmt_sg, a, r, grid, block, s)
+                    : launch_gateup<RFX_FP4, false>(a.fmt_sg, a, r, grid, block, s);
+            break;
+        }
+        if (st)
+            return st;
+    }
+    {
+        const int W = waves_for(max_slots * GH, SI, kMaxFfnWaves);
+        dim3 grid(GH, max_slots), block(64 * W);
+        switch (a.fmt_d) {
+        case RFX_FP2: st = launch_down<RFX_FP2>(a.fmt_sd, a, grid, block, s); break;
+        case RFX_FP3: st = launch_down<RFX_FP3>(a.fmt_sd, a, grid, block, s); break;
+        case RFX_FP4: st = launch_down<RFX_FP4>(a.fmt_sd, a, grid, block, s); break;
+        }
+    }
+    return st;
 }
 
 RouteArgs make_route_args(const rfx_moe_layer *L, const float *x, int q, int k, int32_t *topk_idx, float *topk_w,
@@ -731,7 +814,7 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
     if (L->hidden > 8192) // one workgroup reads a row as 8 float4 per thread
         return fail(RFX_E_UNSUPPORTED, "router: hidden=%d > 8192 for q <= 4", L->hidden);
     const int grid = L->n_experts; // one workgroup per expert row
-    hipLaunchKernelGGL(route_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(route_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream, a);
     return hip_status("route launch");
 }
 
@@ -760,31 +843,7 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     if (q > kMaxDecodeQ) // many tokens: grouped matrix-core path
         return prefill_ffn(L, q, k, xq, xs, topk_w, pairs_sorted, expert_off, resid, y, w, (hipStream_t)stream);
     const FfnArgs a = make_ffn_args(L, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_off, resid, y, w);
-    const int max_slots = (q * k < L->n_experts ? q * k : L->n_experts) + (a.has_shared ? 1 : 0);
-    const hipStream_t s = (hipStream_t)stream;
-    const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);
-    const int SH = (int)ceil_div(L->hidden, 256), SI = (int)ceil_div(L->inter, 256);
-    {
-        const int W = waves_for(max_slots * GI, SH, kMaxFfnWaves);
-        dim3 grid(GI, max_slots), block(64 * W);
-        switch (a.fmt_g) {
-        case RFX_FP2: st = launch_gateup<RFX_FP2>(a.fmt_sg, a, grid, block, s); break;
-        case RFX_FP3: st = launch_gateup<RFX_FP3>(a.fmt_sg, a, grid, block, s); break;
-        case RFX_FP4: st = launch_gateup<RFX_FP4>(a.fmt_sg, a, grid, block, s); break;
-        }
-        if (st)
-            return st;
-    }
-    {
-        const int W = waves_for(max_slots * GH, SI, kMaxFfnWaves);
-        dim3 grid(GH, max_slots), block(64 * W);
-        switch (a.fmt_d) {
-        case RFX_FP2: st = launch_down<RFX_FP2>(a.fmt_sd, a, grid, block, s); break;
-        case RFX_FP3: st = launch_down<RFX_FP3>(a.fmt_sd, a, grid, block, s); break;
-        case RFX_FP4: st = launch_down<RFX_FP4>(a.fmt_sd, a, grid, block, s); break;
-        }
-    }
-    return st;
+    return decode_ffn(L, a, nullptr, (hipStream_t)stream);
 }
 
 int rfx_moe_forward(const rfx_moe_layer *L, const float *x, int q, int k, const float *resid, float *y,
@@ -813,15 +872,31 @@ int rfx_moe_forward(const rfx_moe_layer *L, const float *x, int q, int k, const 
     if (ws_bytes < w.bytes)
         return fail(RFX_E_WORKSPACE, "MoE workspace %zu < %zu bytes", ws_bytes, w.bytes);
     const FfnArgs fa = make_ffn_args(L, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_off, resid, y, w);
-    if (!(flags & RFX_FORWARD_ONE_LAUNCH) || !layer_kernel_takes(fa, q, k)) {
+    const RouteArgs ra = make_route_args(L, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, w);
+    if ((flags & RFX_FORWARD_ONE_LAUNCH) && layer_kernel_takes(fa, q, k))
+        return launch_layer(fa, ra, (hipStream_t)stream);
+    // Routing inside the gate/up workgroups costs each of them the top-k
+    // selection (~2 us before its weights start to stream), which pays for
+    // the router launch's arrival phase only when the gate/up grid runs in
+    // one round of one workgroup per compute unit (measured at q = 1 top-4:
+    // 28.2 against 29.4 us per layer; at q = 4 the workgroups run in
+    // several rounds per CU, each paying the selection again).
+    const int gu_wgs = (int)ceil_div(L->inter, 64) * ((q * k < L->n_experts ? q * k : L->n_experts) +
+                                                      (fa.has_shared ? 1 : 0));
+    if (q > kMaxDecodeQ || L->hidden > 8192 || gu_wgs > device_cus()) {
         if ((st = rfx_moe_route_topk(L, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, ws,
                                      ws_bytes, stream)))
             return st;
         return rfx_moe_ffn(L, q, k, xq, xs, xsum, topk_idx, topk_w, pairs_sorted, expert_off, resid, y, ws, ws_bytes,
                            stream);
     }
-    const RouteArgs ra = make_route_args(L, x, q, k, topk_idx, topk_w, pairs_sorted, expert_off, xq, xs, xsum, w);
-    return launch_layer(fa, ra, (hipStream_t)stream);
+    // the router launch computes the logits and quantizes x, and every
+    // routed gate/up workgroup picks the top k from the logits
+    hipLaunchKernelGGL(route_kernel<false>, dim3(L->n_experts), dim3(256), 0, (hipStream_t)stream, ra);
+    if ((st = hip_status("route launch")))
+        return st;
+    const RouteOut ro{w.logits, topk_idx, topk_w, pairs_sorted, expert_off};
+    return decode_ffn(L, fa, &ro, (hipStream_t)stream);
 }
 
 int rfx_moe_forward_single_launch(const rfx_moe_layer *L, int q, int k)

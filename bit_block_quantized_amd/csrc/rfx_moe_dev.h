@@ -140,8 +140,8 @@ __device__ __forceinline__ void order_pair(uint32_t &ka, int &ia, uint32_t &kb, 
 // id. Each lane sorts its four candidates once; a round then takes the
 // wave maximum of the lane heads and the lowest id among the heads equal
 // to it (one ballot; a second reduction only when several lanes tie), and
-// that lane drops its head. Lane j keeps pick j. Writes topk_idx / topk_w
-// and s_idx[t*k + j]. The last workgroup runs this once per call, with a
+// that lane drops its head. Lane j keeps pick j. Writes s_idx[t*k + j]
+// and, unless topk_idx is null, topk_idx / topk_w. The last workgroup runs this once per call, with a
 // cold instruction cache, so the loops stay rolled and the code short.
 inline __device__ void wave_topk(const float (&l)[4], int E, int k, int t, int lane, int32_t *topk_idx, float *topk_w,
                           int *s_idx)
@@ -194,8 +194,10 @@ inline __device__ void wave_topk(const float (&l)[4], int E, int k, int t, int l
         zz += lane + 64 * r < E ? expf(l[r] - m) : 0.0f;
     const float z = wave_fsum(zz);
     if (lane < k) {
-        topk_idx[t * k + lane] = my_id;
-        topk_w[t * k + lane] = expf(key_logit(my_key) - m) / z;
+        if (topk_idx) {
+            topk_idx[t * k + lane] = my_id;
+            topk_w[t * k + lane] = expf(key_logit(my_key) - m) / z;
+        }
         s_idx[t * k + lane] = my_id;
     }
 }
@@ -300,6 +302,81 @@ __device__ __forceinline__ void route_select(const RouteArgs &a, int ngroups, in
 }
 
 // ------------------------------------------------------------------
+// Routing inside each FFN workgroup. When the router's logits come
+// complete from the previous launch, every gate/up workgroup can pick the
+// top k and bucket the pairs itself (a few hundred instructions) instead of
+// the router launch finding its last workgroup through arrival counters and
+// that workgroup reading the logits back: the launch boundary is the only
+// barrier. The operations and their order are route_select's, so the
+// results are the same bit for bit; one workgroup also writes the routing
+// outputs, which the down launch and the caller read.
+// ------------------------------------------------------------------
+struct RouteOut {
+    const float *logits; // [q][E] router logits (with bias), complete
+    int32_t *topk_idx;   // [q][k]
+    float *topk_w;       // [q][k]
+    int32_t *pairs_sorted;
+    int32_t *expert_off; // [E + 1]
+};
+
+struct RouteLds {
+    __align__(16) int idx[kMaxDecodeQ * kMaxK]; // expert of pair p = t*k + j
+    int pairs[kMaxDecodeQ * kMaxK];             // pairs_sorted
+    int eoff[kMaxE + 1];                        // expert_off
+};
+
+__device__ __forceinline__ void wg_route(const RouteOut &ro, int q, int k, int E, bool out, RouteLds &s)
+{
+    const int tid = threadIdx.x, lane = tid & 63, nt = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), W = nt >> 6;
+    const int np = q * k;
+    for (int i = np + tid; i < kMaxDecodeQ * kMaxK; i += nt)
+        s.idx[i] = 0x7FFFFFFF;
+    for (int t = wave; t < q; t += W) {
+        float l[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int ee = lane + 64 * r;
+            l[r] = ee < E ? ro.logits[(size_t)t * E + ee] : -INFINITY;
+        }
+        wave_topk(l, E, k, t, lane, out ? ro.topk_idx : nullptr, ro.topk_w, s.idx);
+    }
+    __syncthreads();
+    // stable bucketing (route_select's counts), the whole pair list read
+    // once as int4 words (a broadcast: every lane reads the same words);
+    // the unused tail holds a key above every expert, so it counts nowhere
+    int pe[kMaxDecodeQ * kMaxK];
+#pragma unroll
+    for (int c = 0; c < kMaxDecodeQ * kMaxK / 4; c++) {
+        const int4 u = reinterpret_cast<const int4 *>(s.idx)[c];
+        pe[4 * c] = u.x;
+        pe[4 * c + 1] = u.y;
+        pe[4 * c + 2] = u.z;
+        pe[4 * c + 3] = u.w;
+    }
+    if (tid < np) {
+        const int mine = s.idx[tid];
+        int pos = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxDecodeQ * kMaxK; i++)
+            pos += (pe[i] < mine || (pe[i] == mine && i < tid)) ? 1 : 0;
+        s.pairs[pos] = tid;
+        if (out)
+            ro.pairs_sorted[pos] = tid;
+    }
+    for (int e = tid; e <= E; e += nt) {
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxDecodeQ * kMaxK; i++)
+            before += pe[i] < e ? 1 : 0;
+        s.eoff[e] = before;
+        if (out)
+            ro.expert_off[e] = before;
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------
 // Slot plan: slot 0 is the shared expert (when present), then the routed
 // experts that have pairs, in id order. The FFN grids are (row group,
 // slot) with the row group fastest, so the shared expert (the slot with
@@ -400,8 +477,11 @@ struct SlotCols {
     int token[NE];
 };
 
+// pairs_lds: the sorted pairs in LDS (routing inside the workgroup), else
+// null and they are read from a.pairs_sorted.
 template <int NE>
-__device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnArgs &a)
+__device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnArgs &a,
+                                                  const int *pairs_lds = nullptr)
 {
     SlotCols<NE> c;
     const sptr_i32 ps = as_scalar_i32(a.pairs_sorted);
@@ -411,7 +491,7 @@ __device__ __forceinline__ SlotCols<NE> slot_cols(const SlotInfo &si, const FfnA
             c.token[j] = j;
             c.out_idx[j] = a.q * a.k + j;
         } else {
-            const int p = ps[si.pb + j];
+            const int p = pairs_lds ? __builtin_amdgcn_readfirstlane(pairs_lds[si.pb + j]) : ps[si.pb + j];
             c.token[j] = p / a.k;
             c.out_idx[j] = p;
         }
@@ -516,16 +596,20 @@ __device__ __forceinline__ void combine_rows(const FfnArgs &a, int g, int lane)
 }
 
 // Waves per workgroup of the decode gate/up and down kernels: about three
-// waves per SIMD over the chip, at most max_waves, at most one per tile
-// (each wave takes a contiguous share of the row group's tiles; the shares'
-// fp32 partials are summed in wave order, so this choice fixes the
-// summation order and is shared by both decode paths). Host code.
-constexpr int kMaxFfnWaves = 8;
+// waves per SIMD over the chip, rounded down to a power of two (a
+// workgroup's waves then spread evenly over the four SIMDs of a CU: six
+// waves at ~160 registers left room for one workgroup per CU and measured
+// 4.6 us slower per q = 4 top-4 layer than four), at most max_waves, at
+// most one per tile (each wave takes a contiguous share of the row group's
+// tiles; the shares' fp32 partials are summed in wave order, so this choice
+// fixes the summation order and is shared by both decode paths). Host code.
 inline int waves_for(int wgs, int tiles, int max_waves)
 {
     const int target = 3072; // ~3 waves per SIMD over 256 CUs
     int W = (target + wgs - 1) / wgs;
     W = W < 1 ? 1 : W > max_waves ? max_waves : W;
+    while (W & (W - 1))
+        W &= W - 1;
     return W > tiles ? tiles : W;
 }
 

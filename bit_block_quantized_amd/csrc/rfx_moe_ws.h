@@ -14,6 +14,7 @@ namespace rfx {
 constexpr int kMaxK = 8;          // experts per token
 constexpr int kMaxE = 256;        // routed experts per layer
 constexpr int kMaxDecodeQ = 4;    // tokens handled by the decode kernels
+constexpr int kMaxFfnWaves = 8;   // waves per decode FFN workgroup
 constexpr int kPrefillChunk = 64; // tokens per work item of the prefill kernels
 constexpr int kMaxPrefillQ = 1 << 16;
 // Arrival counters of the decode router: one per kRouteGroup workgroups,

@@ -159,9 +159,11 @@ class MoeBuffers:
         self.y = torch.empty((q, H), dtype=torch.float32, device=device)
         self.ws = torch.zeros(moe_workspace_bytes(layer, q, k), dtype=torch.uint8, device=device)
 
-    def forward(self, layer: DeviceMoeLayer, x, resid=None, out=None, one_launch=True, stream=None):
-        """The same as run(), through rfx_moe_forward (one_launch: the
-        single-launch layer kernel for the page's formats at q <= 4)."""
+    def forward(self, layer: DeviceMoeLayer, x, resid=None, out=None, one_launch=False, stream=None):
+        """The same as run(), through rfx_moe_forward: at q <= 4 the router
+        launch computes the logits and every gate/up workgroup picks the top
+        k itself (one_launch: the single-launch layer kernel for the page's
+        formats instead)."""
         from . import moe_forward
         y = self.y if out is None else out
         moe_forward(layer, x, self.q, self.k, y, self.topk_idx, self.topk_w, self.pairs_sorted, self.expert_off,

@@ -342,8 +342,14 @@ int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
                 float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* The whole layer, rfx_moe_route_topk then rfx_moe_ffn, in one call with
- * the same arguments, outputs and results (bit for bit). flags = 0: the
- * two calls (three kernel launches). flags = RFX_FORWARD_ONE_LAUNCH: for
+ * the same arguments, outputs and results (bit for bit). flags = 0: three
+ * kernel launches. When the gate/up grid holds at most one workgroup per
+ * compute unit (q = 1 at the pages' sizes), the router launch only
+ * computes the logits and quantizes x, and every routed gate/up workgroup
+ * picks the top k and buckets the pairs itself from the logits (one of
+ * them writes topk_idx, topk_w, pairs_sorted and expert_off): the launch
+ * boundary replaces the router's arrival counters. Otherwise the two calls.
+ * flags = RFX_FORWARD_ONE_LAUNCH: for
  * q <= 4 with routed gate/up in RFX_FP2, down in RFX_FP3 and the shared
  * expert (if any) in RFX_FP4 ([HM] para 2 and [KK] ROCmFPX section), one
  * kernel launch ([HM] para 3: several positions verified in one fused

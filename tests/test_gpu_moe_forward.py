@@ -1,8 +1,10 @@
-"""GPU tests of rfx_moe_forward, the whole MoE decode layer in one call (one
-kernel launch for FP2 gate/up, FP3 down and an FP4 shared expert at q <= 4).
-Its arithmetic is the two-call path's (rfx_moe_route_topk + rfx_moe_ffn)
-step for step, so every output is compared with that path bit for bit, and
-the layer is also checked stage by stage against the oracle. The kernel's
+"""GPU tests of rfx_moe_forward, the whole MoE decode layer in one call: by
+default the router launch computes the logits and every gate/up workgroup
+picks the top k itself; with the one-launch flag, a single kernel for FP2
+gate/up, FP3 down and an FP4 shared expert at q <= 4. Both compute the
+two-call path's arithmetic (rfx_moe_route_topk + rfx_moe_ffn) step for
+step, so every output is compared with that path bit for bit, and the layer
+is also checked stage by stage against the oracle. The one-launch kernel's
 counters must return to zero after every call: repeated calls on the same
 buffers, graph replays and the chained eight-layer stack check that, and
 the time-bound status word must stay clear."""
@@ -49,16 +51,19 @@ def _same(a, b, what):
 
 
 def _both(torch, dev, x, k, resid=False, single=True):
-    """The layer through moe_forward and through the two calls, on separate
-    buffers, for the same tokens; returns (forward outputs, two-call
-    outputs)."""
+    """The layer through moe_forward (one-launch flag) and through the two
+    calls, on separate buffers, for the same tokens; the default forward
+    path (routing inside the gate/up workgroups) must equal the two calls
+    too. Returns (one-launch forward outputs, two-call outputs, buffers)."""
     q = x.shape[0]
     assert R.moe_forward_single_launch(dev, q, k) == single
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    bf, br = R.MoeBuffers(dev, q, k), R.MoeBuffers(dev, q, k)
-    bf.forward(dev, xd, resid=xd if resid else None)
+    bf, br, b0 = R.MoeBuffers(dev, q, k), R.MoeBuffers(dev, q, k), R.MoeBuffers(dev, q, k)
+    bf.forward(dev, xd, resid=xd if resid else None, one_launch=True)
     br.run(dev, xd, resid=xd if resid else None)
+    b0.forward(dev, xd, resid=xd if resid else None)
     f, r = _read(torch, dev, bf), _read(torch, dev, br)
+    _same(_read(torch, dev, b0), r, "routed forward vs two calls")
     R.moe_forward_status(dev, q, k, bf.ws)
     return f, r, bf
 
@@ -95,17 +100,21 @@ def test_forward_k_edges_and_shared_picks():
         _check_layer(spec, f, x, k, orc, resid=x)
 
 
-def test_forward_default_takes_two_calls():
-    """Without the one-launch flag rfx_moe_forward runs the two calls."""
+@pytest.mark.parametrize("q,k", [(1, 1), (2, 4), (4, 8)])
+def test_forward_default_routes_in_gateup(q, k):
+    """Without the one-launch flag the gate/up workgroups pick the top k
+    from the router's logits; every routing output (written by one
+    workgroup) and y equal the two calls'. Small workgroups (few slots, one
+    wave per workgroup for some shapes) and all k."""
     torch = need_gpu()
     spec = LayerSpec(layer=4, hidden=512, inter=256, n_experts=16, shared=True, bias="zipf")
     dev = spec.build_device()
-    x = inputgen.tokens(4, 1, 2, spec.hidden)
+    x = inputgen.tokens(4, q + 10 * k, q, spec.hidden)
     xd = torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    bf, br = R.MoeBuffers(dev, 2, 4), R.MoeBuffers(dev, 2, 4)
-    bf.forward(dev, xd, resid=xd, one_launch=False)
+    bf, br = R.MoeBuffers(dev, q, k), R.MoeBuffers(dev, q, k)
+    bf.forward(dev, xd, resid=xd)
     br.run(dev, xd, resid=xd)
-    _same(_read(torch, dev, bf), _read(torch, dev, br), "flags = 0")
+    _same(_read(torch, dev, bf), _read(torch, dev, br), f"flags = 0, q={q} k={k}")
 
 
 @pytest.mark.parametrize("fmts", [(4, 4, 2), (3, 2, 3)])
@@ -122,7 +131,8 @@ def test_forward_other_formats_take_two_calls(fmts):
     _same(f, r, "fallback")
 
 
-def test_forward_repeated_calls_reset_counters():
+@pytest.mark.parametrize("one_launch", [True, False])
+def test_forward_repeated_calls_reset_counters(one_launch):
     """Consecutive calls on the same buffers with different tokens and
     token counts' worth of routing: each call's outputs equal the two-call
     path's for the same tokens (a counter left non-zero by one call would
@@ -134,7 +144,7 @@ def test_forward_repeated_calls_reset_counters():
         bf, br = R.MoeBuffers(dev, q, 4), R.MoeBuffers(dev, q, 4)
         for i in range(6):
             xd = torch.from_numpy(inputgen.tokens(6, 100 + i, q, spec.hidden)).cuda()
-            bf.forward(dev, xd, resid=xd)
+            bf.forward(dev, xd, resid=xd, one_launch=one_launch)
             br.run(dev, xd, resid=xd)
             _same(_read(torch, dev, bf), _read(torch, dev, br), f"q={q} call {i}")
         R.moe_forward_status(dev, q, 4, bf.ws)
@@ -142,7 +152,8 @@ def test_forward_repeated_calls_reset_counters():
         say(f"  q={q}: workspace words non-zero after the calls: {int(np.count_nonzero(sync))}")
 
 
-def test_forward_graph_replays():
+@pytest.mark.parametrize("one_launch", [True, False])
+def test_forward_graph_replays(one_launch):
     """Three layers' forward calls captured in one graph and replayed four
     times with eager work in between; every replay's outputs equal the
     eager results."""
@@ -156,7 +167,7 @@ def test_forward_graph_replays():
 
     def chain():
         for l, d in enumerate(devs):
-            bufs[l].forward(d, xs[l], resid=xs[l], out=xs[l + 1])
+            bufs[l].forward(d, xs[l], resid=xs[l], out=xs[l + 1], one_launch=one_launch)
 
     chain()
     torch.cuda.synchronize()
@@ -185,13 +196,16 @@ def test_forward_graph_replays():
         R.moe_forward_status(d, q, k, b.ws)
 
 
-def _stack(torch, devs, x0, k, fused):
+def _stack(torch, devs, x0, k, fused, one_launch=True):
     q, H = x0.shape[0], devs[0].hidden
     bufs = [R.MoeBuffers(d, q, k) for d in devs]
     xb = [torch.from_numpy(np.ascontiguousarray(x0)).cuda()]
     xb += [torch.empty((q, H), dtype=torch.float32, device="cuda") for _ in devs]
     for l, d in enumerate(devs):
-        (bufs[l].forward if fused else bufs[l].run)(d, xb[l], resid=xb[l], out=xb[l + 1])
+        if fused:
+            bufs[l].forward(d, xb[l], resid=xb[l], out=xb[l + 1], one_launch=one_launch)
+        else:
+            bufs[l].run(d, xb[l], resid=xb[l], out=xb[l + 1])
     torch.cuda.synchronize()
     outs = []
     for l, (d, b) in enumerate(zip(devs, bufs)):
@@ -218,8 +232,10 @@ def test_forward_stack_eight_layers(q):
     x0 = inputgen.tokens(100, 0, q, 512)
     fo = _stack(torch, devs, x0, 4, True)
     ro = _stack(torch, devs, x0, 4, False)
+    f0 = _stack(torch, devs, x0, 4, True, one_launch=False)
     for l in range(8):
         _same(fo[l], ro[l], f"layer {l}")
+        _same(f0[l], ro[l], f"routed forward, layer {l}")
     for l, (spec, gpu) in enumerate(zip(specs, fo)):
         _check_layer(spec, gpu, gpu["x"], 4, OracleMoe(spec), resid=gpu["x"])
 
