@@ -616,15 +616,15 @@ def profile_only(args, torch, R, inputgen):
         bufs = [R.MoeBuffers(lay[0], q, k) for lay in layers]
         xs = [torch.from_numpy(inputgen.tokens(l, 7, q, MOE_H)).cuda() for l in range(len(layers))]
         n = max(1, args.steps) * len(layers)
-        ms4 = time_eager(torch, lambda i: bufs[i % len(layers)].run(layers[i % len(layers)][0], xs[i % len(layers)]),
-                         n)
+        ms4 = time_eager(torch, lambda i: bufs[i % len(layers)].forward(layers[i % len(layers)][0],
+                                                                         xs[i % len(layers)]), n)
         sb = [R.MoeBuffers(lay[1], 1, 4) for lay in layers]
         x0 = torch.from_numpy(inputgen.tokens(100, 0, 1, MOE_H)).cuda()
         xbuf = [x0] + [torch.empty((1, MOE_H), dtype=torch.float32, device="cuda") for _ in layers]
 
         def step(i):
             for l, lay in enumerate(layers):
-                sb[l].run(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
+                sb[l].forward(lay[1], xbuf[l], resid=xbuf[l], out=xbuf[l + 1])
 
         ms1 = time_eager(torch, step, max(1, args.steps))
         out = {"only": "moe", "layer_q4_top6_us": round(ms4 * 1e3, 1), "stack_q1_us_per_step": round(ms1 * 1e3, 1),
