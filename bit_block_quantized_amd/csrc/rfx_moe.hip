@@ -677,7 +677,7 @@ int decode_ffn(const rfx_moe_layer *L, const FfnArgs &a, const RouteOut *ro, hip
     const int GI = (int)ceil_div(L->inter, 64), GH = (int)ceil_div(L->hidden, 64);
     const int SH = (int)ceil_div(L->hidden, 256), SI = (int)ceil_div(L->inter, 256);
     {
-        const int W = waves_for(max_slots * GI, SH, kMaxFfnWaves);
+        const int W = waves_for(max_slots * GI, SH, kMaxFfnWaves, kGateUpWaveTarget);
         dim3 grid(GI, max_slots), block(64 * W);
         const RouteOut r = ro ? *ro : RouteOut{};
         switch (a.fmt_g) {
@@ -698,7 +698,7 @@ int decode_ffn(const rfx_moe_layer *L, const FfnArgs &a, const RouteOut *ro, hip
             return st;
     }
     {
-        const int W = waves_for(max_slots * GH, SI, kMaxFfnWaves);
+        const int W = waves_for(max_slots * GH, SI, kMaxFfnWaves, kDownWaveTarget);
         dim3 grid(GH, max_slots), block(64 * W);
         switch (a.fmt_d) {
         case RFX_FP2: st = launch_down<RFX_FP2>(a.fmt_sd, a, grid, block, s); break;

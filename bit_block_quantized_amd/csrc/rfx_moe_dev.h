@@ -595,17 +595,21 @@ __device__ __forceinline__ void combine_rows(const FfnArgs &a, int g, int lane)
     }
 }
 
-// Waves per workgroup of the decode gate/up and down kernels: about three
-// waves per SIMD over the chip, rounded down to a power of two (a
+// Waves per workgroup of the decode gate/up and down kernels: about
+// `target` waves over the chip (gate/up 3072, three per SIMD; down twice
+// that, kDownWaveTarget: its workgroups hold ~120 registers, four waves
+// per SIMD, and measured 1-2 us faster per q = 4 layer with four waves
+// per workgroup than with two), rounded down to a power of two (a
 // workgroup's waves then spread evenly over the four SIMDs of a CU: six
 // waves at ~160 registers left room for one workgroup per CU and measured
 // 4.6 us slower per q = 4 top-4 layer than four), at most max_waves, at
 // most one per tile (each wave takes a contiguous share of the row group's
 // tiles; the shares' fp32 partials are summed in wave order, so this choice
 // fixes the summation order and is shared by both decode paths). Host code.
-inline int waves_for(int wgs, int tiles, int max_waves)
+constexpr int kGateUpWaveTarget = 3072;
+constexpr int kDownWaveTarget = 6144;
+inline int waves_for(int wgs, int tiles, int max_waves, int target)
 {
-    const int target = 3072; // ~3 waves per SIMD over 256 CUs
     int W = (target + wgs - 1) / wgs;
     W = W < 1 ? 1 : W > max_waves ? max_waves : W;
     while (W & (W - 1))

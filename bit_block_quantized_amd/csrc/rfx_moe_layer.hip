@@ -799,8 +799,8 @@ bool layer_kernel_takes(const FfnArgs &f, int q, int k)
         return false;
     const int max_slots = (q * k < f.E ? q * k : f.E) + (f.has_shared ? 1 : 0);
     const int gi = (int)ceil_div(f.I, 64), gh = (int)ceil_div(f.H, 64);
-    const int rpw = rows_per_wg(waves_for(max_slots * gi, (int)ceil_div(f.H, 256), kMaxFfnWaves),
-                                waves_for(max_slots * gh, (int)ceil_div(f.I, 256), kMaxFfnWaves));
+    const int rpw = rows_per_wg(waves_for(max_slots * gi, (int)ceil_div(f.H, 256), kMaxFfnWaves, kGateUpWaveTarget),
+                                waves_for(max_slots * gh, (int)ceil_div(f.I, 256), kMaxFfnWaves, kDownWaveTarget));
     const int64_t n_wg = ceil_div((int64_t)q * (f.H / 32), 8 * rpw) + ceil_div(f.E, rpw) + (int64_t)max_slots * (gi + gh);
     return n_wg <= (int64_t)kMaxExitGroups * kExitGroup;
 }
@@ -815,8 +815,8 @@ int launch_layer(const FfnArgs &f, const RouteArgs &r, hipStream_t stream)
     L.max_slots = (q * k < f.E ? q * k : f.E) + (f.has_shared ? 1 : 0);
     L.gi = (int)ceil_div(f.I, 64);
     L.gh = (int)ceil_div(f.H, 64);
-    L.w_gu = waves_for(L.max_slots * L.gi, (int)ceil_div(f.H, 256), kMaxFfnWaves);
-    L.w_dn = waves_for(L.max_slots * L.gh, (int)ceil_div(f.I, 256), kMaxFfnWaves);
+    L.w_gu = waves_for(L.max_slots * L.gi, (int)ceil_div(f.H, 256), kMaxFfnWaves, kGateUpWaveTarget);
+    L.w_dn = waves_for(L.max_slots * L.gh, (int)ceil_div(f.I, 256), kMaxFfnWaves, kDownWaveTarget);
     const int rpw = rows_per_wg(L.w_gu, L.w_dn), W = 4 * rpw;
     L.n_route = (int)ceil_div(f.E, rpw);
     L.n_quant = (int)ceil_div((int64_t)q * (f.H / 32), 2 * W); // two blocks per wave
