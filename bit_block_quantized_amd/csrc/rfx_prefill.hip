@@ -592,14 +592,22 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
     const int lane = threadIdx.x & 63, g = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const u32x4 *fr = reinterpret_cast<const u32x4 *>(frag) + lane;
-    const float *sxp = lsx + 4 * g;
+    // the scale products sw(row) * sx(token) of a 16 x 16 output tile come
+    // from v_mfma_f32_4x4x1_16b_f32: its output lane l, register v is
+    // A(lane 4 (l / 4) + v) * B(lane l) (measured on gfx950), which is the
+    // 16x16x32 product's layout (token 4 (l / 16) + v, row l % 16) when lane
+    // l holds the scale of token 4 (l / 16) + l % 4 as A and its row's
+    // scale as B. One product per output, rounded once: the same value as
+    // the vector multiply it replaces, with four fewer VALU operations per
+    // output tile and block.
+    const float *sxl = lsx + 4 * g + (lane & 3);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
         const int b = 4 * hf + j;
         if (s * 8 + b >= nb)
             break;
         f16x8 av = __builtin_bit_cast(f16x8, fr[b * 64]);
-        f32x4 sx = *reinterpret_cast<const f32x4 *>(sxp + b * 64);
+        float sa = sxl[b * 64];
         f16x8 wv[M];
         float sw[M];
 #pragma unroll
@@ -607,14 +615,15 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
             wv[m] = wfrag<F>(w[m], j, g);
             sw[m] = wscale<F>(w[m], j);
         }
-        f32x4 dp[M], sx_prev = sx;
+        f32x4 dp[M];
+        float sa_prev = sa;
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) {
             f16x8 av_n = av;
-            f32x4 sx_n = sx;
+            float sa_n = sa;
             if (tt + 1 < NT) {
                 av_n = __builtin_bit_cast(f16x8, fr[((tt + 1) * 8 + b) * 64]);
-                sx_n = *reinterpret_cast<const f32x4 *>(sxp + b * 64 + 16 * (tt + 1));
+                sa_n = sxl[b * 64 + 16 * (tt + 1)];
             }
             f32x4 dc[M];
 #pragma unroll
@@ -622,10 +631,12 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
                 dc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, wv[m], zero, 0, 0, 0);
             if (tt > 0) {
 #pragma unroll
-                for (int m = 0; m < M; m++)
+                for (int m = 0; m < M; m++) {
+                    const f32x4 sc = __builtin_amdgcn_mfma_f32_4x4x1f32(sa_prev, sw[m], zero, 0, 0, 0);
 #pragma unroll
                     for (int v = 0; v < 4; v++)
-                        acc[m][tt - 1][v] = fmaf(dp[m][v], sw[m] * sx_prev[v], acc[m][tt - 1][v]);
+                        acc[m][tt - 1][v] = fmaf(dp[m][v], sc[v], acc[m][tt - 1][v]);
+                }
             }
             if (DBG) {
 #pragma unroll
@@ -644,15 +655,17 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
 #pragma unroll
             for (int m = 0; m < M; m++)
                 dp[m] = dc[m];
-            sx_prev = sx;
+            sa_prev = sa;
             av = av_n;
-            sx = sx_n;
+            sa = sa_n;
         }
 #pragma unroll
-        for (int m = 0; m < M; m++)
+        for (int m = 0; m < M; m++) {
+            const f32x4 sc = __builtin_amdgcn_mfma_f32_4x4x1f32(sa_prev, sw[m], zero, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 4; v++)
-                acc[m][NT - 1][v] = fmaf(dp[m][v], sw[m] * sx_prev[v], acc[m][NT - 1][v]);
+                acc[m][NT - 1][v] = fmaf(dp[m][v], sc[v], acc[m][NT - 1][v]);
+        }
     }
 }
 
