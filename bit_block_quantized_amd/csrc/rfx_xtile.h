@@ -124,13 +124,25 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // scale of block n & 7 in sx[j] and, for FP2/FP3, -off * (block sum) in
 // nsum[j] (off = 3 or 7, the codebook offset folded out of the dot; FP2M:
 // the block sum itself, which multiplies the block minimum); the block's
-// values reach every lane by DPP row broadcast.
+// values reach every lane by DPP row broadcast (sx only for FP2M and
+// FP2S). sxa: lane m holds the scale of column min(m % 4, Q - 1) for block
+// (m / 4) % 8, the A operand of the scale products (scale_products).
 template <int Q>
 struct XTileM {
     u32x4 code;
     float sx[Q];
     int nsum[Q];
+    float sxa;
 };
+
+// The formats whose epilogue is (s_w * s_x) * D, scaled through
+// scale_products; FP2M and FP2S combine two terms per block and keep the
+// broadcast column scales.
+template <int FMT>
+constexpr bool plain_scale()
+{
+    return FMT != RFX_FP2M && FMT != RFX_FP2S;
+}
 
 template <int FMT, int Q, bool FULL>
 __device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int nb, int lane)
@@ -146,9 +158,18 @@ __device__ __forceinline__ XTileM<Q> load_xtile_m(const XCols<Q> &xc, int s, int
     for (int j = 1; j < Q; j++)
         xo += (lane & 3) >= j ? xc.xoff[j] - xc.xoff[j - 1] : 0u;
     xt.code = *reinterpret_cast<const u32x4 *>(xc.xq + xo + (uint32_t)bc * 32u + (uint32_t)(chunk & 1) * 16u);
+    if constexpr (plain_scale<FMT>()) {
+        const int ba = FULL ? s * 8 + ((lane >> 2) & 7) : min(s * 8 + ((lane >> 2) & 7), nb - 1);
+        uint32_t mo = xc.moff[0];
 #pragma unroll
-    for (int j = 0; j < Q; j++)
-        xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
+        for (int j = 1; j < Q; j++)
+            mo += (lane & 3) >= j ? xc.moff[j] - xc.moff[j - 1] : 0u;
+        xt.sxa = xc.xs[mo + (uint32_t)ba];
+    } else {
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            xt.sx[j] = xc.xs[xc.moff[j] + (uint32_t)bs];
+    }
     if (TileFmt<FMT>::needs_sum) {
         constexpr int off = FMT == RFX_FP2 ? 3 : FMT == RFX_FP3 || FMT == RFX_FP3E ? 7 : -1; // FP2M: +sum
 #pragma unroll
@@ -302,6 +323,20 @@ __device__ __forceinline__ XHalf tile_xhalf(const u32x4 &code)
         return XHalf{};
 }
 
+// The scale products of block BI for the lane's row: element j is
+// s_w(row) * s_x(column j, block BI). v_mfma_f32_4x4x1_16b_f32's output
+// lane l, register v is A(lane 4 (l / 4) + v) * B(lane l) (measured on
+// gfx950), and cbsz 4 with abid BI broadcasts lanes 4 BI .. 4 BI + 3 of A
+// to every block: those lanes hold block BI's column scales (sxa), B is the
+// lane's own weight scale. One product per output rounded once, so each is
+// the value of the vector multiply s_w * s_x.
+template <int BI>
+__device__ __forceinline__ f32x4 scale_products(float sxa, float sw)
+{
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_amdgcn_mfma_f32_4x4x1f32(sxa, sw, zero, 4, BI, 0);
+}
+
 template <int FMT, int Q, int BI, bool FULL>
 __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XTileM<Q> &xt, const XHalf &xh,
                                                 int b0, int nb, float (&acc)[Q])
@@ -311,11 +346,10 @@ __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XT
         if (!FULL)
             sw = b0 + BI < nb ? sw : 0.0f;
         const f32x4 d = fp4_block_dots<BI>(t.c[BI], xh);
+        const f32x4 sc = scale_products<BI>(xt.sxa, sw);
 #pragma unroll
-        for (int j = 0; j < Q; j++) {
-            const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
-            acc[j] += (sw * sxb) * d[j];
-        }
+        for (int j = 0; j < Q; j++)
+            acc[j] = fmaf(sc[j], d[j], acc[j]);
         __builtin_amdgcn_sched_barrier(0);
         return;
     }
@@ -339,13 +373,17 @@ __device__ __forceinline__ void tile_block_mfma(const TileRegs<FMT> &t, const XT
         return;
     }
     const i32x4 d = block_dots_mfma<FMT, Q, BI>(sel, xt);
+    if constexpr (FMT == RFX_FP2M) { // sx * (s D + m X)
 #pragma unroll
-    for (int j = 0; j < Q; j++) {
-        const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
-        if (FMT == RFX_FP2M) // sx * (s D + m X)
+        for (int j = 0; j < Q; j++) {
+            const float sxb = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
             acc[j] += sxb * (sw * (float)d[j] + s2 * (float)bcast_row<BI>(xt.nsum[j]));
-        else
-            acc[j] += (sw * sxb) * (float)d[j];
+        }
+    } else {
+        const f32x4 sc = scale_products<BI>(xt.sxa, sw);
+#pragma unroll
+        for (int j = 0; j < Q; j++)
+            acc[j] = fmaf(sc[j], (float)d[j], acc[j]);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -373,10 +411,7 @@ template <int F, int Q, int BI, bool FULL>
 __device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const TileRegs<F> &tu, const XTileM<Q> &xt,
                                                  const XHalf &xh, int b0, int nb, float (&ag)[Q], float (&au)[Q])
 {
-    float sxb[Q];
-#pragma unroll
-    for (int j = 0; j < Q; j++)
-        sxb[j] = __builtin_bit_cast(float, bcast_row<BI>(__builtin_bit_cast(int, xt.sx[j])));
+    static_assert(plain_scale<F>(), "gate/up formats scale as (s_w * s_x) * D");
     if constexpr (F == RFX_FP4) {
         float sg = fp4_scale<BI>(tg), su = fp4_scale<BI>(tu);
         if (!FULL) {
@@ -384,13 +419,15 @@ __device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const Ti
             su = b0 + BI < nb ? su : 0.0f;
         }
         const f32x4 dg = fp4_block_dots<BI>(tg.c[BI], xh);
+        const f32x4 cg = scale_products<BI>(xt.sxa, sg);
 #pragma unroll
         for (int j = 0; j < Q; j++)
-            ag[j] += (sg * sxb[j]) * dg[j];
+            ag[j] = fmaf(cg[j], dg[j], ag[j]);
         const f32x4 du = fp4_block_dots<BI>(tu.c[BI], xh);
+        const f32x4 cu = scale_products<BI>(xt.sxa, su);
 #pragma unroll
         for (int j = 0; j < Q; j++)
-            au[j] += (su * sxb[j]) * du[j];
+            au[j] = fmaf(cu[j], du[j], au[j]);
         __builtin_amdgcn_sched_barrier(0);
         return;
     }
@@ -400,16 +437,18 @@ __device__ __forceinline__ void tile_block2_mfma(const TileRegs<F> &tg, const Ti
     if (!FULL)
         sw = b0 + BI < nb ? sw : 0.0f;
     i32x4 d = block_dots_mfma<F, Q, BI>(sel, xt);
+    const f32x4 cg = scale_products<BI>(xt.sxa, sw);
 #pragma unroll
     for (int j = 0; j < Q; j++)
-        ag[j] += (sw * sxb[j]) * (float)d[j];
+        ag[j] = fmaf(cg[j], (float)d[j], ag[j]);
     decode_block2<F, BI>(tu, sel, sw);
     if (!FULL)
         sw = b0 + BI < nb ? sw : 0.0f;
     d = block_dots_mfma<F, Q, BI>(sel, xt);
+    const f32x4 cu = scale_products<BI>(xt.sxa, sw);
 #pragma unroll
     for (int j = 0; j < Q; j++)
-        au[j] += (sw * sxb[j]) * (float)d[j];
+        au[j] = fmaf(cu[j], (float)d[j], au[j]);
     __builtin_amdgcn_sched_barrier(0);
 }
 
