@@ -25,6 +25,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const int32_t __attribute__((address_space(4))) *sptr_i32;
 typedef const float __attribute__((address_space(4))) *sptr_f32;
 
+// A pointer read from memory (a per-expert table) is generic to the
+// compiler, so loads through it become flat loads, which count against
+// lgkmcnt as well as vmcnt: every wait for an LDS or scalar result then also
+// waits for the weight loads in flight. Device memory and mapped pinned host
+// memory are both in the global aperture, so such a pointer is re-typed as
+// global (an address-space cast the compiler propagates to the loads).
+__device__ __forceinline__ const uint8_t *as_global(const void *p)
+{
+    typedef const __attribute__((address_space(1))) uint8_t *gptr_u8;
+    return (const uint8_t *)(gptr_u8)(uintptr_t)p;
+}
+
 // Uniform pointer -> constant address space, so the compiler reads it with
 // scalar loads (s_load_dwordxN) into SGPRs.
 __device__ __forceinline__ sptr_i32 as_scalar_i32(const void *p) { return (sptr_i32)(uintptr_t)p; }

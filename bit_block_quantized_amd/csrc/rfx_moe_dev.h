@@ -465,7 +465,7 @@ struct FfnArgs {
 __device__ __forceinline__ const uint8_t *expert_mat(const FfnArgs &a, int m, int e)
 {
     if (a.expert_data)
-        return static_cast<const uint8_t *>(a.expert_data[m * a.E + e]);
+        return as_global(a.expert_data[m * a.E + e]);
     return m == 0 ? a.gate + a.gate_stride * (size_t)e
          : m == 1 ? a.up + a.up_stride * (size_t)e : a.down + a.down_stride * (size_t)e;
 }

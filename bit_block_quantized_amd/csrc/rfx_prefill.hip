@@ -370,7 +370,7 @@ struct FfnArgs {
 __device__ __forceinline__ const uint8_t *expert_mat(const FfnArgs &a, int m, int e)
 {
     if (a.expert_data)
-        return static_cast<const uint8_t *>(a.expert_data[m * a.E + e]);
+        return as_global(a.expert_data[m * a.E + e]);
     return m == 0 ? a.gate + a.gate_stride * (size_t)e
          : m == 1 ? a.up + a.up_stride * (size_t)e : a.down + a.down_stride * (size_t)e;
 }
@@ -522,29 +522,27 @@ constexpr int kLdsFrag = 0, kLdsSx = 65536, kLdsRow = 69632, kLdsTok = 69888;
 constexpr int kLdsBytes = 70144;
 
 // One thread's share of a K tile of the item's activation rows: slot t % 64,
-// block t / 64 (32 int8), and the block's fp32 scale. Slots past n and
-// blocks past nb are zero.
+// block t / 64 (32 int8), and the block's fp32 scale. Slots past n read the
+// row the slot map gives them (row 0) and blocks past nb the last block:
+// their products are never stored (slots) or never issued (blocks), and
+// every wave issues the same loads on every path, so the compiler can wait
+// for exactly the loads a step needs (vmcnt(N)) instead of all of them.
 struct ActStage {
     u32x4 x0, x1;
     float sx;
 };
 
 __device__ __forceinline__ ActStage act_load(const int8_t *rows, const float *scales, size_t row_stride,
-                                             size_t scale_stride, const int *slot_src, int n, int s, int nb)
+                                             size_t scale_stride, const int *slot_src, int s, int nb)
 {
     const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
-    const int blk = s * 8 + b;
+    const int blk = min(s * 8 + b, nb - 1);
     ActStage a;
-    a.x0 = u32x4{0u, 0u, 0u, 0u};
-    a.x1 = a.x0;
-    a.sx = 0.0f;
-    if (i < n && blk < nb) {
-        const int src = slot_src[i];
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
-        a.x0 = p[0];
-        a.x1 = p[1];
-        a.sx = scales[(size_t)src * scale_stride + blk];
-    }
+    const int src = slot_src[i];
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
+    a.x0 = p[0];
+    a.x1 = p[1];
+    a.sx = scales[(size_t)src * scale_stride + blk];
     return a;
 }
 
@@ -675,7 +673,10 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
 // barrier per tile). Weights: half tiles in two register sets used in
 // turn, the next half loading while the current one is computed. The wave's
 // M row tiles start at r0[m] in mat[m] (a wave whose rows are past R only
-// stages activations).
+// stages activations). Every load is issued on every path (a wave past R
+// reads row group 0, the last step re-reads its own tile), so each wait
+// covers only the loads it needs: with loads under a branch the compiler
+// waited for all of them before every LDS store.
 template <int F, int M, int NT, bool DBG>
 __device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const int (&r0)[M], int R, int S, int nb,
                                          const int8_t *act, const float *act_s, size_t act_stride,
@@ -689,36 +690,30 @@ __device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const i
     int rin[M];
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        tb[m] = mat[m] + (size_t)(r0[m] >> 6) * S * TB;
-        rin[m] = (r0[m] & 63) + (lane & 15);
+        const int rr = rows_ok ? r0[m] : 0;
+        tb[m] = mat[m] + (size_t)(rr >> 6) * S * TB;
+        rin[m] = (rr & 63) + (lane & 15);
     }
     WHalf<F> wa[M], wb[M];
-    if (rows_ok) {
 #pragma unroll
-        for (int m = 0; m < M; m++)
-            wa[m] = load_whalf<F>(tb[m], rin[m], g, 0);
-    }
-    act_store(act_load(act, act_s, act_stride, act_sstride, slot_src, n, 0, nb),
+    for (int m = 0; m < M; m++)
+        wa[m] = load_whalf<F>(tb[m], rin[m], g, 0);
+    act_store(act_load(act, act_s, act_stride, act_sstride, slot_src, 0, nb),
               reinterpret_cast<uint32_t *>(smem + kLdsFrag), reinterpret_cast<float *>(smem + kLdsSx));
     __syncthreads();
     for (int s = 0; s < S; s++) {
         const uint32_t *frag = reinterpret_cast<const uint32_t *>(smem + kLdsFrag + (s & 1) * 32768);
         const float *lsx = reinterpret_cast<const float *>(smem + kLdsSx + (s & 1) * 2048);
-        if (rows_ok) {
+        const int sn = s + 1 < S ? s + 1 : s;
 #pragma unroll
-            for (int m = 0; m < M; m++)
-                wb[m] = load_whalf<F>(tb[m] + (size_t)s * TB, rin[m], g, 1);
-        }
-        ActStage st{};
-        if (s + 1 < S)
-            st = act_load(act, act_s, act_stride, act_sstride, slot_src, n, s + 1, nb);
+        for (int m = 0; m < M; m++)
+            wb[m] = load_whalf<F>(tb[m] + (size_t)s * TB, rin[m], g, 1);
+        const ActStage st = act_load(act, act_s, act_stride, act_sstride, slot_src, sn, nb);
         if (rows_ok)
             ffn_half<F, M, NT, DBG>(wa, frag, lsx, n, s, 0, nb, acc, dots, r0, R);
-        if (rows_ok && s + 1 < S) {
 #pragma unroll
-            for (int m = 0; m < M; m++)
-                wa[m] = load_whalf<F>(tb[m] + (size_t)(s + 1) * TB, rin[m], g, 0);
-        }
+        for (int m = 0; m < M; m++)
+            wa[m] = load_whalf<F>(tb[m] + (size_t)sn * TB, rin[m], g, 0);
         if (rows_ok)
             ffn_half<F, M, NT, DBG>(wb, frag, lsx, n, s, 1, nb, acc, dots, r0, R);
         if (s + 1 < S) {
