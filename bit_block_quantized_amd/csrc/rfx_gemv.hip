@@ -332,19 +332,24 @@ __device__ __forceinline__ void gemv_body(const GemvArgs &a, int p, int g, float
     } else if (s_begin < s_end) {
         // two tile buffers used in turn (no register copies, which would
         // wait for the loads they copy): tile s + 1 in flight while s is
-        // computed
+        // computed. The loop body loads unconditionally and the last one or
+        // two tiles run after it: with the next tile's loads under a branch,
+        // the compiler's wait for the current tile's first chunk had to
+        // assume they were not issued and waited for nearly all of them.
         constexpr bool BC = LBC && use_bcast<Q>();
         WTile<FMT, Q> ta = load_wtile<FMT, Q, FULL, BC>(gbase, s_begin, lane, xc, a.nb), tb;
-        for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end)
-                tb = load_wtile<FMT, Q, FULL, BC>(gbase, s + 1, lane, xc, a.nb);
+        int s = s_begin;
+        for (; s + 2 < s_end; s += 2) {
+            tb = load_wtile<FMT, Q, FULL, BC>(gbase, s + 1, lane, xc, a.nb);
             compute_tile<FMT, Q, DOTS, FULL, BC>(ta, s, row, a, xc, acc);
-            if (s + 1 >= s_end)
-                break;
-            if (s + 2 < s_end)
-                ta = load_wtile<FMT, Q, FULL, BC>(gbase, s + 2, lane, xc, a.nb);
+            ta = load_wtile<FMT, Q, FULL, BC>(gbase, s + 2, lane, xc, a.nb);
             compute_tile<FMT, Q, DOTS, FULL, BC>(tb, s + 1, row, a, xc, acc);
         }
+        if (s + 1 < s_end)
+            tb = load_wtile<FMT, Q, FULL, BC>(gbase, s + 1, lane, xc, a.nb);
+        compute_tile<FMT, Q, DOTS, FULL, BC>(ta, s, row, a, xc, acc);
+        if (s + 1 < s_end)
+            compute_tile<FMT, Q, DOTS, FULL, BC>(tb, s + 1, row, a, xc, acc);
     }
     if (DOTS)
         return;
@@ -405,17 +410,20 @@ __device__ __forceinline__ void gemv_body_mx(const GemvArgs &a, int p, int g, fl
     const uint8_t *gbase = a.W + (size_t)g * a.S * TileFmt<RFX_FP4>::bytes;
     constexpr int TB = TileFmt<RFX_FP4>::bytes;
     if (LBC && s_end - s_begin > 1) {
+        // the loop body loads unconditionally (see gemv_body)
         MxTile<Q> ta = load_mx_tile<Q, FULL>(gbase + (size_t)s_begin * TB, s_begin, a.nb, lane, xc, ml), tb;
-        for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end)
-                tb = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 1) * TB, s + 1, a.nb, lane, xc, ml);
+        int s = s_begin;
+        for (; s + 2 < s_end; s += 2) {
+            tb = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 1) * TB, s + 1, a.nb, lane, xc, ml);
             compute_mx_tile<Q>(ta, ml, acc);
-            if (s + 1 >= s_end)
-                break;
-            if (s + 2 < s_end)
-                ta = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 2) * TB, s + 2, a.nb, lane, xc, ml);
+            ta = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 2) * TB, s + 2, a.nb, lane, xc, ml);
             compute_mx_tile<Q>(tb, ml, acc);
         }
+        if (s + 1 < s_end)
+            tb = load_mx_tile<Q, FULL>(gbase + (size_t)(s + 1) * TB, s + 1, a.nb, lane, xc, ml);
+        compute_mx_tile<Q>(ta, ml, acc);
+        if (s + 1 < s_end)
+            compute_mx_tile<Q>(tb, ml, acc);
     } else {
         for (int s = s_begin; s < s_end; s++) {
             const MxTile<Q> t = load_mx_tile<Q, FULL>(gbase + (size_t)s * TB, s, a.nb, lane, xc, ml);

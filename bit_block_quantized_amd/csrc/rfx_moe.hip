@@ -212,18 +212,26 @@ __device__ void gateup_body(const FfnArgs &a, const SlotInfo &si, int g, int lan
             const GUTile<FG, NE> t = load_gu<FG, NE>(gm, um, s, nbH, xc, lane);
             gateup_tile<FG, NE>(t, s, nbH, xc, ag, au);
         }
+    } else if (s_end - s_begin == 1) {
+        const GUTile<FG, NE> t = load_gu<FG, NE>(gm, um, s_begin, nbH, xc, lane);
+        gateup_tile<FG, NE>(t, s_begin, nbH, xc, ag, au);
     } else if (s_begin < s_end) {
+        // every load is issued on every path, so the wait for a tile's
+        // first chunk leaves the next tile's loads in flight (with them
+        // under a branch, the compiler waited for those too); an odd count
+        // of three or more re-reads its last tile once
         GUTile<FG, NE> ta = load_gu<FG, NE>(gm, um, s_begin, nbH, xc, lane), tb;
-        for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end)
-                tb = load_gu<FG, NE>(gm, um, s + 1, nbH, xc, lane);
+        int s = s_begin;
+        for (; s + 2 < s_end; s += 2) {
+            tb = load_gu<FG, NE>(gm, um, s + 1, nbH, xc, lane);
             gateup_tile<FG, NE>(ta, s, nbH, xc, ag, au);
-            if (s + 1 >= s_end)
-                break;
-            if (s + 2 < s_end)
-                ta = load_gu<FG, NE>(gm, um, s + 2, nbH, xc, lane);
+            ta = load_gu<FG, NE>(gm, um, s + 2, nbH, xc, lane);
             gateup_tile<FG, NE>(tb, s + 1, nbH, xc, ag, au);
         }
+        tb = load_gu<FG, NE>(gm, um, min(s + 1, s_end - 1), nbH, xc, lane);
+        gateup_tile<FG, NE>(ta, s, nbH, xc, ag, au);
+        if (s + 1 < s_end)
+            gateup_tile<FG, NE>(tb, s + 1, nbH, xc, ag, au);
     }
     // fixed-order reduction over waves; red[w][m][j][row], m = gate/up
 #pragma unroll
@@ -456,18 +464,23 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
         ao[j] = 0.0f;
     const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
     const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
-    if (s_begin < s_end) {
+    if (s_end - s_begin == 1) {
+        const DTile<FD, NE> t = load_dn<FD, NE>(dm, s_begin, nbI, xc, lane);
+        down_tile<FD, NE>(t, s_begin, nbI, xc, ao);
+    } else if (s_begin < s_end) {
+        // loads on every path, as in gateup_body
         DTile<FD, NE> da = load_dn<FD, NE>(dm, s_begin, nbI, xc, lane), db;
-        for (int s = s_begin; s < s_end; s += 2) {
-            if (s + 1 < s_end)
-                db = load_dn<FD, NE>(dm, s + 1, nbI, xc, lane);
+        int s = s_begin;
+        for (; s + 2 < s_end; s += 2) {
+            db = load_dn<FD, NE>(dm, s + 1, nbI, xc, lane);
             down_tile<FD, NE>(da, s, nbI, xc, ao);
-            if (s + 1 >= s_end)
-                break;
-            if (s + 2 < s_end)
-                da = load_dn<FD, NE>(dm, s + 2, nbI, xc, lane);
+            da = load_dn<FD, NE>(dm, s + 2, nbI, xc, lane);
             down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
         }
+        db = load_dn<FD, NE>(dm, min(s + 1, s_end - 1), nbI, xc, lane);
+        down_tile<FD, NE>(da, s, nbI, xc, ao);
+        if (s + 1 < s_end)
+            down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
     }
 #pragma unroll
     for (int j = 0; j < NE; j++)
