@@ -37,6 +37,10 @@ __device__ __forceinline__ const uint8_t *as_global(const void *p)
     return (const uint8_t *)(gptr_u8)(uintptr_t)p;
 }
 
+// s_waitcnt immediate (gfx9 encoding): lgkmcnt = 0, vmcnt and expcnt at
+// their maxima: wait for every outstanding scalar and LDS operation only.
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+
 // Uniform pointer -> constant address space, so the compiler reads it with
 // scalar loads (s_load_dwordxN) into SGPRs.
 __device__ __forceinline__ sptr_i32 as_scalar_i32(const void *p) { return (sptr_i32)(uintptr_t)p; }
@@ -355,10 +359,18 @@ template <int FMT, int Q, int NQ, bool FULL>
 __device__ __forceinline__ void tile_blocks(const TileRegs<FMT> &t, int b0, int nb, const XCols<Q> &xc,
                                             float (&acc)[Q])
 {
+    XBlock<Q> xn = load_xblock<TileFmt<FMT>::needs_sum, Q>(xc, FULL ? b0 : min(b0, nb - 1));
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
-        const int b = FULL ? b0 + bi : min(b0 + bi, nb - 1);
-        const XBlock<Q> xb = load_xblock<TileFmt<FMT>::needs_sum, Q>(xc, b);
+        // block bi's scalar loads are done here; the next block's are
+        // issued now, so they are in flight during this block's work
+        // (scalar loads return out of order: a wait covers all of them)
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        const XBlock<Q> xb = xn;
+        __builtin_amdgcn_sched_barrier(0);
+        if (bi + 1 < 8)
+            xn = load_xblock<TileFmt<FMT>::needs_sum, Q>(xc, FULL ? b0 + bi + 1 : min(b0 + bi + 1, nb - 1));
+        __builtin_amdgcn_sched_barrier(0);
         Sel8 sel;
         float sw;
         decode_block<FMT>(t, bi, sel, sw);
@@ -379,10 +391,15 @@ template <int FG, int FU, int Q, bool FULL>
 __device__ __forceinline__ void tile_blocks2(const TileRegs<FG> &tg, const TileRegs<FU> &tu, int b0, int nb,
                                              const XCols<Q> &xc, float (&ag)[Q], float (&au)[Q])
 {
+    XBlock<Q> xn = load_xblock<true, Q>(xc, FULL ? b0 : min(b0, nb - 1));
 #pragma unroll
     for (int bi = 0; bi < 8; bi++) {
-        const int b = FULL ? b0 + bi : min(b0 + bi, nb - 1);
-        const XBlock<Q> xb = load_xblock<true, Q>(xc, b);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0); // as in tile_blocks
+        const XBlock<Q> xb = xn;
+        __builtin_amdgcn_sched_barrier(0);
+        if (bi + 1 < 8)
+            xn = load_xblock<true, Q>(xc, FULL ? b0 + bi + 1 : min(b0 + bi + 1, nb - 1));
+        __builtin_amdgcn_sched_barrier(0);
         Sel8 sel;
         float sw;
         decode_block<FG>(tg, bi, sel, sw);

@@ -150,8 +150,9 @@ __device__ __forceinline__ MxX<Q> load_mx_x(int s, int nb, const XCols<Q> &xc, c
 #pragma unroll
         for (int p = 0; p < MxX<Q>::NP; p++) {
             x.xr[h][p] = *reinterpret_cast<const u32x4 *>(xc.xq + (ml.xo[p] + 32u * (uint32_t)blk));
-            const float sxv = SX ? xc.xs[ml.mo[p] + (uint32_t)blk] : 0.0f;
-            x.sx[h][p] = ml.lo[p] ? sxv : 0.0f;
+            // masked where it is used (compute_mx): a select here would
+            // wait for the load before the tile's weight loads are issued
+            x.sx[h][p] = SX ? xc.xs[ml.mo[p] + (uint32_t)blk] : 0.0f;
         }
     }
     return x;
@@ -232,6 +233,7 @@ __device__ __forceinline__ void compute_mx(const MxW (&w)[M], const MxX<Q> &x, c
 #pragma unroll
         for (int p = 0; p < MxX<Q>::NP; p++) {
             const i32x8 b = build_b<Q>(x.xr[h][p], ml, p);
+            const float sx = ml.lo[p] ? x.sx[h][p] : 0.0f;
 #pragma unroll
             for (int m = 0; m < M; m++) {
 #pragma unroll
@@ -242,7 +244,7 @@ __device__ __forceinline__ void compute_mx(const MxW (&w)[M], const MxX<Q> &x, c
                     for (int v = 0; v < 4; v++) {
                         const float hi = p == 0 ? high_part<0>(d[v]) : high_part<1>(d[v]);
                         const float blk = d[v] + hi;
-                        acc[m][g][v] = fmaf(x.sx[h][p], blk, acc[m][g][v]);
+                        acc[m][g][v] = fmaf(sx, blk, acc[m][g][v]);
                     }
                 }
             }
