@@ -53,7 +53,8 @@ inline int prefill_max_items(int q, int k, int E)
 struct MoeWs {
     float *logits;      // [q][E] (decode)
     unsigned *route_cnt; // [kRouteMaxGroups + 1] counters, kRouteCntStride words apart
-    float *h;           // [NP][I]   NP = q*k + q (decode keeps it for inspection)
+    float *h;           // [NP][I]   NP = q*k + q (decode keeps it for inspection; prefill
+                        // holds f16 copies of h~ [NP][I] and of the token codes [q][H] here)
     int8_t *hq;         // [NP][I]
     float *hs;          // [NP][I/32]
     int32_t *hsum;      // [NP][I/32]
@@ -78,7 +79,10 @@ inline MoeWs carve(void *base, int q, int k, int E, int H, int I)
     };
     const size_t o_logits = take((size_t)q * E * 4);
     const size_t o_rc = take((size_t)(kRouteMaxGroups + 1) * kRouteCntStride * 4);
-    const size_t o_h = take(NP * I * 4);
+    // prefill (q > kMaxDecodeQ) keeps no fp32 h: the region holds f16 copies
+    // of h~ ([NP][I]) and of the token codes ([q][H]) instead
+    const size_t h_bytes = q > kMaxDecodeQ ? (NP * I * 2 + (size_t)q * H * 2 > NP * I * 4 ? NP * I * 2 + (size_t)q * H * 2 : NP * I * 4) : NP * I * 4;
+    const size_t o_h = take(h_bytes);
     const size_t o_hq = take(NP * I);
     const size_t o_hs = take(NP * (I / 32) * 4);
     const size_t o_hsum = take(NP * (I / 32) * 4);

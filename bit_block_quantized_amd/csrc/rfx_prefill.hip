@@ -317,8 +317,9 @@ __global__ __launch_bounds__(1024) void bucket_kernel(BucketArgs a)
 //
 // Each work item is up to 64 tokens of one expert. A workgroup of eight
 // waves takes one item and a range of output rows; per 256-column K tile
-// the item's int8 activations are staged once into LDS as f16 operand
-// fragments, and every wave decodes the packed blocks of its own rows
+// the item's activations are staged once into LDS as f16 operand
+// fragments (direct-to-LDS loads from an f16 copy of the int8 codes, made
+// once per layer), and every wave decodes the packed blocks of its own rows
 // straight from memory into f16 fragments through the codebook (byte
 // permutes of a table of f16 high bytes: every codebook value is a small
 // integer whose f16 low byte is zero). v_mfma_f32_16x16x32_f16 then takes
@@ -363,6 +364,8 @@ struct FfnArgs {
     int probe_expert, probe_first;
     int32_t *dots[3];
     const void *const *expert_data; // placement table [3][E] or null
+    const uint16_t *xh; // f16 copy of xq [T][H] (workspace)
+    uint16_t *hh;       // f16 copy of h~ [rows][I] (workspace)
 };
 
 // Matrix m (0 gate, 1 up, 2 down) of routed expert e: from the placement
@@ -521,45 +524,58 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t x, uint32_t &p01, uint32_t 
 constexpr int kLdsFrag = 0, kLdsSx = 65536, kLdsRow = 69632, kLdsTok = 69888;
 constexpr int kLdsBytes = 70144;
 
-// One thread's share of a K tile of the item's activation rows: slot t % 64,
-// block t / 64 (32 int8), and the block's fp32 scale. Slots past n read the
-// row the slot map gives them (row 0) and blocks past nb the last block:
-// their products are never stored (slots) or never issued (blocks), and
-// every wave issues the same loads on every path, so the compiler can wait
-// for exactly the loads a step needs (vmcnt(N)) instead of all of them.
-struct ActStage {
-    u32x4 x0, x1;
-    float sx;
-};
-
-__device__ __forceinline__ ActStage act_load(const int8_t *rows, const float *scales, size_t row_stride,
-                                             size_t scale_stride, const int *slot_src, int s, int nb)
+// Activation staging by direct loads into LDS (global_load_lds_dwordx4):
+// the item's rows come from an f16 copy of the int8 codes (exact), written
+// once per layer, so the K loop spends no registers and no conversion on
+// them. Wave w stages block w of a K tile: fragment (tt, w) of every token
+// tile tt < NT (lane l: 16 bytes of slot 16 tt + l % 16, values
+// 8 (l / 16) .. + 7 of the block, which is the MFMA A-operand layout) and
+// the slots' fp32 scales of the block. Slots past n read the row the slot
+// map gives them (row 0) and blocks past nb the last block: their products
+// are never stored (slots) or never issued (blocks).
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst)
 {
-    const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
-    const int blk = min(s * 8 + b, nb - 1);
-    ActStage a;
-    const int src = slot_src[i];
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(rows + (size_t)src * row_stride + (size_t)blk * 32);
-    a.x0 = p[0];
-    a.x1 = p[1];
-    a.sx = scales[(size_t)src * scale_stride + blk];
-    return a;
+    typedef const __attribute__((address_space(1))) void *gptr;
+    typedef __attribute__((address_space(3))) void *lptr;
+    __builtin_amdgcn_global_load_lds((gptr)(uintptr_t)src, (lptr)(uint32_t)(uintptr_t)lds_dst, 16, 0, 0);
 }
 
-// ... converted to f16 fragments (values 8g .. 8g + 7 are K group g).
-__device__ __forceinline__ void act_store(const ActStage &a, uint32_t *frag, float *lsx)
+__device__ __forceinline__ void lds_dma4(const void *src, void *lds_dst)
 {
-    const int i = threadIdx.x & 63, b = threadIdx.x >> 6;
-    const uint32_t x[8] = {a.x0.x, a.x0.y, a.x0.z, a.x0.w, a.x1.x, a.x1.y, a.x1.z, a.x1.w};
-    u32x4 *f = reinterpret_cast<u32x4 *>(frag) + ((i >> 4) * 8 + b) * 64 + (i & 15);
+    typedef const __attribute__((address_space(1))) void *gptr;
+    typedef __attribute__((address_space(3))) void *lptr;
+    __builtin_amdgcn_global_load_lds((gptr)(uintptr_t)src, (lptr)(uint32_t)(uintptr_t)lds_dst, 4, 0, 0);
+}
+
+template <int NT>
+struct ActDma {
+    uint32_t frag[NT]; // byte offsets of the lane's fragment rows in the f16 copy
+    uint32_t sc;       // byte offset of the lane's slot row of scales
+};
+
+template <int NT>
+__device__ __forceinline__ ActDma<NT> act_dma_setup(const int *slot_src, size_t row_stride, int nb)
+{
+    const int lane = threadIdx.x & 63;
+    ActDma<NT> d;
 #pragma unroll
-    for (int g = 0; g < 4; g++) {
-        uint32_t p0, p1, p2, p3;
-        i8x4_to_f16(x[2 * g], p0, p1);
-        i8x4_to_f16(x[2 * g + 1], p2, p3);
-        f[16 * g] = u32x4{p0, p1, p2, p3};
-    }
-    lsx[b * 64 + i] = a.sx;
+    for (int tt = 0; tt < NT; tt++)
+        d.frag[tt] = (uint32_t)slot_src[16 * tt + (lane & 15)] * (uint32_t)(row_stride * 2) + 16u * (uint32_t)(lane >> 4);
+    d.sc = (uint32_t)slot_src[lane] * (uint32_t)(nb * 4);
+    return d;
+}
+
+template <int NT>
+__device__ __forceinline__ void act_dma(const ActDma<NT> &d, const uint16_t *rows, const float *scales, int s,
+                                        int nb, char *frag_buf, char *sx_buf)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int blk = min(s * 8 + wave, nb - 1);
+    const char *rb = reinterpret_cast<const char *>(rows) + (size_t)blk * 64;
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++)
+        lds_dma16(rb + d.frag[tt], frag_buf + (tt * 8 + wave) * 1024);
+    lds_dma4(reinterpret_cast<const char *>(scales) + (size_t)blk * 4 + d.sc, sx_buf + wave * 256);
 }
 
 // Slot -> (h / o row, token) maps of an item, in LDS.
@@ -582,10 +598,10 @@ __device__ __forceinline__ void fill_slots(const FfnArgs &a, const Item &it, int
 // tt - 1's results are scaled, and tile tt + 1's operands are read from LDS
 // meanwhile. With DBG and dots[m] set, each block dot is also stored,
 // [row][slot][block].
-template <int F, int M, int NT, bool DBG>
+template <int F, int M, int NT, bool DBG, typename Hook>
 __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t *frag, const float *lsx, int n,
                                          int s, int hf, int nb, float (&acc)[M][NT][4], int32_t *const (&dots)[M],
-                                         const int (&r0)[M], int R)
+                                         const int (&r0)[M], int R, Hook &&after_first)
 {
     const int lane = threadIdx.x & 63, g = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -612,6 +628,11 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
         for (int m = 0; m < M; m++) {
             wv[m] = wfrag<F>(w[m], j, g);
             sw[m] = wscale<F>(w[m], j);
+        }
+        if (j == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            after_first();
+            __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 dp[M];
         float sa_prev = sa;
@@ -679,9 +700,9 @@ __device__ __forceinline__ void ffn_half(const WHalf<F> (&w)[M], const uint32_t 
 // waited for all of them before every LDS store.
 template <int F, int M, int NT, bool DBG>
 __device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const int (&r0)[M], int R, int S, int nb,
-                                         const int8_t *act, const float *act_s, size_t act_stride,
-                                         size_t act_sstride, const int *slot_src, int n, char *smem,
-                                         float (&acc)[M][NT][4], int32_t *const (&dots)[M])
+                                         const uint16_t *act, const float *act_s, size_t act_stride,
+                                         const int *slot_src, int n, char *smem, float (&acc)[M][NT][4],
+                                         int32_t *const (&dots)[M])
 {
     constexpr int TB = TileFmt<F>::bytes;
     const int lane = threadIdx.x & 63, g = lane >> 4;
@@ -694,12 +715,13 @@ __device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const i
         tb[m] = mat[m] + (size_t)(rr >> 6) * S * TB;
         rin[m] = (rr & 63) + (lane & 15);
     }
+    const ActDma<NT> ad = act_dma_setup<NT>(slot_src, act_stride, nb);
     WHalf<F> wa[M], wb[M];
 #pragma unroll
     for (int m = 0; m < M; m++)
         wa[m] = load_whalf<F>(tb[m], rin[m], g, 0);
-    act_store(act_load(act, act_s, act_stride, act_sstride, slot_src, 0, nb),
-              reinterpret_cast<uint32_t *>(smem + kLdsFrag), reinterpret_cast<float *>(smem + kLdsSx));
+    act_dma<NT>(ad, act, act_s, 0, nb, smem + kLdsFrag, smem + kLdsSx);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     for (int s = 0; s < S; s++) {
         const uint32_t *frag = reinterpret_cast<const uint32_t *>(smem + kLdsFrag + (s & 1) * 32768);
@@ -708,21 +730,30 @@ __device__ __forceinline__ void ffn_pipe(const uint8_t *const (&mat)[M], const i
 #pragma unroll
         for (int m = 0; m < M; m++)
             wb[m] = load_whalf<F>(tb[m] + (size_t)s * TB, rin[m], g, 1);
-        const ActStage st = act_load(act, act_s, act_stride, act_sstride, slot_src, sn, nb);
         if (rows_ok)
-            ffn_half<F, M, NT, DBG>(wa, frag, lsx, n, s, 0, nb, acc, dots, r0, R);
+            ffn_half<F, M, NT, DBG>(wa, frag, lsx, n, s, 0, nb, acc, dots, r0, R, [] {});
+        // The next tile's activations (direct to LDS) and its first weight
+        // half are issued once this half's first block has its weights:
+        // while a direct-to-LDS load is in flight the compiler waits for
+        // every outstanding load (vmcnt(0)) wherever it waits for one, so
+        // none may be pending where wb is waited for.
+        const auto stage = [&] {
+            act_dma<NT>(ad, act, act_s, sn, nb, smem + kLdsFrag + ((s + 1) & 1) * 32768,
+                        smem + kLdsSx + ((s + 1) & 1) * 2048);
 #pragma unroll
-        for (int m = 0; m < M; m++)
-            wa[m] = load_whalf<F>(tb[m] + (size_t)sn * TB, rin[m], g, 0);
-        if (rows_ok)
-            ffn_half<F, M, NT, DBG>(wb, frag, lsx, n, s, 1, nb, acc, dots, r0, R);
-        if (s + 1 < S) {
-            act_store(st, reinterpret_cast<uint32_t *>(smem + kLdsFrag + ((s + 1) & 1) * 32768),
-                      reinterpret_cast<float *>(smem + kLdsSx + ((s + 1) & 1) * 2048));
-            __syncthreads();
+            for (int m = 0; m < M; m++)
+                wa[m] = load_whalf<F>(tb[m] + (size_t)sn * TB, rin[m], g, 0);
+        };
+        if (rows_ok) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); // wb: the only loads in flight
+            ffn_half<F, M, NT, DBG>(wb, frag, lsx, n, s, 1, nb, acc, dots, r0, R, stage);
         }
+        if (!rows_ok)
+            stage();
+        // the next tile's staging has landed in every wave before any reads it
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
     }
-    __syncthreads(); // every wave done with the fragments (the epilogue reuses them)
 }
 
 // Gate/up: one workgroup = 128 intermediate rows of gate and of up x one
@@ -742,8 +773,7 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
     const uint8_t *const mats[2] = {gm, um};
     const int r0[2] = {rw, rw};
     float acc[2][NT][4] = {};
-    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.I, S, nbH, a.xq, a.xs, (size_t)a.H, (size_t)nbH, slot_tok, it.n, smem, acc,
-                            dots);
+    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.I, S, nbH, a.xh, a.xs, (size_t)a.H, slot_tok, it.n, smem, acc, dots);
     const bool rows_ok = rw < a.I;
 
     // epilogue: h, amax over this wave's 16 rows per token, then over the
@@ -809,9 +839,20 @@ __device__ void gateup_body(const FfnArgs &a, const Item &it, const uint8_t *gm,
         // 64 slots x 128 rows of codes, 16 bytes per thread
         const int i = tid >> 3, piece = tid & 7;
         const int row = blockIdx.x * kGateRows + 16 * piece;
-        if (i < it.n && row < a.I)
-            *reinterpret_cast<u32x4 *>(a.ws.hq + (size_t)slot_row[i] * a.I + row) =
-                *reinterpret_cast<const u32x4 *>(hq_l + i * kGateRows + 16 * piece);
+        if (i < it.n && row < a.I) {
+            const u32x4 c = *reinterpret_cast<const u32x4 *>(hq_l + i * kGateRows + 16 * piece);
+            *reinterpret_cast<u32x4 *>(a.ws.hq + (size_t)slot_row[i] * a.I + row) = c;
+            // the same codes as f16, which the down launch stages
+            uint32_t f[8];
+            i8x4_to_f16(c.x, f[0], f[1]);
+            i8x4_to_f16(c.y, f[2], f[3]);
+            i8x4_to_f16(c.z, f[4], f[5]);
+            i8x4_to_f16(c.w, f[6], f[7]);
+            const u32x4 f0 = {f[0], f[1], f[2], f[3]}, f1 = {f[4], f[5], f[6], f[7]};
+            u32x4 *hp = reinterpret_cast<u32x4 *>(a.hh + (size_t)slot_row[i] * a.I + row);
+            hp[0] = f0;
+            hp[1] = f1;
+        }
     }
 }
 
@@ -858,8 +899,7 @@ __device__ void down_body(const FfnArgs &a, const Item &it, const uint8_t *dm, c
     const uint8_t *const mats[2] = {dm, dm};
     const int r0[2] = {rw, rw + 16};
     float acc[2][NT][4] = {};
-    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.H, S, nbI, a.ws.hq, a.ws.hs, (size_t)a.I, (size_t)nbI, slot_row, it.n, smem,
-                            acc, dots);
+    ffn_pipe<F, 2, NT, DBG>(mats, r0, a.H, S, nbI, a.hh, a.ws.hs, (size_t)a.I, slot_row, it.n, smem, acc, dots);
     if (rw >= a.H)
         return;
 #pragma unroll
@@ -906,6 +946,24 @@ __global__ __launch_bounds__(kFfnThreads, 3) void prefill_down_kernel(FfnArgs a)
         down_dispatch<FSD, DBG>(a, it, a.sh_down, smem);
     else
         down_dispatch<FD, DBG>(a, it, expert_mat(a, 2, it.expert), smem);
+}
+
+// f16 copy of the int8 token codes (exact), 16 per thread; n % 16 == 0.
+__global__ __launch_bounds__(256) void codes_f16_kernel(const int8_t *xq, uint16_t *xh, size_t n)
+{
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    if (i >= n)
+        return;
+    const u32x4 c = *reinterpret_cast<const u32x4 *>(xq + i);
+    uint32_t f[8];
+    i8x4_to_f16(c.x, f[0], f[1]);
+    i8x4_to_f16(c.y, f[2], f[3]);
+    i8x4_to_f16(c.z, f[4], f[5]);
+    i8x4_to_f16(c.w, f[6], f[7]);
+    const u32x4 f0 = {f[0], f[1], f[2], f[3]}, f1 = {f[4], f[5], f[6], f[7]};
+    u32x4 *p = reinterpret_cast<u32x4 *>(xh + i);
+    p[0] = f0;
+    p[1] = f1;
 }
 
 // y[t] = resid[t] + o_shared[t] + sum_j w[t][j] o[t*k + j], slot order.
@@ -1052,6 +1110,20 @@ int prefill_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const fl
     a.probe_expert = -1;
     a.probe_first = -1;
     a.expert_data = L->expert_data;
+    // f16 copies in the workspace's h region (prefill keeps no fp32 h); the
+    // kernels address their rows with 32-bit byte offsets
+    if ((size_t)(q * k + q) * L->inter * 2 >= ((size_t)1 << 32) || (size_t)q * L->hidden * 2 >= ((size_t)1 << 32))
+        return fail(RFX_E_UNSUPPORTED, "prefill: f16 activation copies of %d tokens exceed 4 GiB", q);
+    a.hh = reinterpret_cast<uint16_t *>(w.h);
+    a.xh = a.hh + (size_t)(q * k + q) * L->inter;
+    {
+        const size_t n = (size_t)q * L->hidden;
+        hipLaunchKernelGGL(codes_f16_kernel, dim3((unsigned)((n / 16 + 255) / 256)), dim3(256), 0, stream, xq,
+                           const_cast<uint16_t *>(a.xh), n);
+        int st = hip_status("prefill f16 codes launch");
+        if (st)
+            return st;
+    }
     const int fsg = has_shared ? L->sh_gate.fmt : L->gate.fmt;
     const int fsd = has_shared ? L->sh_down.fmt : L->down.fmt;
     const int items = prefill_max_items(q, k, L->n_experts);
