@@ -152,6 +152,23 @@ def time_graph(torch, g, reps):
     return e0.elapsed_time(e1) / reps  # ms per replay
 
 
+PREWARM_S = 0.2
+
+
+def prewarm_graph(torch, g):
+    """Replay g until at least PREWARM_S seconds have passed; returns the
+    number of replays (untimed)."""
+    torch.cuda.synchronize()
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < PREWARM_S:
+        for _ in range(8):
+            g.replay()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def time_eager(torch, fn, n):
     for i in range(10):
         fn(i)
@@ -763,6 +780,11 @@ def main():
     # one graph of that many grouped launches, replayed --warmup times
     # untimed first
     g = graph_of(torch, lambda i: R.gemv_grouped(garrs[i % rot], gws), args.steps)
+    # untimed pre-warm: the same steps for at least PREWARM_S of wall clock,
+    # so the timed steps run at the GPU's sustained clocks whatever --steps
+    # and --warmup are (measured on MI355X: a fresh process reads ~1 us more
+    # per step over the first few milliseconds of back-to-back launches)
+    prewarm = prewarm_graph(torch, g)
     for _ in range(args.warmup):
         g.replay()
     ms = time_graph(torch, g, 1) / args.steps
@@ -788,7 +810,9 @@ def main():
                                "launch per step, rotated weight copies",
                    "rows": N, "cols": K, "formats": ["FP2", "FP3", "FP4"], "q": [1, 4],
                    "copies": {FMT_NAME[f]: len(work[f]["mats"]) for f in FORMATS},
-                   "timing": "one HIP graph of --steps grouped launches after --warmup untimed replays"},
+                   "timing": "one HIP graph of --steps grouped launches after an untimed pre-warm of the same "
+                             "graph (prewarm_replays, at least 0.2 s) and --warmup untimed replays",
+                   "prewarm_replays": prewarm},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gemv_grouped_kernel (FP2/FP3/FP4 x q=1,4, 7168x7168)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
