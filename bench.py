@@ -140,8 +140,13 @@ def graph_of(torch, fn, n):
     return g
 
 
-def time_graph(torch, g, reps):
-    g.replay()
+def time_graph(torch, g, reps, prewarm=True):
+    """ms per replay of g over reps timed replays, after an untimed pre-warm
+    (prewarm_graph) or, with prewarm=False, one untimed replay."""
+    if prewarm:
+        prewarm_graph(torch, g)
+    else:
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -787,7 +792,7 @@ def main():
     prewarm = prewarm_graph(torch, g)
     for _ in range(args.warmup):
         g.replay()
-    ms = time_graph(torch, g, 1) / args.steps
+    ms = time_graph(torch, g, 1, prewarm=False) / args.steps
     value = step_bytes / (ms * 1e-3) / 1e9
     del g
     log(f"step: grouped {ms * 1e3:.2f} us ({value:.0f} GB/s), six launches {ms_six * 1e3:.2f} us")
