@@ -335,7 +335,9 @@ int rfx_moe_route_topk(const rfx_moe_layer *L, const float *x, int q, int k, int
  * with the int8 activations (as f16, exact) on v_mfma_f32_16x16x32_f16, one
  * instruction per 32-weight block, so each fp32 result is the exact integer
  * block dot, then scaled by the weight and activation block scales in fp32
- * ([HM] para 3: integer dot products over the packed codes). */
+ * ([HM] para 3: integer dot products over the packed codes). The prefill
+ * path keeps f16 copies of the token codes and of h~ in ws and returns
+ * RFX_E_UNSUPPORTED when either copy would exceed 4 GiB. */
 int rfx_moe_ffn(const rfx_moe_layer *L, int q, int k, const int8_t *xq, const float *xs,
                 const int32_t *xsum, const int32_t *topk_idx, const float *topk_w,
                 const int32_t *pairs_sorted, const int32_t *expert_off, const float *resid,
