@@ -408,34 +408,39 @@ __global__ __launch_bounds__(512) void gateup_kernel(FfnArgs a, RouteOut ro)
 // ------------------------------------------------------------------
 // Expert down projection, shared expert and the weighted combine.
 // ------------------------------------------------------------------
+// MF: one-token slots take the matrix-core dots too (the same exact
+// integers and fp32 sums as the scalar-operand path). Chosen per call: in
+// calls with two or more tokens most routed slots have one, and the matrix
+// core measured 1.6 us faster per q = 4 top-6 layer; at q = 1 the
+// scalar-operand path measured 2 us faster per 8-layer step.
 template <int FD, int NE>
 struct DTile {
     TileRegs<FD> w;
     XTileM<NE> x;
 };
 
-template <int FD, int NE>
+template <int FD, int NE, bool MF>
 __device__ __forceinline__ DTile<FD, NE> load_dn(const uint8_t *dm, int s, int nbI, const XCols<NE> &xc, int lane)
 {
     DTile<FD, NE> t;
-    if (NE >= 2)
+    if (NE >= 2 || MF)
         t.x = load_xtile_m<FD, NE, false>(xc, s, nbI, lane);
     t.w = load_tile<FD>(dm + (size_t)s * TileFmt<FD>::bytes, lane);
     return t;
 }
 
-template <int FD, int NE>
+template <int FD, int NE, bool MF>
 __device__ __forceinline__ void down_tile(const DTile<FD, NE> &t, int s, int nbI, const XCols<NE> &xc,
                                           float (&ao)[NE])
 {
-    if (NE >= 2)
+    if (NE >= 2 || MF)
         tile_blocks_mfma<FD, NE, false>(t.w, t.x, s * 8, nbI, ao);
     else
         tile_blocks<FD, NE, NE, false>(t.w, s * 8, nbI, xc, ao);
 }
 
 
-template <int FD, int NE>
+template <int FD, int NE, bool MF = false>
 __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane, int wave, int W, float *red)
 {
     const SlotCols<NE> cols = slot_cols<NE>(si, a);
@@ -465,22 +470,22 @@ __device__ void down_body(const FfnArgs &a, const SlotInfo &si, int g, int lane,
     const int s_begin = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * wave) / (unsigned)W));
     const int s_end = __builtin_amdgcn_readfirstlane((int)((unsigned)(S * (wave + 1)) / (unsigned)W));
     if (s_end - s_begin == 1) {
-        const DTile<FD, NE> t = load_dn<FD, NE>(dm, s_begin, nbI, xc, lane);
-        down_tile<FD, NE>(t, s_begin, nbI, xc, ao);
+        const DTile<FD, NE> t = load_dn<FD, NE, MF>(dm, s_begin, nbI, xc, lane);
+        down_tile<FD, NE, MF>(t, s_begin, nbI, xc, ao);
     } else if (s_begin < s_end) {
         // loads on every path, as in gateup_body
-        DTile<FD, NE> da = load_dn<FD, NE>(dm, s_begin, nbI, xc, lane), db;
+        DTile<FD, NE> da = load_dn<FD, NE, MF>(dm, s_begin, nbI, xc, lane), db;
         int s = s_begin;
         for (; s + 2 < s_end; s += 2) {
-            db = load_dn<FD, NE>(dm, s + 1, nbI, xc, lane);
-            down_tile<FD, NE>(da, s, nbI, xc, ao);
-            da = load_dn<FD, NE>(dm, s + 2, nbI, xc, lane);
-            down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
+            db = load_dn<FD, NE, MF>(dm, s + 1, nbI, xc, lane);
+            down_tile<FD, NE, MF>(da, s, nbI, xc, ao);
+            da = load_dn<FD, NE, MF>(dm, s + 2, nbI, xc, lane);
+            down_tile<FD, NE, MF>(db, s + 1, nbI, xc, ao);
         }
-        db = load_dn<FD, NE>(dm, min(s + 1, s_end - 1), nbI, xc, lane);
-        down_tile<FD, NE>(da, s, nbI, xc, ao);
+        db = load_dn<FD, NE, MF>(dm, min(s + 1, s_end - 1), nbI, xc, lane);
+        down_tile<FD, NE, MF>(da, s, nbI, xc, ao);
         if (s + 1 < s_end)
-            down_tile<FD, NE>(db, s + 1, nbI, xc, ao);
+            down_tile<FD, NE, MF>(db, s + 1, nbI, xc, ao);
     }
 #pragma unroll
     for (int j = 0; j < NE; j++)
@@ -548,6 +553,8 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
         case 1:
             if constexpr (FSD == RFX_FP4)
                 down_body_mx<1>(a, si, g, lane, wave, W, red);
+            else if (a.q >= 2)
+                down_body<FSD, 1, true>(a, si, g, lane, wave, W, red);
             else
                 down_body<FSD, 1>(a, si, g, lane, wave, W, red);
             break;
@@ -566,6 +573,8 @@ __global__ __launch_bounds__(1024) void down_kernel(FfnArgs a)
         case 1:
             if constexpr (FD == RFX_FP4)
                 down_body_mx<1>(a, si, g, lane, wave, W, red);
+            else if (a.q >= 2)
+                down_body<FD, 1, true>(a, si, g, lane, wave, W, red);
             else
                 down_body<FD, 1>(a, si, g, lane, wave, W, red);
             break;
