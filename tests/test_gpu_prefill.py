@@ -325,3 +325,18 @@ def test_prefill_uneven_expert_and_token_counts():
     x = inputgen.tokens(13, 77, 77, spec.hidden)
     gpu = _run(torch, spec, dev, x, 3)
     _check_all(spec, gpu, x, 3, orc)
+
+
+def test_prefill_hidden_wider_than_the_h_rows():
+    """hidden 1024 against inter 128 at top-1: the f16 copies of the token
+    codes and of h~ that the FFN stages from take more than the fp32 h rows
+    of the workspace region they live in (H > (k + 1) I), so the region must
+    be sized for them; every stage is checked against the oracle."""
+    torch = need_gpu()
+    say("prefill hidden 1024 inter 128 k=1 q=96")
+    spec = LayerSpec(layer=17, hidden=1024, inter=128, n_experts=8, shared=True)
+    dev = spec.build_device()
+    orc = OracleMoe(spec)
+    x = inputgen.tokens(17, 96, 96, spec.hidden)
+    gpu = _run(torch, spec, dev, x, 1)
+    _check_all(spec, gpu, x, 1, orc)

@@ -394,3 +394,20 @@ def test_placement_table_validation_without_gpu():
     assert L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, need, None) == -1  # stacks NULL, no table
     lay.expert_data = good + 4
     assert L.rfx_moe_ffn(ctypes.byref(lay), 1, 2, f, f, f, f, f, f, f, f, f, f, need, None) == -2
+
+
+def test_prefill_workspace_holds_the_f16_activation_copies():
+    """The prefill FFN keeps f16 copies of the token codes ([q][H]) and of
+    h~ ([q*k + q][I]) in the workspace; its size must cover them even where
+    they exceed the fp32 h rows the decode path keeps (H > (k + 1) I)."""
+    L = R.lib()
+    good = 0x7f0000000000
+    H, I, E, k = 4096, 256, 4, 1
+    z = R.QMat(0, 0, 0, 0, None)
+    lay = R.MoeLayerC(H, I, E, 0, R.QMat(2, I, H, E, good), R.QMat(2, I, H, E, good),
+                      R.QMat(3, H, I, E, good), z, z, z, good, None)
+    for q in (64, 2048):
+        need = L.rfx_moe_workspace_bytes(ctypes.byref(lay), q, k)
+        assert need >= q * H * 2 + (q * k + q) * I * 2 + (q * k + q) * I  # copies + int8 h~
+    # the decode sizes keep fp32 h only
+    assert L.rfx_moe_workspace_bytes(ctypes.byref(lay), 4, k) >= (4 * k + 4) * I * 4
