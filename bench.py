@@ -663,8 +663,9 @@ def profile_only(args, torch, R, inputgen):
 
 
 def per_config(out):
-    """Each workload's fraction of the 8 TB/s peak (the target is judged per
-    workload), in one place."""
+    """Each workload's fraction of the 8 TB/s peak, gathered in one place:
+    the dense GEMV (per launch and grouped), the MoE layer, the stacks and
+    prefill."""
     pc = {}
     if "config1" in out:
         c1 = out["config1"]
