@@ -701,7 +701,7 @@ def main():
                     help="fmt,q | grouped | moe | prefill: launch only this, eagerly, for a profiler")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the decode path has no multi-GPU part); "
+        print("bench.py: this benchmark measures one GPU only (the decode path has no multi-GPU part); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1:

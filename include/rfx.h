@@ -44,7 +44,7 @@ enum {
     RFX_E_INVAL = -1,      /* bad shape, format, count or null pointer */
     RFX_E_ALIGN = -2,      /* pointer not aligned as required */
     RFX_E_RANGE = -3,      /* non-finite weight, or fp16 scale overflow */
-    RFX_E_UNSUPPORTED = -4,/* valid request this build does not implement */
+    RFX_E_UNSUPPORTED = -4,/* valid request this library does not implement */
     RFX_E_WORKSPACE = -5,  /* workspace missing or too small */
     RFX_E_HIP = -6,        /* a HIP runtime call or launch failed */
     RFX_E_TIMEOUT = -7     /* a bounded device-side wait ran out (rfx_moe_forward_status) */
